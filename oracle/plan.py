@@ -1,0 +1,188 @@
+"""Reference SH-Tile planner and FLOPs-aware placement, in plain Python.
+
+TEST INFRASTRUCTURE ONLY.  Used by the tests to check the library's planner
+bit for bit; it shares no code with it.
+
+SH-Tiles (Libra technical review, section 5.1, eq. 6).  The packed sequence
+is cut at global token positions into blocks of at most B tokens (a block may
+straddle samples, the last one may be short) and the h_q query heads into
+equal contiguous shards of W heads.  Tile t = (block b, shard s) with
+tile_id = b * S + s, S = h_q / W (block-major: the pages break placement ties
+"by tile ID" and leave the numbering open, so this is a reading).
+
+KV groups (section 5.2, eq. 7).  K(t) is the set of samples the block
+intersects; it is contiguous, so it is reported as [sample_first, sample_last].
+
+Tile FLOPs (section 5.3, eq. 8).  For every sample j that block b intersects,
+with sample-local query positions a..e-1 inside the block, query position q
+pairs with q + 1 keys; pairs_t = W * sum_j sum_{q=a}^{e-1} (q + 1).  Forward
+FLOPs are 4 * d per pair (two matrix products of 2 * d each).
+
+Work items (a reading: on one GPU the workers are CUs and a whole SH-Tile is
+too coarse for 256 of them).  Every tile is split into items that one
+workgroup of four 64-query waves runs:
+  * for each KV head kappa whose query heads meet the tile's shard, the heads
+    H = shard ∩ group(kappa) are cut into groups of nh heads, nh = 4 if |H| is a
+    multiple of 4, else 2 if even, else 1;
+  * each head group takes the tile's rows in chunks of 256 / nh positions.
+An item's pairs are eq. 8 restricted to its rows and heads; its cost is its
+pairs plus a fixed per-item overhead (a planner parameter).
+Items are numbered in (tile_id, kappa, head group, row chunk) order.
+
+Key-major items for the dK/dV pass: keys are cut at global positions into
+chunks of 128; item (chunk c, KV head kappa) has id c * h_kv + kappa and covers
+all g = h_q / h_kv query heads of kappa.  Its pairs count, for every key k in
+the chunk, the queries q >= k of k's sample: g * sum_k (end(k) - k).
+
+Placement (Algorithm 2, section 5.4).  C = (1 + tau) * sum f / |W|.  Units go
+in order of decreasing f, then id.  Among workers whose load stays <= C the
+placer takes the minimum of (dcomm, load, worker id); if there is none it
+takes the minimum of (load, dcomm, worker id).  On one GPU every tensor is
+already in HBM, so dcomm is 0 unless a caller passes a cost function.  A
+worker runs its units in the order they were placed.  The round-robin mode
+(unit i to worker i mod |W|) is the no-placement ablation.
+"""
+from __future__ import annotations
+
+WAVES = 4
+WAVE_QUERIES = 64
+ITEM_COLUMNS = WAVES * WAVE_QUERIES      # query positions x heads per forward item
+KV_CHUNK = 128                           # keys per dK/dV item
+
+
+def _ranges(cu):
+    cu = [int(x) for x in cu]
+    if not cu or cu[0] != 0:
+        raise ValueError("cu_seqlens must start at 0")
+    for a, b in zip(cu, cu[1:]):
+        if b < a:
+            raise ValueError("cu_seqlens must be non-decreasing")
+    return [(cu[j], cu[j + 1]) for j in range(len(cu) - 1)]
+
+
+def _triangle_sum(a: int, e: int) -> int:
+    """sum_{q=a}^{e-1} (q + 1), summed term by term."""
+    return sum(q + 1 for q in range(a, e))
+
+
+def _block_pairs(ranges, lo: int, hi: int):
+    """Per-head causal pairs of query rows [lo, hi) and the non-empty samples they touch."""
+    pairs = 0
+    touched = []
+    for j, (s, e) in enumerate(ranges):
+        a, b = max(lo, s), min(hi, e)
+        if a >= b:
+            continue
+        touched.append(j)
+        pairs += _triangle_sum(a - s, b - s)
+    return pairs, touched
+
+
+def sh_tiles(cu, total_tokens: int, h_q: int, B: int, W: int) -> list:
+    """Tiles in tile_id order, each with its rows, heads, K(t) and eq. 8 pairs."""
+    if B <= 0 or W <= 0 or h_q % W:
+        raise ValueError("bad tile shape")
+    ranges = _ranges(cu)
+    if ranges and ranges[-1][1] != total_tokens:
+        raise ValueError("cu_seqlens must end at L")
+    S = h_q // W
+    nblocks = (total_tokens + B - 1) // B
+    out = []
+    for b in range(nblocks):
+        lo, hi = b * B, min(total_tokens, (b + 1) * B)
+        per_head, touched = _block_pairs(ranges, lo, hi)
+        for s in range(S):
+            out.append(dict(tile_id=b * S + s, block=b, shard=s, tok_begin=lo, tok_end=hi,
+                            head_begin=s * W, head_count=W,
+                            sample_first=touched[0], sample_last=touched[-1],
+                            pairs=W * per_head))
+    return out
+
+
+def _head_group_size(n: int) -> int:
+    if n % 4 == 0:
+        return 4
+    if n % 2 == 0:
+        return 2
+    return 1
+
+
+def fwd_items(cu, total_tokens, h_q, h_kv, B, W, overhead=0) -> list:
+    """Forward / dQ work items in id order."""
+    g = h_q // h_kv
+    ranges = _ranges(cu)
+    items = []
+    for t in sh_tiles(cu, total_tokens, h_q, B, W):
+        h_lo, h_hi = t["head_begin"], t["head_begin"] + t["head_count"]
+        for kappa in range(h_lo // g, (h_hi - 1) // g + 1):
+            heads = list(range(max(h_lo, kappa * g), min(h_hi, (kappa + 1) * g)))
+            nh = _head_group_size(len(heads))
+            rows = ITEM_COLUMNS // nh
+            for gi in range(len(heads) // nh):
+                for r0 in range(t["tok_begin"], t["tok_end"], rows):
+                    r1 = min(t["tok_end"], r0 + rows)
+                    per_head, _ = _block_pairs(ranges, r0, r1)
+                    items.append(dict(id=len(items), tile_id=t["tile_id"], row0=r0, nrows=r1 - r0,
+                                      kv_head=kappa, head0=heads[gi * nh], nheads=nh,
+                                      pairs=nh * per_head, cost=nh * per_head + overhead))
+    return items
+
+
+def kv_items(cu, total_tokens, h_q, h_kv, overhead=0) -> list:
+    """dK/dV work items in id order (chunk-major, then KV head)."""
+    g = h_q // h_kv
+    ranges = _ranges(cu)
+    items = []
+    nchunks = (total_tokens + KV_CHUNK - 1) // KV_CHUNK
+    for c in range(nchunks):
+        lo, hi = c * KV_CHUNK, min(total_tokens, (c + 1) * KV_CHUNK)
+        per_head = 0
+        for s, e in ranges:
+            a, b = max(lo, s), min(hi, e)
+            per_head += sum(e - k for k in range(a, b))
+        for kappa in range(h_kv):
+            items.append(dict(id=len(items), tile_id=-1, row0=lo, nrows=hi - lo, kv_head=kappa,
+                              head0=kappa * g, nheads=g, pairs=g * per_head,
+                              cost=g * per_head + overhead))
+    return items
+
+
+def place(costs, n_workers: int, tau: float = 0.03, dcomm=None):
+    """Algorithm 2: returns (worker of each unit, units in placement order)."""
+    n = len(costs)
+    dcomm = dcomm or (lambda t, r: 0)
+    C = (1.0 + tau) * float(sum(costs)) / n_workers
+    order = sorted(range(n), key=lambda t: (-costs[t], t))
+    load = [0] * n_workers
+    sigma = [None] * n
+    for t in order:
+        fits = [r for r in range(n_workers) if float(load[r] + costs[t]) <= C]
+        if fits:
+            r = min(fits, key=lambda r: (dcomm(t, r), load[r], r))
+        else:
+            r = min(range(n_workers), key=lambda r: (load[r], dcomm(t, r), r))
+        sigma[t] = r
+        load[r] += costs[t]
+    return sigma, order
+
+
+def round_robin(n_units: int, n_workers: int):
+    return [i % n_workers for i in range(n_units)], list(range(n_units))
+
+
+def queue(costs, n_workers, tau=0.03, mode="lpt"):
+    """Per-worker queues as CSR: (offsets[n_workers + 1], unit ids, per-worker load)."""
+    if mode == "lpt":
+        sigma, order = place(costs, n_workers, tau)
+    else:
+        sigma, order = round_robin(len(costs), n_workers)
+    per = [[] for _ in range(n_workers)]
+    for t in order:
+        per[sigma[t]].append(t)
+    offsets = [0]
+    ids = []
+    for r in range(n_workers):
+        ids += per[r]
+        offsets.append(len(ids))
+    load = [sum(costs[t] for t in per[r]) for r in range(n_workers)]
+    return offsets, ids, load
