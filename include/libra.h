@@ -1,0 +1,188 @@
+/*
+ * libra.h -- C ABI of the MI355X (gfx950) packed variable-length causal
+ * attention library: SH-Tile planner, FLOPs-aware tile-to-CU placement,
+ * and persistent forward / backward attention kernels.
+ *
+ * Operation (Libra technical review, section 1 "Sequence packing" and
+ * section 5.3 under eq. 8; Libra paper, section 2.3): samples are packed into
+ * one sequence of L tokens described by cu_seqlens (n + 1 int32 prefix sums,
+ * cu_seqlens[0] = 0, cu_seqlens[n] = L).  Query token i of sample j attends to
+ * the keys of sample j at positions cu_seqlens[j] .. i (diagonal included),
+ * never across samples.  Query head h reads KV head h / (h_q / h_kv).
+ *
+ *   O   = softmax(scale * Q K^T + mask) V          (bf16 out, fp32 accumulate)
+ *   LSE = log(sum exp(scale * Q K^T + mask))        (natural log, fp32)
+ *
+ * Conventions shared by every entry point:
+ *   - All tensors are contiguous and token-major:
+ *       q, o, dout, dq : [L, h_q, head_dim] bf16
+ *       k, v, dk, dv   : [L, h_kv, head_dim] bf16
+ *       lse            : [h_q, L] fp32
+ *     Device pointers must be 16-byte aligned.
+ *   - The caller owns and allocates every buffer, host and device.  The
+ *     library allocates nothing, keeps no global state, never synchronises,
+ *     and only enqueues work on the stream it is given (a hipStream_t passed
+ *     as void*; NULL is the default stream).
+ *   - Every argument is validated on the host before anything is enqueued;
+ *     a failed check returns a negative libra_status and enqueues nothing.
+ *     A launch error returns LIBRA_EHIP.  Faults inside kernels surface at
+ *     the caller's next synchronisation.
+ *   - A plan is a pure function of (cu_seqlens, libra_plan_params); one plan
+ *     serves every layer with the same packing (Libra paper, section 4.1:
+ *     the assignment is reused across layers with the same layout).  The
+ *     device copy of a plan is a byte copy of the host buffer, uploaded by
+ *     the caller.
+ */
+#ifndef LIBRA_H
+#define LIBRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LIBRA_OK = 0,
+  LIBRA_EINVAL = -1,        /* malformed argument: pointer, cu_seqlens, shape, plan */
+  LIBRA_ESIZE = -2,         /* a caller buffer is too small (required size returned) */
+  LIBRA_EUNSUPPORTED = -3,  /* well formed but not supported (e.g. head_dim) */
+  LIBRA_EHIP = -4           /* the HIP runtime rejected a launch */
+} libra_status;
+
+enum {
+  LIBRA_ASSIGN_PLACER = 0,       /* Algorithm 2 (FLOPs-aware, heaviest first) */
+  LIBRA_ASSIGN_ROUND_ROBIN = 1   /* item i -> CU i mod num_cus (ablation) */
+};
+
+#define LIBRA_PLAN_MAGIC 0x4152424Cu   /* "LBRA" little-endian */
+#define LIBRA_PLAN_VERSION 1u
+
+/* Planner inputs.  SH-Tiles (Libra technical review, section 5.1, eq. 6)
+ * are tile_tokens (B) tokens by tile_heads (W = h_q / H) query heads. */
+typedef struct {
+  int32_t total_tokens;   /* L >= 0 */
+  int32_t num_samples;    /* n >= 0; cu_seqlens holds n + 1 entries */
+  int32_t h_q;            /* query heads, a multiple of h_kv */
+  int32_t h_kv;           /* key/value heads >= 1 */
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t tile_tokens;    /* B >= 1: sequence block of an SH-Tile */
+  int32_t tile_heads;     /* W >= 1, divides h_q: head shard width */
+  int32_t num_cus;        /* workers = persistent workgroups; 0 means 256 */
+  float tau;              /* soft-target slack of Algorithm 2 (0.03 on the pages) */
+  int32_t assign;         /* LIBRA_ASSIGN_* */
+  int64_t item_overhead;  /* cost added to every work item, in causal-pair units */
+} libra_plan_params;
+
+/* One SH-Tile t = (block, shard), tile_id = block * (h_q / W) + shard.
+ * Samples sample_first..sample_last are its KV groups K(t) (section 5.2,
+ * eq. 7); pairs is its eq. 8 count of unmasked (query, key, head) triples. */
+typedef struct {
+  int32_t tile_id, block, shard;
+  int32_t tok_begin, tok_end;       /* tokens [tok_begin, tok_end) */
+  int32_t head_begin, head_count;   /* query heads [head_begin, head_begin + head_count) */
+  int32_t sample_first, sample_last;
+  int32_t n_items;                  /* forward work items cut from the tile */
+  int64_t pairs;
+} libra_tile;
+
+/* One unit of work for one persistent workgroup.
+ * Forward / dQ items: query rows [row0, row0 + nrows) of heads
+ *   [head0, head0 + nheads), all reading KV head kv_head; nheads is 1, 2 or 4
+ *   and nrows * nheads <= 256.
+ * dK/dV items (tile_id == -1): key rows [row0, row0 + nrows) of kv_head,
+ *   gathering the gradient of all h_q / h_kv query heads of that KV head. */
+typedef struct {
+  int32_t row0, nrows;
+  int32_t kv_head, head0, nheads;
+  int32_t tile_id;
+  int32_t id;                       /* position in the planner's enumeration */
+  int32_t reserved;
+  int64_t cost;                     /* placement key: pairs + item_overhead */
+  int64_t pairs;                    /* unmasked (query, key, head) triples */
+} libra_item;
+
+/* Header at offset 0 of every plan buffer.  Sections follow at the given
+ * byte offsets: tiles[n_tiles]; items[n_items] grouped by CU in placement
+ * order with cu_off[num_cus + 1] (CSR); the same for the dK/dV queue. */
+typedef struct {
+  uint32_t magic, version;
+  uint64_t bytes;
+  libra_plan_params params;
+  int32_t num_cus;                  /* resolved worker count */
+  int32_t n_tiles, n_items, n_kv_items;
+  int64_t total_pairs;              /* sum of tile pairs = h_q * sum_j l_j (l_j + 1) / 2 */
+  int64_t load_max, load_sum;       /* per-CU cost of the forward/dQ queue */
+  int64_t kv_load_max, kv_load_sum; /* per-CU cost of the dK/dV queue */
+  uint64_t off_tiles, off_items, off_cu_off, off_kv_items, off_kv_cu_off;
+  uint64_t checksum;                /* FNV-1a over 64-bit words, this field as 0 */
+} libra_plan_info;
+
+/* Per-workgroup record of a persistent kernel (optional output).  hw_id and
+ * xcc_id identify the physical CU; t_start / t_end are ticks of the
+ * constant-rate device clock (libra_device_clock_khz). */
+typedef struct {
+  uint32_t hw_id, xcc_id, n_items, reserved;
+  uint64_t t_start, t_end;
+} libra_cu_record;
+
+/* Build a plan on the host (pure function, thread-safe, no device work).
+ * cu_seqlens: host int32[num_samples + 1].  buf == NULL: only *bytes is set to
+ * the size needed.  Otherwise *bytes is the capacity of buf (8-byte aligned);
+ * LIBRA_ESIZE if too small (with *bytes set to the size needed).
+ * Tiles follow eq. 6-8 (Libra technical review, section 5); work items are
+ * placed on CUs by Algorithm 2 (section 5.4) with no communication term, or
+ * round-robin.  Errors: LIBRA_EINVAL for malformed cu_seqlens or parameters,
+ * LIBRA_EUNSUPPORTED for head_dim other than 64 or 128. */
+libra_status libra_plan(const int32_t *cu_seqlens, const libra_plan_params *params,
+                        void *buf, size_t *bytes);
+
+/* Validate a plan buffer of the given size (magic, version, size, section
+ * bounds, checksum) and copy its header to *info (may be NULL). */
+libra_status libra_plan_check(const void *plan, size_t bytes, libra_plan_info *info);
+
+/* Device workspace the forward needs (transposed V), in bytes. */
+libra_status libra_attn_fwd_workspace(const void *plan, size_t *bytes);
+
+/* Forward pass.  plan: host plan buffer; plan_dev: its byte copy on the
+ * device.  Writes o [L, h_q, d] bf16 and lse [h_q, L] fp32.  softmax_scale > 0
+ * (commonly 1/sqrt(head_dim)).  workspace: device buffer of at least
+ * libra_attn_fwd_workspace bytes (contents need not be initialised).
+ * records: NULL or device libra_cu_record[num_cus].
+ * Enqueues a transpose of V and one persistent kernel of num_cus workgroups
+ * that runs each CU's queue of work items (Libra technical review, section
+ * 5.4: the placement decided on the host is only executed here). */
+libra_status libra_attn_fwd(const void *plan, const void *plan_dev,
+                            const void *q, const void *k, const void *v,
+                            const int32_t *cu_seqlens_dev, void *o, float *lse,
+                            float softmax_scale, void *workspace, size_t workspace_bytes,
+                            libra_cu_record *records, void *stream);
+
+/* Device workspace the backward needs, in bytes. */
+libra_status libra_attn_bwd_workspace(const void *plan, size_t *bytes);
+
+/* Backward pass: dq [L, h_q, d], dk and dv [L, h_kv, d] (bf16) from q, k, v,
+ * the forward's o and lse, and dout.  Reuses the plan's forward assignment
+ * for dQ and its key-major queue for dK/dV (Libra paper, section 4.3.3: the
+ * backward reuses the forward placement).  records: NULL or device
+ * libra_cu_record[2 * num_cus] (dK/dV kernel, then dQ kernel). */
+libra_status libra_attn_bwd(const void *plan, const void *plan_dev,
+                            const void *q, const void *k, const void *v,
+                            const void *o, const void *dout, const float *lse,
+                            const int32_t *cu_seqlens_dev,
+                            void *dq, void *dk, void *dv, float softmax_scale,
+                            void *workspace, size_t workspace_bytes,
+                            libra_cu_record *records, void *stream);
+
+/* Frequency of the clock in libra_cu_record, for the current device. */
+libra_status libra_device_clock_khz(int32_t *khz);
+
+/* Static description of a status code. */
+const char *libra_status_str(libra_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBRA_H */

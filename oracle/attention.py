@@ -81,34 +81,40 @@ def _row_groups(first: int, last: int, keys: int):
         r += step
 
 
-def _scores(Qr, K, rows0, scale):
-    """scale * Q K^T for sample-local rows rows0.., keys 0..K.shape[0]-1, causally masked."""
+def _scores(Qr, K, rows, scale):
+    """scale * Q K^T for the sample-local query rows ``rows``; key k > row is masked."""
     S = scale * (Qr @ K.T)
-    i = np.arange(rows0, rows0 + Qr.shape[0])[:, None]
-    kk = np.arange(K.shape[0])[None, :]
-    S[kk > i] = -np.inf
+    S[np.arange(K.shape[0])[None, :] > np.asarray(rows)[:, None]] = -np.inf
     return S
+
+
+def attend_rows(Qr, K, V, rows, scale):
+    """O and LSE of query rows of one sample and one head.
+
+    Qr [n, d] holds the queries at sample-local positions ``rows``; K and V
+    [m, d] hold the sample's keys and values 0..m-1 with m > max(rows).
+    Row i sees keys 0..i only.
+    """
+    S = _scores(Qr, K, rows, scale)
+    m = S.max(axis=1)
+    P = np.exp(S - m[:, None])
+    l = P.sum(axis=1)
+    return (P @ V) / l[:, None], m + np.log(l)
 
 
 def head_rows(q, k, v, start, end, h, kv, first, last, scale):
     """O rows and LSE of sample-local rows [first, last) of one sample and one Q head.
 
     q, k, v are float64 [L, heads, d]; (start, end) is the sample's token range.
-    Row i uses keys 0..i of the same sample only.
     """
     d = q.shape[2]
     O = np.empty((last - first, d))
     lse = np.empty(last - first)
     for r0, r1 in _row_groups(first, last, last):
-        Qr = q[start + r0:start + r1, h]
-        K = k[start:start + r1, kv]
-        V = v[start:start + r1, kv]
-        S = _scores(Qr, K, r0, scale)
-        m = S.max(axis=1)
-        P = np.exp(S - m[:, None])
-        l = P.sum(axis=1)
-        O[r0 - first:r1 - first] = (P @ V) / l[:, None]
-        lse[r0 - first:r1 - first] = m + np.log(l)
+        o_g, l_g = attend_rows(q[start + r0:start + r1, h], k[start:start + r1, kv],
+                               v[start:start + r1, kv], np.arange(r0, r1), scale)
+        O[r0 - first:r1 - first] = o_g
+        lse[r0 - first:r1 - first] = l_g
     return O, lse
 
 
@@ -172,7 +178,7 @@ def backward_tail(q, k, v, dout, start, end, kv, first, scale):
             dOr = dout[start + r0:start + r1, h]
             K = k[start:start + r1, kv]
             V = v[start:start + r1, kv]
-            S = _scores(Qr, K, r0, scale)
+            S = _scores(Qr, K, np.arange(r0, r1), scale)
             m = S.max(axis=1)
             P = np.exp(S - m[:, None])
             Phat = P / P.sum(axis=1)[:, None]

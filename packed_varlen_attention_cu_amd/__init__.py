@@ -1,0 +1,249 @@
+"""Python binding of the libra C ABI (``include/libra.h``).
+
+Argument marshalling only: every step of the planner and of the attention
+pass runs in the native library ``_lib/liblibra.so``.  Functions named
+``libra_*`` mirror the C entry points one to one; ``Plan``, ``attn_fwd`` and
+``attn_bwd`` are conveniences that allocate outputs with torch (which is
+used for device memory and streams only).  Importing this package fails
+loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "liblibra.so")
+
+LIBRA_OK, LIBRA_EINVAL, LIBRA_ESIZE, LIBRA_EUNSUPPORTED, LIBRA_EHIP = 0, -1, -2, -3, -4
+ASSIGN_PLACER, ASSIGN_ROUND_ROBIN = 0, 1
+PLAN_MAGIC, PLAN_VERSION = 0x4152424C, 1
+
+
+class LibraError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {libra_status_str(status)} ({status})")
+
+
+class PlanParams(ctypes.Structure):
+    _fields_ = [("total_tokens", ctypes.c_int32), ("num_samples", ctypes.c_int32),
+                ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("tile_tokens", ctypes.c_int32), ("tile_heads", ctypes.c_int32),
+                ("num_cus", ctypes.c_int32), ("tau", ctypes.c_float), ("assign", ctypes.c_int32),
+                ("item_overhead", ctypes.c_int64)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32), ("bytes", ctypes.c_uint64),
+                ("params", PlanParams), ("num_cus", ctypes.c_int32), ("n_tiles", ctypes.c_int32),
+                ("n_items", ctypes.c_int32), ("n_kv_items", ctypes.c_int32),
+                ("total_pairs", ctypes.c_int64), ("load_max", ctypes.c_int64),
+                ("load_sum", ctypes.c_int64), ("kv_load_max", ctypes.c_int64),
+                ("kv_load_sum", ctypes.c_int64), ("off_tiles", ctypes.c_uint64),
+                ("off_items", ctypes.c_uint64), ("off_cu_off", ctypes.c_uint64),
+                ("off_kv_items", ctypes.c_uint64), ("off_kv_cu_off", ctypes.c_uint64),
+                ("checksum", ctypes.c_uint64)]
+
+
+TILE_DTYPE = np.dtype([("tile_id", "<i4"), ("block", "<i4"), ("shard", "<i4"), ("tok_begin", "<i4"),
+                       ("tok_end", "<i4"), ("head_begin", "<i4"), ("head_count", "<i4"),
+                       ("sample_first", "<i4"), ("sample_last", "<i4"), ("n_items", "<i4"),
+                       ("pairs", "<i8")])
+ITEM_DTYPE = np.dtype([("row0", "<i4"), ("nrows", "<i4"), ("kv_head", "<i4"), ("head0", "<i4"),
+                       ("nheads", "<i4"), ("tile_id", "<i4"), ("id", "<i4"), ("reserved", "<i4"),
+                       ("cost", "<i8"), ("pairs", "<i8")])
+RECORD_DTYPE = np.dtype([("hw_id", "<u4"), ("xcc_id", "<u4"), ("n_items", "<u4"), ("reserved", "<u4"),
+                         ("t_start", "<u8"), ("t_end", "<u8")])
+
+assert ctypes.sizeof(PlanParams) == 48 and ctypes.sizeof(PlanInfo) == 168
+assert TILE_DTYPE.itemsize == 48 and ITEM_DTYPE.itemsize == 48 and RECORD_DTYPE.itemsize == 32
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m packed_varlen_attention_cu_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.libra_plan.argtypes = [vp, ctypes.POINTER(PlanParams), vp, ctypes.POINTER(sz)]
+    lib.libra_plan_check.argtypes = [vp, sz, ctypes.POINTER(PlanInfo)]
+    lib.libra_attn_fwd_workspace.argtypes = [vp, ctypes.POINTER(sz)]
+    lib.libra_attn_bwd_workspace.argtypes = [vp, ctypes.POINTER(sz)]
+    lib.libra_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
+    lib.libra_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
+                                   vp, sz, vp, vp]
+    lib.libra_device_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int32)]
+    lib.libra_status_str.argtypes = [ctypes.c_int]
+    lib.libra_status_str.restype = ctypes.c_char_p
+    for name in ("libra_plan", "libra_plan_check", "libra_attn_fwd_workspace", "libra_attn_bwd_workspace",
+                 "libra_attn_fwd", "libra_attn_bwd", "libra_device_clock_khz"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int, what: str):
+    if status != LIBRA_OK:
+        raise LibraError(status, what)
+
+
+def _ptr(t):
+    """Device/host address of a torch tensor or numpy array (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+# ----------------------------------------------------------------- C entry points
+def libra_status_str(status: int) -> str:
+    return _lib.libra_status_str(int(status)).decode()
+
+
+def libra_plan(cu_seqlens, params: PlanParams) -> np.ndarray:
+    """Build a plan; returns the host buffer as an 8-byte aligned uint8 array."""
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    need = ctypes.c_size_t(0)
+    _check(_lib.libra_plan(cu.ctypes.data, ctypes.byref(params), None, ctypes.byref(need)), "libra_plan")
+    words = np.zeros((need.value + 7) // 8, dtype=np.uint64)
+    buf = words.view(np.uint8)[:need.value]
+    cap = ctypes.c_size_t(need.value)
+    _check(_lib.libra_plan(cu.ctypes.data, ctypes.byref(params), buf.ctypes.data, ctypes.byref(cap)),
+           "libra_plan")
+    return buf
+
+
+def libra_plan_check(buf: np.ndarray) -> PlanInfo:
+    info = PlanInfo()
+    _check(_lib.libra_plan_check(buf.ctypes.data, buf.nbytes, ctypes.byref(info)), "libra_plan_check")
+    return info
+
+
+def libra_attn_fwd_workspace(plan_host: np.ndarray) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.libra_attn_fwd_workspace(plan_host.ctypes.data, ctypes.byref(n)), "libra_attn_fwd_workspace")
+    return n.value
+
+
+def libra_attn_bwd_workspace(plan_host: np.ndarray) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.libra_attn_bwd_workspace(plan_host.ctypes.data, ctypes.byref(n)), "libra_attn_bwd_workspace")
+    return n.value
+
+
+def libra_attn_fwd(plan_host, plan_dev, q, k, v, cu_seqlens_dev, o, lse, softmax_scale, workspace,
+                   workspace_bytes, records, stream):
+    _check(_lib.libra_attn_fwd(_ptr(plan_host), _ptr(plan_dev), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(cu_seqlens_dev), _ptr(o), _ptr(lse), float(softmax_scale),
+                               _ptr(workspace), int(workspace_bytes), _ptr(records), stream),
+           "libra_attn_fwd")
+
+
+def libra_attn_bwd(plan_host, plan_dev, q, k, v, o, dout, lse, cu_seqlens_dev, dq, dk, dv,
+                   softmax_scale, workspace, workspace_bytes, records, stream):
+    _check(_lib.libra_attn_bwd(_ptr(plan_host), _ptr(plan_dev), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                               _ptr(dout), _ptr(lse), _ptr(cu_seqlens_dev), _ptr(dq), _ptr(dk), _ptr(dv),
+                               float(softmax_scale), _ptr(workspace), int(workspace_bytes),
+                               _ptr(records), stream),
+           "libra_attn_bwd")
+
+
+def libra_device_clock_khz() -> int:
+    khz = ctypes.c_int32(0)
+    _check(_lib.libra_device_clock_khz(ctypes.byref(khz)), "libra_device_clock_khz")
+    return khz.value
+
+
+# ----------------------------------------------------------------- conveniences
+class Plan:
+    """A host plan buffer, typed views of its sections, and (lazily) its device copy."""
+
+    def __init__(self, cu_seqlens, *, total_tokens, h_q, h_kv, head_dim, tile_tokens, tile_heads,
+                 num_cus=0, tau=0.03, assign=ASSIGN_PLACER, item_overhead=0):
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        self.params = PlanParams(int(total_tokens), int(cu.size - 1), int(h_q), int(h_kv), int(head_dim),
+                                 int(tile_tokens), int(tile_heads), int(num_cus), float(tau), int(assign),
+                                 int(item_overhead))
+        self.cu_seqlens = cu
+        self.host = libra_plan(cu, self.params)
+        self.info = libra_plan_check(self.host)
+        self._dev = {}
+
+    def _section(self, off, count, dtype):
+        return self.host[off:off + count * dtype.itemsize].view(dtype)
+
+    @property
+    def tiles(self):
+        return self._section(self.info.off_tiles, self.info.n_tiles, TILE_DTYPE)
+
+    @property
+    def items(self):
+        return self._section(self.info.off_items, self.info.n_items, ITEM_DTYPE)
+
+    @property
+    def cu_off(self):
+        return self._section(self.info.off_cu_off, self.info.num_cus + 1, np.dtype("<i4"))
+
+    @property
+    def kv_items(self):
+        return self._section(self.info.off_kv_items, self.info.n_kv_items, ITEM_DTYPE)
+
+    @property
+    def kv_cu_off(self):
+        return self._section(self.info.off_kv_cu_off, self.info.num_cus + 1, np.dtype("<i4"))
+
+    def device(self, device="cuda"):
+        """Byte copy of the plan (and cu_seqlens) in device memory, cached per device."""
+        import torch
+        dev = torch.device(device)
+        if dev not in self._dev:
+            plan = torch.from_numpy(self.host.copy()).to(dev)
+            cu = torch.from_numpy(self.cu_seqlens.copy()).to(dev)
+            self._dev[dev] = (plan, cu)
+        return self._dev[dev]
+
+
+def _stream_handle(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def attn_fwd(plan: Plan, q, k, v, softmax_scale=None, *, out=None, lse=None, workspace=None,
+             records=None):
+    """Forward pass on torch tensors (bf16, [L, h, d], contiguous); returns (o, lse)."""
+    import torch
+    p = plan.params
+    scale = 1.0 / math.sqrt(p.head_dim) if softmax_scale is None else softmax_scale
+    dev = q.device
+    plan_dev, cu_dev = plan.device(dev)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((p.h_q, p.total_tokens), dtype=torch.float32, device=dev) if lse is None else lse
+    ws_bytes = libra_attn_fwd_workspace(plan.host)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    libra_attn_fwd(plan.host, plan_dev, q, k, v, cu_dev, o, lse, scale, workspace, workspace.numel(),
+                   records, _stream_handle(dev))
+    return o, lse
+
+
+def attn_bwd(plan: Plan, q, k, v, o, lse, dout, softmax_scale=None, *, workspace=None, records=None):
+    """Backward pass; returns (dq, dk, dv) as bf16 tensors."""
+    import torch
+    p = plan.params
+    scale = 1.0 / math.sqrt(p.head_dim) if softmax_scale is None else softmax_scale
+    dev = q.device
+    plan_dev, cu_dev = plan.device(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = libra_attn_bwd_workspace(plan.host)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    libra_attn_bwd(plan.host, plan_dev, q, k, v, o, dout, lse, cu_dev, dq, dk, dv, scale, workspace,
+                   workspace.numel(), records, _stream_handle(dev))
+    return dq, dk, dv

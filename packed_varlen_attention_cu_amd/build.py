@@ -1,0 +1,67 @@
+"""Build the in-tree shared library ``_lib/liblibra.so`` with hipcc for gfx950.
+
+Usage: ``python -m packed_varlen_attention_cu_amd.build`` (or ``build()``).
+Every call compiles from source; nothing is cached.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIBDIR = os.path.join(HERE, "_lib")
+LIB = os.path.join(LIBDIR, "liblibra.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+HOST_SOURCES = ["plan.cpp"]
+DEVICE_SOURCES = ["attn_fwd.hip", "attn_bwd.hip"]
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall"]
+# Packed fp32 VALU forms are kept out of the generated code on purpose.
+DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-munsafe-fp-atomics",
+                # keep MFMA accumulators in architectural VGPRs: the softmax works on them
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return r
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(LIBDIR, exist_ok=True)
+    objdir = os.path.join(LIBDIR, "obj")
+    shutil.rmtree(objdir, ignore_errors=True)
+    os.makedirs(objdir)
+    jobs = []
+    for src in HOST_SOURCES:
+        jobs.append([HIPCC, *COMMON, "-x", "c++", "-c", os.path.join(CSRC, src),
+                     "-o", os.path.join(objdir, src + ".o")])
+    for src in DEVICE_SOURCES:
+        jobs.append([HIPCC, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src),
+                     "-o", os.path.join(objdir, src + ".o")])
+    with ThreadPoolExecutor(min(8, len(jobs))) as ex:
+        for r in ex.map(_run, jobs):
+            if verbose and (r.stdout or r.stderr):
+                print(r.stdout, r.stderr, file=sys.stderr)
+    objs = [os.path.join(objdir, s + ".o") for s in HOST_SOURCES + DEVICE_SOURCES]
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    shutil.rmtree(objdir, ignore_errors=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,378 @@
+// Forward packed block-diagonal causal attention on gfx950 (CDNA4).
+//
+// One persistent workgroup per CU runs the queue of work items the host
+// planner assigned to it (Libra technical review, section 5.4: placement is
+// decided on the host, the device only executes it).  A work item is up to
+// 256 query columns (positions x heads) of one KV head; each of the four
+// waves owns 64 query positions of one query head.
+//
+// Per item the workgroup walks key blocks of 64 from the start of the sample
+// holding the item's first row to its last row.  K and V^T blocks are staged
+// in LDS once and read by every wave, so all query heads of a GQA group share
+// one copy.  Each wave computes S^T = K Q^T with bf16 MFMA (its query columns
+// land one per lane, so row statistics need no cross-lane reduction beyond
+// the two 32-lane halves), applies the block-diagonal causal mask only on
+// blocks that straddle a sample start or the diagonal, skips blocks that are
+// wholly masked for it, and keeps an fp32 online softmax:
+//   m' = max(m, max_k s * c),  P = 2^(s c - m'),  l = l 2^(m - m') + sum P,
+//   O^T = O^T 2^(m - m') + V^T P^T            with c = scale * log2(e).
+// P is rounded to bf16 for the PV product and l sums the rounded values, so
+// the weights applied to V sum to exactly l.  The epilogue writes O = O^T / l
+// (bf16) and LSE = (m + log2 l) ln 2 (natural log, fp32).
+//
+// V is transposed once per call into the workspace (Vt [h_kv][d][Lp]) so both
+// MFMA operands read 16 contiguous bytes per lane from LDS.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "device_common.h"
+#include "libra.h"
+#include "plan_layout.h"
+
+namespace libra {
+
+constexpr int kThreads = 256;
+constexpr int kBN = 64;          // keys per block
+constexpr int kTileTok = 64;     // tokens per transpose tile
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// src [L][H][D] (token-major) -> dst [H][D][Lp]; tokens L..Lp-1 are zero.
+template <int D>
+__global__ __launch_bounds__(kThreads) void transpose_heads_kernel(const uint16_t *__restrict__ src,
+                                                                   uint16_t *__restrict__ dst, int L,
+                                                                   int H, int Lp) {
+  constexpr int kStride = D + 2;   // odd word stride: column reads hit distinct banks
+  __shared__ uint16_t tile[kTileTok * kStride];
+  const int t0 = blockIdx.x * kTileTok;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  constexpr int kChunks = D / 8;
+  for (int c = tid; c < kTileTok * kChunks; c += kThreads) {
+    const int r = c / kChunks, cc = c % kChunks;
+    const int tok = t0 + r;
+    u32x4 val = zero_u32x4();
+    if (tok < L) val = *reinterpret_cast<const u32x4 *>(src + ((int64_t)tok * H + h) * D + cc * 8);
+    uint32_t *row = reinterpret_cast<uint32_t *>(tile + r * kStride + cc * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) row[i] = val[i];
+  }
+  __syncthreads();
+  for (int c = tid; c < D * (kTileTok / 8); c += kThreads) {
+    const int d = c / (kTileTok / 8), j = c % (kTileTok / 8);
+    u32x4 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = tile[(8 * j + 2 * i) * kStride + d];
+      const uint32_t hi = tile[(8 * j + 2 * i + 1) * kStride + d];
+      out[i] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4 *>(dst + ((int64_t)h * D + d) * Lp + t0 + 8 * j) = out;
+  }
+}
+
+struct FwdArgs {
+  const libra_item *items;
+  const int32_t *cu_off;
+  const uint16_t *q, *k, *vt;
+  const int32_t *cu;
+  uint16_t *o;
+  float *lse;
+  libra_cu_record *records;
+  int n_samples, L, Lp, h_q, h_kv;
+  float scale_log2;
+};
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_kernel(FwdArgs a) {
+  constexpr int NS = D / 16;                    // reduction slabs of d
+  constexpr int ND = D / 32;                    // 32-row tiles of d in O^T
+  constexpr int KS = D + 8;                     // K row stride in LDS (elements)
+  constexpr int VS = kBN + 8;                   // V^T row stride in LDS (elements)
+  constexpr int KCH = kBN * D / 8 / kThreads;   // 16-byte chunks per thread, K block
+  constexpr int VCH = D * kBN / 8 / kThreads;   // 16-byte chunks per thread, V^T block
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBN * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * VS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int w = blockIdx.x;
+  const uint64_t t_start = wall_clock64();
+  const int beg = a.cu_off[w], end = a.cu_off[w + 1];
+  const float sl2 = a.scale_log2;
+  const float NEG_INF = -__builtin_inff();
+
+  for (int it = beg; it < end; ++it) {
+    const libra_item item = a.items[it];
+    const int row0 = item.row0, nrows = item.nrows, kvh = item.kv_head, nh = item.nheads;
+    const int head = item.head0 + (wave % nh);
+    const int sub = wave / nh;
+    const int wrow0 = row0 + sub * 64;
+    const int wrows = min(64, nrows - sub * 64);
+
+    int qpos[2], qss[2];
+    bool qok[2];
+    bf16x8 qop[2][NS];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int r = qt * 32 + col;
+      qok[qt] = r < wrows;
+      qpos[qt] = wrow0 + r;
+      qss[qt] = qok[qt] ? segment_start(a.cu, a.n_samples, qpos[qt]) : 0;
+      const uint16_t *qp = a.q + ((int64_t)qpos[qt] * a.h_q + head) * D + 8 * half;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        qop[qt][s] = as_bf16x8(qok[qt] ? *reinterpret_cast<const u32x4 *>(qp + 16 * s) : zero_u32x4());
+    }
+    const int kstart = segment_start(a.cu, a.n_samples, row0) & ~(kBN - 1);
+    const int kend = row0 + nrows;
+    const int nblk = (kend - kstart + kBN - 1) / kBN;
+
+    f32x16 oacc[2][ND];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) oacc[qt][dt] = zero16();
+    float m_run[2] = {NEG_INF, NEG_INF}, l_run[2] = {0.0f, 0.0f};
+
+    u32x4 kreg[KCH], vreg[VCH];
+    auto gload = [&](int k0) {
+#pragma unroll
+      for (int j = 0; j < KCH; ++j) {
+        const int c = tid + kThreads * j;
+        const int r = c / (D / 8), cc = c % (D / 8);
+        const int key = k0 + r;
+        kreg[j] = key < a.L ? *reinterpret_cast<const u32x4 *>(a.k + ((int64_t)key * a.h_kv + kvh) * D + cc * 8)
+                            : zero_u32x4();
+      }
+#pragma unroll
+      for (int j = 0; j < VCH; ++j) {
+        const int c = tid + kThreads * j;
+        const int d = c / (kBN / 8), cc = c % (kBN / 8);
+        vreg[j] = *reinterpret_cast<const u32x4 *>(a.vt + ((int64_t)kvh * D + d) * a.Lp + k0 + cc * 8);
+      }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+      for (int j = 0; j < KCH; ++j) {
+        const int c = tid + kThreads * j;
+        *reinterpret_cast<u32x4 *>(k_lds + (c / (D / 8)) * KS + (c % (D / 8)) * 8) = kreg[j];
+      }
+#pragma unroll
+      for (int j = 0; j < VCH; ++j) {
+        const int c = tid + kThreads * j;
+        *reinterpret_cast<u32x4 *>(v_lds + (c / (kBN / 8)) * VS + (c % (kBN / 8)) * 8) = vreg[j];
+      }
+    };
+
+    if (nblk > 0) gload(kstart);
+    for (int b = 0; b < nblk; ++b) {
+      const int k0 = kstart + b * kBN;
+      lstore();
+      __syncthreads();
+      if (b + 1 < nblk) gload(k0 + kBN);
+
+      bool touch = false, partial = false;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        if (qok[qt]) {
+          touch |= (k0 <= qpos[qt]) && (k0 + kBN - 1 >= qss[qt]);
+          partial |= !((k0 >= qss[qt]) && (k0 + kBN - 1 <= qpos[qt]));
+        }
+      }
+      if (wave_any(touch)) {
+        const bool masked = wave_any(partial);
+        f32x16 sacc[2][2];   // [key tile][query tile]
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          sacc[kt][0] = zero16();
+          sacc[kt][1] = zero16();
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+                k_lds + (kt * 32 + sigma_row(col)) * KS + 16 * s + 8 * half));
+            sacc[kt][0] = mfma32x32x16(ka, qop[0][s], sacc[kt][0]);
+            sacc[kt][1] = mfma32x32x16(ka, qop[1][s], sacc[kt][1]);
+          }
+        }
+        u32x4 pw[2][2][2];   // [query tile][key tile][16-key slab]: bf16 P^T operands
+        float alpha[2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          if (masked) {
+            const int lo = qok[qt] ? qss[qt] : 1, hi = qok[qt] ? qpos[qt] : 0;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int key = k0 + kt * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
+                if (key < lo || key > hi) sacc[kt][qt][r] = NEG_INF;
+              }
+          }
+          float mx = NEG_INF;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][qt][r]);
+          mx = halves_max(mx);
+          const float m_new = fmaxf(m_run[qt], mx * sl2);
+          const float m_use = m_new == NEG_INF ? 0.0f : m_new;
+          alpha[qt] = exp2_fast(m_run[qt] - m_use);
+          m_run[qt] = m_new;
+          float psum = 0.0f;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float p0 = exp2_fast(fmaf(sacc[kt][qt][8 * t + 2 * i], sl2, -m_use));
+                const float p1 = exp2_fast(fmaf(sacc[kt][qt][8 * t + 2 * i + 1], sl2, -m_use));
+                const uint32_t wv = pack_bf16x2(p0, p1);
+                psum += bf16_lo(wv) + bf16_hi(wv);
+                pw[qt][kt][t][i] = wv;
+              }
+          l_run[qt] = l_run[qt] * alpha[qt] + psum;
+        }
+        if (wave_any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) oacc[qt][dt][r] *= alpha[qt];
+        }
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+                  v_lds + (dt * 32 + col) * VS + kt * 32 + 16 * t + 8 * half));
+              oacc[0][dt] = mfma32x32x16(va, as_bf16x8(pw[0][kt][t]), oacc[0][dt]);
+              oacc[1][dt] = mfma32x32x16(va, as_bf16x8(pw[1][kt][t]), oacc[1][dt]);
+            }
+      }
+      __syncthreads();
+    }
+
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float lt = halves_sum(l_run[qt]);
+      const float inv = 1.0f / lt;
+      if (qok[qt]) {
+        uint16_t *op = a.o + ((int64_t)qpos[qt] * a.h_q + head) * D;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            u32x2 pk;
+            pk[0] = pack_bf16x2(oacc[qt][dt][4 * c] * inv, oacc[qt][dt][4 * c + 1] * inv);
+            pk[1] = pack_bf16x2(oacc[qt][dt][4 * c + 2] * inv, oacc[qt][dt][4 * c + 3] * inv);
+            *reinterpret_cast<u32x2 *>(op + dt * 32 + 8 * c + 4 * half) = pk;
+          }
+        if (half == 0) a.lse[(int64_t)head * a.L + qpos[qt]] = (m_run[qt] + __log2f(lt)) * kLn2;
+      }
+    }
+  }
+
+  __syncthreads();
+  if (a.records != nullptr && tid == 0) {
+    libra_cu_record rec;
+    rec.hw_id = hw_id_reg();
+    rec.xcc_id = xcc_id_reg();
+    rec.n_items = (uint32_t)(end - beg);
+    rec.reserved = 0;
+    rec.t_start = t_start;
+    rec.t_end = wall_clock64();
+    a.records[w] = rec;
+  }
+}
+
+size_t transposed_bytes(int64_t heads, int64_t d, int64_t L) {
+  return (size_t)round_up(heads * d * round_up(L, kTileTok) * 2, 256);
+}
+
+libra_status launch_transpose(const void *src, void *dst, int L, int H, int D, hipStream_t s) {
+  const int Lp = (int)round_up(L, kTileTok);
+  dim3 grid(Lp / kTileTok, H);
+  if (D == 128)
+    hipLaunchKernelGGL(transpose_heads_kernel<128>, grid, dim3(kThreads), 0, s,
+                       static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst), L, H, Lp);
+  else
+    hipLaunchKernelGGL(transpose_heads_kernel<64>, grid, dim3(kThreads), 0, s,
+                       static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst), L, H, Lp);
+  return hipGetLastError() == hipSuccess ? LIBRA_OK : LIBRA_EHIP;
+}
+
+bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+}  // namespace libra
+
+using namespace libra;
+
+extern "C" libra_status libra_attn_fwd_workspace(const void *plan, size_t *bytes) {
+  libra_plan_info h;
+  if (!bytes || plan_header(plan, &h) != LIBRA_OK) return LIBRA_EINVAL;
+  *bytes = transposed_bytes(h.params.h_kv, h.params.head_dim, h.params.total_tokens);
+  return LIBRA_OK;
+}
+
+extern "C" libra_status libra_attn_fwd(const void *plan, const void *plan_dev, const void *q,
+                                       const void *k, const void *v, const int32_t *cu_dev, void *o,
+                                       float *lse, float softmax_scale, void *workspace,
+                                       size_t workspace_bytes, libra_cu_record *records, void *stream) {
+  libra_plan_info h;
+  if (plan_header(plan, &h) != LIBRA_OK) return LIBRA_EINVAL;
+  const libra_plan_params &p = h.params;
+  if (p.head_dim != 64 && p.head_dim != 128) return LIBRA_EUNSUPPORTED;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return LIBRA_EINVAL;
+  if (p.total_tokens == 0) return LIBRA_OK;
+  if (!plan_dev || !q || !k || !v || !cu_dev || !o || !lse || !workspace) return LIBRA_EINVAL;
+  if (misaligned(plan_dev, 16) || misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) ||
+      misaligned(o, 16) || misaligned(lse, 4) || misaligned(cu_dev, 4) || misaligned(workspace, 16) ||
+      misaligned(records, 16))
+    return LIBRA_EINVAL;
+  const size_t need = transposed_bytes(p.h_kv, p.head_dim, p.total_tokens);
+  if (workspace_bytes < need) return LIBRA_ESIZE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  libra_status st = launch_transpose(v, workspace, p.total_tokens, p.h_kv, p.head_dim, s);
+  if (st != LIBRA_OK) return st;
+
+  FwdArgs a;
+  const char *pd = static_cast<const char *>(plan_dev);
+  a.items = reinterpret_cast<const libra_item *>(pd + h.off_items);
+  a.cu_off = reinterpret_cast<const int32_t *>(pd + h.off_cu_off);
+  a.q = static_cast<const uint16_t *>(q);
+  a.k = static_cast<const uint16_t *>(k);
+  a.vt = static_cast<const uint16_t *>(workspace);
+  a.cu = cu_dev;
+  a.o = static_cast<uint16_t *>(o);
+  a.lse = lse;
+  a.records = records;
+  a.n_samples = p.num_samples;
+  a.L = p.total_tokens;
+  a.Lp = (int)round_up(p.total_tokens, kTileTok);
+  a.h_q = p.h_q;
+  a.h_kv = p.h_kv;
+  a.scale_log2 = softmax_scale * kLog2e;
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? LIBRA_OK : LIBRA_EHIP;
+}
+
+extern "C" libra_status libra_device_clock_khz(int32_t *khz) {
+  if (!khz) return LIBRA_EINVAL;
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LIBRA_EHIP;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return LIBRA_EHIP;
+  *khz = v;
+  return LIBRA_OK;
+}

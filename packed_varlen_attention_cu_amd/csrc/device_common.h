@@ -1,0 +1,108 @@
+// Device-side building blocks for gfx950 (CDNA4) attention kernels.
+//
+// Matrix products use v_mfma_f32_32x32x16_bf16: A is 32x16, B is 16x32, both
+// bf16; C/D is 32x32 fp32.  Per lane l (wave of 64):
+//   A operand: row l % 32, eight reduction elements of group l / 32;
+//   B operand: column l % 32, eight reduction elements of group l / 32;
+//   C/D: column l % 32, rows 8 * (r / 4) + 4 * (l / 32) + (r % 4), r = 0..15.
+// The kernels only assume that A and B place the reduction index the same
+// way, so every operand below is loaded with reduction element (l / 32, i) =
+// index 8 * (l / 32) + i of a 16-wide slab.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace libra {
+
+typedef __bf16 bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ u32x4 zero_u32x4() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return z;
+}
+
+// Two fp32 values rounded to bf16 (nearest even) and packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// The two fp32 values a packed bf16 pair stands for.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Combine a per-lane value with the same lane of the other 32-lane half.
+__device__ __forceinline__ float halves_max(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0; }
+
+// Start of the sample that contains token q: the largest cu[j] <= q, j < n.
+__device__ __forceinline__ int segment_start(const int32_t *__restrict__ cu, int n, int q) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= q) lo = mid; else hi = mid;
+  }
+  return cu[lo];
+}
+
+// End of the sample that contains token k: the smallest cu[j] > k, j <= n.
+__device__ __forceinline__ int segment_end(const int32_t *__restrict__ cu, int n, int k) {
+  int lo = 0, hi = n;   // cu[lo] <= k < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= k) lo = mid; else hi = mid;
+  }
+  return cu[hi];
+}
+
+// Physical placement of the running wave, for per-CU busy records.
+__device__ __forceinline__ uint32_t hw_id_reg() {
+  return __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4);    // HW_REG_HW_ID
+}
+__device__ __forceinline__ uint32_t xcc_id_reg() {
+  return __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 20);   // HW_REG_XCC_ID
+}
+
+// Row m of a 32-row C tile produced from A rows loaded in the order sigma:
+// sigma swaps bits 2 and 3, so C registers 8t..8t+7 of lane half h hold
+// A rows 16t + 8h + 0..7 (contiguous), ready to be a B operand.
+__device__ __forceinline__ int sigma_row(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+}  // namespace libra

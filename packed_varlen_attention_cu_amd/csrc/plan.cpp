@@ -1,0 +1,337 @@
+// Host SH-Tile planner and FLOPs-aware work placement.
+//
+// SH-Tiles follow the Libra technical review, section 5: the packed sequence
+// is cut at global token positions into blocks of at most B tokens and the
+// query heads into shards of W heads (eq. 6); a tile's KV groups are the
+// samples its block intersects (eq. 7); its cost is the exact number of
+// unmasked causal pairs, sum over those samples of sum_{q=a}^{e-1} (q + 1),
+// times W (eq. 8).  Algorithm 2 (section 5.4) places work heaviest first on
+// the least-loaded worker under a soft target C = (1 + tau) * mean.
+//
+// On one GPU the workers are the CUs, every tensor is already in HBM (the
+// communication term of eq. 9 is zero), and a tile is cut into work items a
+// single workgroup of four 64-query waves executes (see libra.h).  With a zero
+// communication term both branches of Algorithm 2 pick the worker of least
+// (load, id) -- whenever any worker fits under C the least loaded one does --
+// so the placement is a binary heap keyed by (load, worker id).
+//
+// Everything here is integer arithmetic and bitwise deterministic.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <functional>
+#include <queue>
+#include <vector>
+
+#include "libra.h"
+#include "plan_layout.h"
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kWaveQueries = 64;
+constexpr int kItemColumns = kWaves * kWaveQueries;  // query positions x heads
+constexpr int kKvChunk = 128;                        // keys per dK/dV item
+constexpr int kDefaultCus = 256;
+constexpr int kMaxCus = 1 << 16;
+
+// sum_{q=a}^{e-1} (q + 1) for sample-local query positions a <= e.
+inline int64_t triangle(int64_t a, int64_t e) { return (e * (e + 1) - a * (a + 1)) / 2; }
+
+// Per-head causal pairs of query rows [lo, hi); `j` walks forward over samples.
+int64_t query_pairs(const int32_t *cu, int n, int64_t lo, int64_t hi, int *j) {
+  while (*j < n && cu[*j + 1] <= lo) ++*j;
+  int64_t pairs = 0;
+  for (int s = *j; s < n && cu[s] < hi; ++s) {
+    int64_t a = std::max<int64_t>(lo, cu[s]), e = std::min<int64_t>(hi, cu[s + 1]);
+    if (a < e) pairs += triangle(a - cu[s], e - cu[s]);
+  }
+  return pairs;
+}
+
+// Per-head pairs seen from keys [lo, hi): each key k pairs with queries k..end(k)-1.
+int64_t key_pairs(const int32_t *cu, int n, int64_t lo, int64_t hi, int *j) {
+  while (*j < n && cu[*j + 1] <= lo) ++*j;
+  int64_t pairs = 0;
+  for (int s = *j; s < n && cu[s] < hi; ++s) {
+    int64_t a = std::max<int64_t>(lo, cu[s]), b = std::min<int64_t>(hi, cu[s + 1]);
+    if (a < b) pairs += (b - a) * (int64_t)cu[s + 1] - (a + b - 1) * (b - a) / 2;
+  }
+  return pairs;
+}
+
+int head_group(int n) { return n % 4 == 0 ? 4 : (n % 2 == 0 ? 2 : 1); }
+
+libra_status validate(const int32_t *cu, const libra_plan_params *p) {
+  if (!cu || !p) return LIBRA_EINVAL;
+  if (p->total_tokens < 0 || p->num_samples < 0) return LIBRA_EINVAL;
+  if (p->h_q <= 0 || p->h_kv <= 0 || p->h_q % p->h_kv) return LIBRA_EINVAL;
+  if (p->tile_tokens <= 0 || p->tile_heads <= 0 || p->h_q % p->tile_heads) return LIBRA_EINVAL;
+  if (p->num_cus < 0 || p->num_cus > kMaxCus) return LIBRA_EINVAL;
+  if (!(p->tau >= 0.0f) || !std::isfinite(p->tau)) return LIBRA_EINVAL;
+  if (p->assign != LIBRA_ASSIGN_PLACER && p->assign != LIBRA_ASSIGN_ROUND_ROBIN) return LIBRA_EINVAL;
+  if (p->item_overhead < 0) return LIBRA_EINVAL;
+  if (cu[0] != 0) return LIBRA_EINVAL;
+  for (int j = 0; j < p->num_samples; ++j)
+    if (cu[j + 1] < cu[j]) return LIBRA_EINVAL;
+  if (cu[p->num_samples] != p->total_tokens) return LIBRA_EINVAL;
+  if (p->head_dim != 64 && p->head_dim != 128) return LIBRA_EUNSUPPORTED;
+  return LIBRA_OK;
+}
+
+struct Queue {
+  std::vector<libra_item> items;   // in CU order
+  std::vector<int32_t> cu_off;
+  int64_t load_max = 0, load_sum = 0;
+};
+
+// Algorithm 2 with a zero communication term (or round-robin), emitted as CSR.
+Queue place(std::vector<libra_item> units, int workers, float tau, int mode) {
+  (void)tau;  // the soft target cannot change the choice when dcomm == 0
+  Queue q;
+  const size_t n = units.size();
+  std::vector<int32_t> worker(n);
+  std::vector<int32_t> order(n);
+  for (size_t i = 0; i < n; ++i) order[i] = (int32_t)i;
+  std::vector<int64_t> load(workers, 0);
+  if (mode == LIBRA_ASSIGN_PLACER) {
+    std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+      return units[a].cost != units[b].cost ? units[a].cost > units[b].cost : a < b;
+    });
+    using Entry = std::pair<int64_t, int32_t>;  // (load, worker)
+    std::priority_queue<Entry, std::vector<Entry>, std::greater<Entry>> heap;
+    for (int32_t r = 0; r < workers; ++r) heap.push({0, r});
+    for (int32_t t : order) {
+      Entry e = heap.top();
+      heap.pop();
+      worker[t] = e.second;
+      e.first += units[t].cost;
+      load[e.second] = e.first;
+      heap.push(e);
+    }
+  } else {
+    for (size_t t = 0; t < n; ++t) {
+      worker[t] = (int32_t)(t % workers);
+      load[worker[t]] += units[t].cost;
+    }
+  }
+  q.cu_off.assign(workers + 1, 0);
+  for (size_t t = 0; t < n; ++t) q.cu_off[worker[t] + 1]++;
+  for (int r = 0; r < workers; ++r) q.cu_off[r + 1] += q.cu_off[r];
+  std::vector<int32_t> fill(q.cu_off.begin(), q.cu_off.end() - 1);
+  q.items.resize(n);
+  for (int32_t t : order) q.items[fill[worker[t]]++] = units[t];
+  for (int r = 0; r < workers; ++r) {
+    q.load_max = std::max(q.load_max, load[r]);
+    q.load_sum += load[r];
+  }
+  return q;
+}
+
+size_t align64(size_t x) { return (x + 63) & ~size_t(63); }
+
+uint64_t fnv1a_words(const void *buf, size_t bytes) {
+  const uint64_t *w = static_cast<const uint64_t *>(buf);
+  uint64_t h = 0xcbf29ce484222325ull;
+  for (size_t i = 0; i < bytes / 8; ++i) {
+    h ^= w[i];
+    h *= 0x100000001b3ull;
+  }
+  return h;
+}
+
+}  // namespace
+
+namespace libra {
+
+uint64_t plan_checksum(const void *plan, size_t bytes) {
+  libra_plan_info hdr;
+  std::memcpy(&hdr, plan, sizeof hdr);
+  hdr.checksum = 0;
+  uint64_t h = fnv1a_words(&hdr, sizeof hdr);
+  const char *p = static_cast<const char *>(plan);
+  uint64_t rest = fnv1a_words(p + sizeof hdr, bytes - sizeof hdr);
+  return h ^ (rest * 0x9e3779b97f4a7c15ull);
+}
+
+libra_status plan_header(const void *plan, libra_plan_info *out) {
+  if (!plan) return LIBRA_EINVAL;
+  std::memcpy(out, plan, sizeof *out);
+  if (out->magic != LIBRA_PLAN_MAGIC || out->version != LIBRA_PLAN_VERSION) return LIBRA_EINVAL;
+  return LIBRA_OK;
+}
+
+}  // namespace libra
+
+extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *pp, void *buf,
+                                   size_t *bytes) {
+  if (!bytes) return LIBRA_EINVAL;
+  libra_status st = validate(cu, pp);
+  if (st != LIBRA_OK) return st;
+  libra_plan_params p = *pp;
+  const int workers = p.num_cus ? p.num_cus : kDefaultCus;
+  const int n = p.num_samples;
+  const int64_t L = p.total_tokens;
+  const int g = p.h_q / p.h_kv;
+  const int S = p.h_q / p.tile_heads;
+  const int64_t nblocks = (L + p.tile_tokens - 1) / p.tile_tokens;
+
+  // Tiles (eq. 6-8) and forward items.
+  std::vector<libra_tile> tiles;
+  std::vector<libra_item> items;
+  tiles.reserve(nblocks * S);
+  int jb = 0;
+  for (int64_t b = 0; b < nblocks; ++b) {
+    const int64_t lo = b * p.tile_tokens, hi = std::min<int64_t>(L, lo + p.tile_tokens);
+    const int64_t per_head = query_pairs(cu, n, lo, hi, &jb);
+    // K(t): the non-empty samples the block meets (all samples from jb end after lo).
+    int first = -1, last = -1;
+    for (int s = jb; s < n && cu[s] < hi; ++s) {
+      if (cu[s + 1] == cu[s]) continue;
+      if (first < 0) first = s;
+      last = s;
+    }
+    for (int s = 0; s < S; ++s) {
+      libra_tile t{};
+      t.tile_id = (int32_t)(b * S + s);
+      t.block = (int32_t)b;
+      t.shard = s;
+      t.tok_begin = (int32_t)lo;
+      t.tok_end = (int32_t)hi;
+      t.head_begin = s * p.tile_heads;
+      t.head_count = p.tile_heads;
+      t.sample_first = first;
+      t.sample_last = last;
+      t.pairs = per_head * p.tile_heads;
+      const int h_lo = t.head_begin, h_hi = h_lo + p.tile_heads;
+      int32_t made = 0;
+      for (int kv = h_lo / g; kv <= (h_hi - 1) / g; ++kv) {
+        const int a = std::max(h_lo, kv * g), e = std::min(h_hi, (kv + 1) * g);
+        const int nh = head_group(e - a);
+        const int rows = kItemColumns / nh;
+        for (int gi = 0; gi < (e - a) / nh; ++gi) {
+          int ji = jb;
+          for (int64_t r0 = lo; r0 < hi; r0 += rows) {
+            const int64_t r1 = std::min<int64_t>(hi, r0 + rows);
+            libra_item it{};
+            it.row0 = (int32_t)r0;
+            it.nrows = (int32_t)(r1 - r0);
+            it.kv_head = kv;
+            it.head0 = a + gi * nh;
+            it.nheads = nh;
+            it.tile_id = t.tile_id;
+            it.id = (int32_t)items.size();
+            it.pairs = nh * query_pairs(cu, n, r0, r1, &ji);
+            it.cost = it.pairs + p.item_overhead;
+            items.push_back(it);
+            ++made;
+          }
+        }
+      }
+      t.n_items = made;
+      tiles.push_back(t);
+    }
+  }
+
+  // Key-major dK/dV items: chunks of 128 keys, all g query heads of a KV head.
+  std::vector<libra_item> kv_items;
+  const int64_t nchunks = (L + kKvChunk - 1) / kKvChunk;
+  kv_items.reserve(nchunks * p.h_kv);
+  int jk = 0;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t lo = c * kKvChunk, hi = std::min<int64_t>(L, lo + kKvChunk);
+    const int64_t per_head = key_pairs(cu, n, lo, hi, &jk);
+    for (int kv = 0; kv < p.h_kv; ++kv) {
+      libra_item it{};
+      it.row0 = (int32_t)lo;
+      it.nrows = (int32_t)(hi - lo);
+      it.kv_head = kv;
+      it.head0 = kv * g;
+      it.nheads = g;
+      it.tile_id = -1;
+      it.id = (int32_t)kv_items.size();
+      it.pairs = g * per_head;
+      it.cost = it.pairs + p.item_overhead;
+      kv_items.push_back(it);
+    }
+  }
+
+  Queue fq = place(items, workers, p.tau, p.assign);
+  Queue kq = place(kv_items, workers, p.tau, p.assign);
+
+  libra_plan_info hdr{};
+  hdr.magic = LIBRA_PLAN_MAGIC;
+  hdr.version = LIBRA_PLAN_VERSION;
+  hdr.params = p;
+  hdr.num_cus = workers;
+  hdr.n_tiles = (int32_t)tiles.size();
+  hdr.n_items = (int32_t)items.size();
+  hdr.n_kv_items = (int32_t)kv_items.size();
+  for (const auto &t : tiles) hdr.total_pairs += t.pairs;
+  hdr.load_max = fq.load_max;
+  hdr.load_sum = fq.load_sum;
+  hdr.kv_load_max = kq.load_max;
+  hdr.kv_load_sum = kq.load_sum;
+  size_t off = align64(sizeof(libra_plan_info));
+  hdr.off_tiles = off;
+  off = align64(off + tiles.size() * sizeof(libra_tile));
+  hdr.off_items = off;
+  off = align64(off + fq.items.size() * sizeof(libra_item));
+  hdr.off_cu_off = off;
+  off = align64(off + fq.cu_off.size() * sizeof(int32_t));
+  hdr.off_kv_items = off;
+  off = align64(off + kq.items.size() * sizeof(libra_item));
+  hdr.off_kv_cu_off = off;
+  off = align64(off + kq.cu_off.size() * sizeof(int32_t));
+  hdr.bytes = off;
+
+  if (!buf) {
+    *bytes = off;
+    return LIBRA_OK;
+  }
+  if (*bytes < off || (reinterpret_cast<uintptr_t>(buf) & 7)) {
+    *bytes = off;
+    return (reinterpret_cast<uintptr_t>(buf) & 7) ? LIBRA_EINVAL : LIBRA_ESIZE;
+  }
+  char *out = static_cast<char *>(buf);
+  std::memset(out, 0, off);
+  std::memcpy(out + hdr.off_tiles, tiles.data(), tiles.size() * sizeof(libra_tile));
+  std::memcpy(out + hdr.off_items, fq.items.data(), fq.items.size() * sizeof(libra_item));
+  std::memcpy(out + hdr.off_cu_off, fq.cu_off.data(), fq.cu_off.size() * sizeof(int32_t));
+  std::memcpy(out + hdr.off_kv_items, kq.items.data(), kq.items.size() * sizeof(libra_item));
+  std::memcpy(out + hdr.off_kv_cu_off, kq.cu_off.data(), kq.cu_off.size() * sizeof(int32_t));
+  std::memcpy(out, &hdr, sizeof hdr);
+  hdr.checksum = libra::plan_checksum(out, off);
+  std::memcpy(out, &hdr, sizeof hdr);
+  *bytes = off;
+  return LIBRA_OK;
+}
+
+extern "C" libra_status libra_plan_check(const void *plan, size_t bytes, libra_plan_info *info) {
+  libra_plan_info hdr;
+  if (!plan || bytes < sizeof hdr) return LIBRA_EINVAL;
+  if (libra::plan_header(plan, &hdr) != LIBRA_OK) return LIBRA_EINVAL;
+  if (hdr.bytes != bytes) return LIBRA_EINVAL;
+  const uint64_t ends[] = {
+      hdr.off_tiles + (uint64_t)hdr.n_tiles * sizeof(libra_tile),
+      hdr.off_items + (uint64_t)hdr.n_items * sizeof(libra_item),
+      hdr.off_cu_off + (uint64_t)(hdr.num_cus + 1) * sizeof(int32_t),
+      hdr.off_kv_items + (uint64_t)hdr.n_kv_items * sizeof(libra_item),
+      hdr.off_kv_cu_off + (uint64_t)(hdr.num_cus + 1) * sizeof(int32_t)};
+  for (uint64_t e : ends)
+    if (e > bytes) return LIBRA_EINVAL;
+  if (libra::plan_checksum(plan, bytes) != hdr.checksum) return LIBRA_EINVAL;
+  if (info) *info = hdr;
+  return LIBRA_OK;
+}
+
+extern "C" const char *libra_status_str(libra_status s) {
+  switch (s) {
+    case LIBRA_OK: return "ok";
+    case LIBRA_EINVAL: return "invalid argument";
+    case LIBRA_ESIZE: return "buffer too small";
+    case LIBRA_EUNSUPPORTED: return "unsupported configuration";
+    case LIBRA_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}

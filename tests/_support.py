@@ -1,0 +1,170 @@
+"""Shared helpers for the GPU parity tests: inputs from ``synth``, references from ``oracle``."""
+from __future__ import annotations
+
+import math
+import os
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+import synth
+
+# Tolerances.  Outputs: max |err| <= 2e-2 and mean |err| <= 2e-3 against the
+# fp64 oracle; gradients: max |err| / max |ref| <= 5e-2 per tensor.  LSE has
+# no stated bound: it is fp32 with l summed from bf16-rounded weights, whose
+# relative error is at most 2^-9, so |d LSE| <= 2^-9 plus fp32 rounding; the
+# tests allow 5e-3.
+O_MAX, O_MEAN = 2e-2, 2e-3
+LSE_MAX = 5e-3
+GRAD_REL = 5e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(bits: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def from_dev_bf16(t) -> np.ndarray:
+    import torch
+    return synth.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+
+
+def bits_of(t) -> np.ndarray:
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def make_plan(w: synth.Workload, cu, **kw):
+    import packed_varlen_attention_cu_amd as lib
+    return lib.Plan(cu, total_tokens=w.total_tokens, h_q=w.h_q, h_kv=w.h_kv, head_dim=w.head_dim,
+                    tile_tokens=kw.pop("tile_tokens", w.tile_tokens),
+                    tile_heads=kw.pop("tile_heads", w.tile_heads), **kw)
+
+
+def scale_of(w):
+    return 1.0 / math.sqrt(w.head_dim)
+
+
+def check_out(o_gpu, o_ref, what=""):
+    err = np.abs(o_gpu - o_ref)
+    mx, mean = float(err.max()), float(err.mean())
+    say(f"  {what} out max|err| {mx:.3e} mean|err| {mean:.3e}")
+    assert np.isfinite(o_gpu).all(), f"{what}: non-finite output"
+    assert mx <= O_MAX, f"{what}: max|err| {mx} > {O_MAX}"
+    assert mean <= O_MEAN, f"{what}: mean|err| {mean} > {O_MEAN}"
+
+
+def check_lse(l_gpu, l_ref, what=""):
+    err = float(np.abs(l_gpu - l_ref).max())
+    say(f"  {what} lse max|err| {err:.3e}")
+    assert np.isfinite(l_gpu).all()
+    assert err <= LSE_MAX, f"{what}: lse max|err| {err} > {LSE_MAX}"
+
+
+def check_grad(g_gpu, g_ref, what=""):
+    scale = float(np.abs(g_ref).max())
+    err = float(np.abs(g_gpu - g_ref).max())
+    rel = err / max(scale, 1e-30)
+    fro = float(np.linalg.norm(g_gpu - g_ref) / max(np.linalg.norm(g_ref), 1e-30))
+    say(f"  {what} grad max|err|/max|ref| {rel:.3e} (max|ref| {scale:.3e}) rel-fro {fro:.3e}")
+    assert np.isfinite(g_gpu).all(), f"{what}: non-finite gradient"
+    assert rel <= GRAD_REL, f"{what}: {rel} > {GRAD_REL}"
+
+
+# ------------------------------------------------------------ oracle in worker threads
+# (numpy releases the GIL inside large array operations; threads avoid forking a
+# process that has initialised the GPU)
+def _pool(n):
+    return ThreadPoolExecutor(max_workers=n)
+
+
+def workers():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _fwd_rows_job(args):
+    import oracle.attention as A
+    qr, kp, vp, rows, scale, h_kv = args       # qr [n, h_q, d]; kp/vp [m, h_kv, d]
+    h_q = qr.shape[1]
+    o = np.zeros(qr.shape)
+    lse = np.zeros((h_q, qr.shape[0]))
+    for h in range(h_q):
+        kv = A.kv_head(h, h_q, h_kv)
+        o[:, h], lse[h] = A.attend_rows(qr[:, h], kp[:, kv], vp[:, kv], rows, scale)
+    return o, lse
+
+
+def oracle_fwd_rows(qb, kb, vb, cu, scale, rows, chunk=64):
+    """O [n, h_q, d] and LSE [h_q, n] of the given global rows, from the oracle.
+
+    Rows are grouped by sample; each job gets only its query rows and the
+    key/value prefix those rows can see (widened once per sample).
+    """
+    import oracle.attention as A
+    rows = np.asarray(sorted(set(int(r) for r in rows)), dtype=np.int64)
+    cu = np.asarray(cu, dtype=np.int64)
+    jobs, order = [], []
+    j_of = np.searchsorted(cu, rows, side="right") - 1
+    for j in np.unique(j_of):
+        s = int(cu[j])
+        rj = rows[j_of == j]
+        m_all = int(rj.max() - s) + 1
+        kp, vp = A.widen_bf16(kb[s:s + m_all]), A.widen_bf16(vb[s:s + m_all])
+        for part in np.array_split(rj, (rj.size + chunk - 1) // chunk):
+            local = part - s
+            m = int(local.max()) + 1
+            jobs.append((A.widen_bf16(qb[part]), kp[:m], vp[:m], local, scale, kb.shape[1]))
+            order.append(part)
+    outs_o, outs_l = [], []
+    with _pool(workers()) as ex:
+        for o, l in ex.map(_fwd_rows_job, jobs):
+            outs_o.append(o)
+            outs_l.append(l)
+    got_rows = np.concatenate(order)
+    perm = np.argsort(got_rows)
+    return got_rows[perm], np.concatenate(outs_o, axis=0)[perm], np.concatenate(outs_l, axis=1)[:, perm]
+
+
+def _bwd_tail_job(args):
+    import oracle.attention as A
+    q, k, v, do, kv, first, scale = args
+    n = q.shape[0]
+    return A.backward_tail(q, k, v, do, 0, n, kv, first, scale)
+
+
+def oracle_bwd_tails(qb, kb, vb, dob, cu, scale, units):
+    """Backward of (sample j, kv head, first row) units; returns a list of (dq, dk, dv)."""
+    import oracle.attention as A
+    jobs = []
+    for j, kv, first in units:
+        s, e = int(cu[j]), int(cu[j + 1])
+        jobs.append((A.widen_bf16(qb[s:e]), A.widen_bf16(kb[s:e]), A.widen_bf16(vb[s:e]),
+                     A.widen_bf16(dob[s:e]), kv, first, scale))
+    with _pool(workers()) as ex:
+        return list(ex.map(_bwd_tail_job, jobs))
+
+
+def sample_rows(cu, tile_tokens, n_random, seed, long_len=4096, edge=32, boundary_stride=1):
+    """Rows to check at full size: edges of long samples, tile boundaries, random rows."""
+    rng = np.random.default_rng(seed)
+    cu = np.asarray(cu, dtype=np.int64)
+    L = int(cu[-1])
+    rows = set()
+    for j in range(len(cu) - 1):
+        s, e = int(cu[j]), int(cu[j + 1])
+        if e - s >= long_len:
+            rows.update(range(s, min(e, s + edge)))
+            rows.update(range(max(s, e - edge), e))
+        elif e > s:
+            rows.add(s)
+            rows.add(e - 1)
+    for b in range(tile_tokens, L, tile_tokens * boundary_stride):
+        rows.update((b - 1, b))
+    rows.update(int(x) for x in rng.integers(0, L, size=n_random))
+    return np.array(sorted(r for r in rows if 0 <= r < L), dtype=np.int64)

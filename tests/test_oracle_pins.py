@@ -251,11 +251,9 @@ def test_rejects_bad_cu_seqlens():
 
 # ---------------------------------------------------- planted slips are caught
 def _mutant_scores(offset):
-    def scores(Qr, K, rows0, scale):
+    def scores(Qr, K, rows, scale):
         S = scale * (Qr @ K.T)
-        i = np.arange(rows0, rows0 + Qr.shape[0])[:, None]
-        kk = np.arange(K.shape[0])[None, :]
-        S[kk > i + offset] = -np.inf
+        S[np.arange(K.shape[0])[None, :] > np.asarray(rows)[:, None] + offset] = -np.inf
         return S
     return scores
 
