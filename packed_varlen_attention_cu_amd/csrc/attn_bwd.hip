@@ -1,18 +1,506 @@
-// Backward pass (placeholder until the kernels land).
+// Backward packed block-diagonal causal attention on gfx950 (CDNA4).
+//
+// Gradients of O = softmax(scale Q K^T + mask) V for the block-diagonal
+// causal mask (Libra technical review, section 1 "Sequence packing"; the
+// pages leave the backward to the attention kernel and state only that it
+// reuses the forward placement with reversed transfers, Libra paper section
+// 4.3.3).  With P = exp(scale S - LSE) recomputed from the forward's LSE:
+//   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Work is split into two deterministic persistent passes (no atomics):
+//   * key-major dK/dV: an item is 128 keys of one KV head; each wave owns 32
+//     keys and walks every query block of every query head of the group that
+//     can see them, accumulating dK^T and dV^T in registers (GQA heads are
+//     summed in place);
+//   * query-major dQ: the forward's items and CU assignment, each wave owning
+//     64 query positions of one head and walking its key blocks.
+// Q, dO and K are transposed once per call into the workspace so that every
+// MFMA operand is 16 contiguous bytes per lane in LDS; D = rowsum(dO * O)
+// (fp32) is computed first from the forward's bf16 O.
 #include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "device_common.h"
 #include "libra.h"
 #include "plan_layout.h"
 
+namespace libra {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kQB = 64;      // query rows per block in the dK/dV pass
+constexpr int kKB = 32;      // key rows per block in the dQ pass
+
+inline int64_t round_up64(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// D[h][t] = sum_d dO[t][h][d] * O[t][h][d], one row per D/8 lanes.
+template <int D>
+__global__ __launch_bounds__(kThreads) void rowdot_kernel(const uint16_t *__restrict__ o,
+                                                          const uint16_t *__restrict__ dout,
+                                                          float *__restrict__ dvec, int L, int h_q) {
+  constexpr int LPR = D / 8;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  const int64_t rows = (int64_t)L * h_q;
+  float acc = 0.0f;
+  if (row < rows) {
+    const u32x4 x = *reinterpret_cast<const u32x4 *>(o + row * D + sub * 8);
+    const u32x4 y = *reinterpret_cast<const u32x4 *>(dout + row * D + sub * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += bf16_lo(x[i]) * bf16_lo(y[i]) + bf16_hi(x[i]) * bf16_hi(y[i]);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (sub == 0 && row < rows) {
+    const int64_t t = row / h_q, h = row % h_q;
+    dvec[h * L + t] = acc;
+  }
+}
+
+struct BwdArgs {
+  const libra_item *items;     // dK/dV: key-major queue; dQ: forward queue
+  const int32_t *cu_off;
+  const uint16_t *q, *k, *v, *dout;
+  const uint16_t *qt, *dot, *kt;   // transposed [heads][D][Lp]
+  const float *lse, *dvec;         // [h_q][L]
+  const int32_t *cu;
+  uint16_t *dq, *dk, *dv;
+  libra_cu_record *records;
+  int n_samples, L, Lp, h_q, h_kv;
+  float scale, scale_log2;
+};
+
+__device__ __forceinline__ void write_record(const BwdArgs &a, int w, int n, uint64_t t0) {
+  libra_cu_record rec;
+  rec.hw_id = hw_id_reg();
+  rec.xcc_id = xcc_id_reg();
+  rec.n_items = (uint32_t)n;
+  rec.reserved = 0;
+  rec.t_start = t0;
+  rec.t_end = wall_clock64();
+  a.records[w] = rec;
+}
+
+// ----------------------------------------------------------------- dK / dV pass
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NS = D / 16, ND = D / 32;
+  constexpr int RS = D + 8;            // row stride of Q / dO blocks (elements)
+  constexpr int TS = kQB + 8;          // row stride of Q^T / dO^T blocks
+  constexpr int RCH = kQB * D / 8 / kThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kQB * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t do_lds[kQB * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[D * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t dot_lds[D * TS];
+  __shared__ __attribute__((aligned(16))) float lse_lds[kQB];
+  __shared__ __attribute__((aligned(16))) float dd_lds[kQB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int w = blockIdx.x;
+  const uint64_t t_start = wall_clock64();
+  const int beg = a.cu_off[w], end = a.cu_off[w + 1];
+  const float c = a.scale_log2;
+
+  for (int it = beg; it < end; ++it) {
+    const libra_item item = a.items[it];
+    const int row0 = item.row0, nrows = item.nrows, kvh = item.kv_head;
+    const int kloc = wave * 32 + col;
+    const bool kok = kloc < nrows;
+    const int key = row0 + kloc;
+    const int kend = kok ? segment_end(a.cu, a.n_samples, key) : 0;   // queries [key, kend)
+
+    bf16x8 kop[NS], vop[NS];
+    {
+      const int64_t base = ((int64_t)key * a.h_kv + kvh) * D + 8 * half;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        kop[s] = as_bf16x8(kok ? *reinterpret_cast<const u32x4 *>(a.k + base + 16 * s) : zero_u32x4());
+        vop[s] = as_bf16x8(kok ? *reinterpret_cast<const u32x4 *>(a.v + base + 16 * s) : zero_u32x4());
+      }
+    }
+    const int qstart = row0 & ~(kQB - 1);
+    const int qend = segment_end(a.cu, a.n_samples, row0 + nrows - 1);
+    const int nqb = (qend - qstart + kQB - 1) / kQB;
+
+    f32x16 dkacc[ND], dvacc[ND];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      dkacc[dt] = zero16();
+      dvacc[dt] = zero16();
+    }
+
+    for (int hh = 0; hh < item.nheads; ++hh) {
+      const int h = item.head0 + hh;
+      for (int qb = 0; qb < nqb; ++qb) {
+        const int q0 = qstart + qb * kQB;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < RCH; ++j) {
+          const int cidx = tid + kThreads * j;
+          const int r = cidx / (D / 8), cc = cidx % (D / 8);
+          const int qq = q0 + r;
+          const int64_t g = ((int64_t)qq * a.h_q + h) * D + cc * 8;
+          const bool ok = qq < a.L;
+          *reinterpret_cast<u32x4 *>(q_lds + r * RS + cc * 8) =
+              ok ? *reinterpret_cast<const u32x4 *>(a.q + g) : zero_u32x4();
+          *reinterpret_cast<u32x4 *>(do_lds + r * RS + cc * 8) =
+              ok ? *reinterpret_cast<const u32x4 *>(a.dout + g) : zero_u32x4();
+          const int d = cidx / (kQB / 8), tc = cidx % (kQB / 8);
+          const int64_t gt = ((int64_t)h * D + d) * a.Lp + q0 + tc * 8;
+          *reinterpret_cast<u32x4 *>(qt_lds + d * TS + tc * 8) = *reinterpret_cast<const u32x4 *>(a.qt + gt);
+          *reinterpret_cast<u32x4 *>(dot_lds + d * TS + tc * 8) = *reinterpret_cast<const u32x4 *>(a.dot + gt);
+        }
+        if (tid < kQB) {
+          const int qq = q0 + tid;
+          const bool ok = qq < a.L;
+          lse_lds[tid] = ok ? a.lse[(int64_t)h * a.L + qq] * kLog2e : 0.0f;
+          dd_lds[tid] = ok ? a.dvec[(int64_t)h * a.L + qq] : 0.0f;
+        }
+        __syncthreads();
+
+        const bool touch = kok && (q0 + kQB - 1 >= key) && (q0 < kend);
+        const bool full = !kok || ((key <= q0) && (q0 + kQB - 1 < kend));
+        if (!wave_any(touch)) continue;
+        const bool masked = wave_any(!full);
+
+        f32x16 sacc[2], pacc[2];   // per 32-query tile: S and dP, C layout (lane = key)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          sacc[qt] = zero16();
+          pacc[qt] = zero16();
+          const int arow = (qt * 32 + sigma_row(col)) * RS + 8 * half;
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4 *>(q_lds + arow + 16 * s));
+            const bf16x8 da = as_bf16x8(*reinterpret_cast<const u32x4 *>(do_lds + arow + 16 * s));
+            sacc[qt] = mfma32x32x16(qa, kop[s], sacc[qt]);
+            pacc[qt] = mfma32x32x16(da, vop[s], pacc[qt]);
+          }
+        }
+        u32x4 pw[2][2], dsw[2][2];   // [query tile][16-query slab]
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int ql = qt * 32 + 16 * t + 8 * half;   // first of 8 consecutive queries
+            const float4 l0 = *reinterpret_cast<const float4 *>(lse_lds + ql);
+            const float4 l1 = *reinterpret_cast<const float4 *>(lse_lds + ql + 4);
+            const float4 d0 = *reinterpret_cast<const float4 *>(dd_lds + ql);
+            const float4 d1 = *reinterpret_cast<const float4 *>(dd_lds + ql + 4);
+            const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+            const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+            float p[8], ds[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int r = 8 * t + i;
+              float pv = exp2_fast(fmaf(sacc[qt][r], c, -lv[i]));
+              if (masked) {
+                const int qq = q0 + ql + i;
+                if (!(kok && key <= qq && qq < kend)) pv = 0.0f;
+              }
+              p[i] = pv;
+              ds[i] = pv * (pacc[qt][r] - dv8[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              pw[qt][t][i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
+              dsw[qt][t][i] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
+            }
+          }
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int off = (dt * 32 + col) * TS + qt * 32 + 16 * t + 8 * half;
+              const bf16x8 oa = as_bf16x8(*reinterpret_cast<const u32x4 *>(dot_lds + off));
+              const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4 *>(qt_lds + off));
+              dvacc[dt] = mfma32x32x16(oa, as_bf16x8(pw[qt][t]), dvacc[dt]);
+              dkacc[dt] = mfma32x32x16(qa, as_bf16x8(dsw[qt][t]), dkacc[dt]);
+            }
+      }
+    }
+
+    if (kok) {
+      const int64_t base = ((int64_t)key * a.h_kv + kvh) * D;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const int d = dt * 32 + 8 * cc + 4 * half;
+          u32x2 kk, vv;
+          kk[0] = pack_bf16x2(dkacc[dt][4 * cc] * a.scale, dkacc[dt][4 * cc + 1] * a.scale);
+          kk[1] = pack_bf16x2(dkacc[dt][4 * cc + 2] * a.scale, dkacc[dt][4 * cc + 3] * a.scale);
+          vv[0] = pack_bf16x2(dvacc[dt][4 * cc], dvacc[dt][4 * cc + 1]);
+          vv[1] = pack_bf16x2(dvacc[dt][4 * cc + 2], dvacc[dt][4 * cc + 3]);
+          *reinterpret_cast<u32x2 *>(a.dk + base + d) = kk;
+          *reinterpret_cast<u32x2 *>(a.dv + base + d) = vv;
+        }
+    }
+  }
+  __syncthreads();
+  if (a.records != nullptr && tid == 0) write_record(a, w, end - beg, t_start);
+}
+
+// ----------------------------------------------------------------- dQ pass
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dq_kernel(BwdArgs a) {
+  constexpr int NS = D / 16, ND = D / 32;
+  constexpr int RS = D + 8;            // K / V block row stride
+  constexpr int TS = kKB + 8;          // K^T block row stride
+  constexpr int RCH = kKB * D / 8 / kThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKB * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kKB * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[D * TS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int w = blockIdx.x;
+  const uint64_t t_start = wall_clock64();
+  const int beg = a.cu_off[w], end = a.cu_off[w + 1];
+  const float c = a.scale_log2;
+
+  for (int it = beg; it < end; ++it) {
+    const libra_item item = a.items[it];
+    const int row0 = item.row0, nrows = item.nrows, kvh = item.kv_head, nh = item.nheads;
+    const int head = item.head0 + (wave % nh);
+    const int sub = wave / nh;
+    const int wrow0 = row0 + sub * 64;
+    const int wrows = min(64, nrows - sub * 64);
+
+    int qpos[2], qss[2];
+    bool qok[2];
+    float lse2[2], dd[2];
+    bf16x8 qop[2][NS], dop[2][NS];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int r = qt * 32 + col;
+      qok[qt] = r < wrows;
+      qpos[qt] = wrow0 + r;
+      qss[qt] = qok[qt] ? segment_start(a.cu, a.n_samples, qpos[qt]) : 0;
+      lse2[qt] = qok[qt] ? a.lse[(int64_t)head * a.L + qpos[qt]] * kLog2e : 0.0f;
+      dd[qt] = qok[qt] ? a.dvec[(int64_t)head * a.L + qpos[qt]] : 0.0f;
+      const int64_t base = ((int64_t)qpos[qt] * a.h_q + head) * D + 8 * half;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        qop[qt][s] = as_bf16x8(qok[qt] ? *reinterpret_cast<const u32x4 *>(a.q + base + 16 * s) : zero_u32x4());
+        dop[qt][s] = as_bf16x8(qok[qt] ? *reinterpret_cast<const u32x4 *>(a.dout + base + 16 * s) : zero_u32x4());
+      }
+    }
+    const int kstart = segment_start(a.cu, a.n_samples, row0) & ~(kKB - 1);
+    const int kend = row0 + nrows;
+    const int nkb = (kend - kstart + kKB - 1) / kKB;
+
+    f32x16 dqacc[2][ND];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) dqacc[qt][dt] = zero16();
+
+    for (int b = 0; b < nkb; ++b) {
+      const int k0 = kstart + b * kKB;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < RCH; ++j) {
+        const int cidx = tid + kThreads * j;
+        const int r = cidx / (D / 8), cc = cidx % (D / 8);
+        const int kk = k0 + r;
+        const int64_t g = ((int64_t)kk * a.h_kv + kvh) * D + cc * 8;
+        const bool ok = kk < a.L;
+        *reinterpret_cast<u32x4 *>(k_lds + r * RS + cc * 8) =
+            ok ? *reinterpret_cast<const u32x4 *>(a.k + g) : zero_u32x4();
+        *reinterpret_cast<u32x4 *>(v_lds + r * RS + cc * 8) =
+            ok ? *reinterpret_cast<const u32x4 *>(a.v + g) : zero_u32x4();
+        const int d = cidx / (kKB / 8), tc = cidx % (kKB / 8);
+        *reinterpret_cast<u32x4 *>(kt_lds + d * TS + tc * 8) =
+            *reinterpret_cast<const u32x4 *>(a.kt + ((int64_t)kvh * D + d) * a.Lp + k0 + tc * 8);
+      }
+      __syncthreads();
+
+      bool touch = false, partial = false;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        if (qok[qt]) {
+          touch |= (k0 <= qpos[qt]) && (k0 + kKB - 1 >= qss[qt]);
+          partial |= !((k0 >= qss[qt]) && (k0 + kKB - 1 <= qpos[qt]));
+        }
+      }
+      if (!wave_any(touch)) continue;
+      const bool masked = wave_any(partial);
+
+      const int arow = sigma_row(col) * RS + 8 * half;
+      f32x16 sacc[2], pacc[2];   // S^T and dP^T per query tile (lane = query)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        sacc[qt] = zero16();
+        pacc[qt] = zero16();
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(k_lds + arow + 16 * s));
+        const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(v_lds + arow + 16 * s));
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          sacc[qt] = mfma32x32x16(ka, qop[qt][s], sacc[qt]);
+          pacc[qt] = mfma32x32x16(va, dop[qt][s], pacc[qt]);
+        }
+      }
+      u32x4 dsw[2][2];   // [query tile][16-key slab]
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const int lo = qok[qt] ? qss[qt] : 1, hi = qok[qt] ? qpos[qt] : 0;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float ds2[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int r = 8 * t + 2 * i + e;
+              float pv = exp2_fast(fmaf(sacc[qt][r], c, -lse2[qt]));
+              if (masked) {
+                const int kk = k0 + 16 * t + 8 * half + 2 * i + e;
+                if (kk < lo || kk > hi) pv = 0.0f;
+              }
+              ds2[e] = pv * (pacc[qt][r] - dd[qt]);
+            }
+            dsw[qt][t][i] = pack_bf16x2(ds2[0], ds2[1]);
+          }
+      }
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+              kt_lds + (dt * 32 + col) * TS + 16 * t + 8 * half));
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) dqacc[qt][dt] = mfma32x32x16(ka, as_bf16x8(dsw[qt][t]), dqacc[qt][dt]);
+        }
+    }
+
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      if (!qok[qt]) continue;
+      uint16_t *op = a.dq + ((int64_t)qpos[qt] * a.h_q + head) * D;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          u32x2 pk;
+          pk[0] = pack_bf16x2(dqacc[qt][dt][4 * cc] * a.scale, dqacc[qt][dt][4 * cc + 1] * a.scale);
+          pk[1] = pack_bf16x2(dqacc[qt][dt][4 * cc + 2] * a.scale, dqacc[qt][dt][4 * cc + 3] * a.scale);
+          *reinterpret_cast<u32x2 *>(op + dt * 32 + 8 * cc + 4 * half) = pk;
+        }
+    }
+  }
+  __syncthreads();
+  if (a.records != nullptr && tid == 0) write_record(a, w, end - beg, t_start);
+}
+
+struct BwdLayout {
+  size_t qt, dot, kt, dvec, total;
+};
+
+BwdLayout bwd_layout(const libra_plan_params &p) {
+  BwdLayout l;
+  l.qt = 0;
+  l.dot = l.qt + transposed_bytes(p.h_q, p.head_dim, p.total_tokens);
+  l.kt = l.dot + transposed_bytes(p.h_q, p.head_dim, p.total_tokens);
+  l.dvec = l.kt + transposed_bytes(p.h_kv, p.head_dim, p.total_tokens);
+  l.total = l.dvec + (size_t)round_up64((int64_t)p.h_q * p.total_tokens * 4, 256);
+  return l;
+}
+
+template <int D>
+libra_status launch_bwd(const libra_plan_info &h, BwdArgs a, const char *plan_dev, const void *o,
+                        hipStream_t s) {
+  const libra_plan_params &p = h.params;
+  const int64_t rows = (int64_t)p.total_tokens * p.h_q;
+  const int rows_per_block = kThreads / (D / 8);
+  hipLaunchKernelGGL(rowdot_kernel<D>, dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
+                     dim3(kThreads), 0, s, static_cast<const uint16_t *>(o), a.dout,
+                     const_cast<float *>(a.dvec), p.total_tokens, p.h_q);
+  BwdArgs kvargs = a;
+  kvargs.items = reinterpret_cast<const libra_item *>(plan_dev + h.off_kv_items);
+  kvargs.cu_off = reinterpret_cast<const int32_t *>(plan_dev + h.off_kv_cu_off);
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(h.num_cus), dim3(kThreads), 0, s, kvargs);
+  BwdArgs qargs = a;
+  qargs.items = reinterpret_cast<const libra_item *>(plan_dev + h.off_items);
+  qargs.cu_off = reinterpret_cast<const int32_t *>(plan_dev + h.off_cu_off);
+  if (a.records) qargs.records = a.records + h.num_cus;
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(h.num_cus), dim3(kThreads), 0, s, qargs);
+  return hipGetLastError() == hipSuccess ? LIBRA_OK : LIBRA_EHIP;
+}
+
+}  // namespace
+}  // namespace libra
+
+using namespace libra;
+
 extern "C" libra_status libra_attn_bwd_workspace(const void *plan, size_t *bytes) {
   libra_plan_info h;
-  if (!bytes || libra::plan_header(plan, &h) != LIBRA_OK) return LIBRA_EINVAL;
-  *bytes = 0;
+  if (!bytes || plan_header(plan, &h) != LIBRA_OK) return LIBRA_EINVAL;
+  *bytes = bwd_layout(h.params).total;
   return LIBRA_OK;
 }
 
-extern "C" libra_status libra_attn_bwd(const void *, const void *, const void *, const void *,
-                                       const void *, const void *, const void *, const float *,
-                                       const int32_t *, void *, void *, void *, float, void *, size_t,
-                                       libra_cu_record *, void *) {
-  return LIBRA_EUNSUPPORTED;
+extern "C" libra_status libra_attn_bwd(const void *plan, const void *plan_dev, const void *q,
+                                       const void *k, const void *v, const void *o, const void *dout,
+                                       const float *lse, const int32_t *cu_dev, void *dq, void *dk,
+                                       void *dv, float softmax_scale, void *workspace,
+                                       size_t workspace_bytes, libra_cu_record *records, void *stream) {
+  libra_plan_info h;
+  if (plan_header(plan, &h) != LIBRA_OK) return LIBRA_EINVAL;
+  const libra_plan_params &p = h.params;
+  if (p.head_dim != 64 && p.head_dim != 128) return LIBRA_EUNSUPPORTED;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return LIBRA_EINVAL;
+  if (p.total_tokens == 0) return LIBRA_OK;
+  if (!plan_dev || !q || !k || !v || !o || !dout || !lse || !cu_dev || !dq || !dk || !dv || !workspace)
+    return LIBRA_EINVAL;
+  if (misaligned(plan_dev, 16) || misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) ||
+      misaligned(o, 16) || misaligned(dout, 16) || misaligned(lse, 4) || misaligned(cu_dev, 4) ||
+      misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) || misaligned(workspace, 256) ||
+      misaligned(records, 16))
+    return LIBRA_EINVAL;
+  const BwdLayout lay = bwd_layout(p);
+  if (workspace_bytes < lay.total) return LIBRA_ESIZE;
+
+  char *ws = static_cast<char *>(workspace);
+  libra_status st;
+  if ((st = launch_transpose(q, ws + lay.qt, p.total_tokens, p.h_q, p.head_dim, stream)) != LIBRA_OK) return st;
+  if ((st = launch_transpose(dout, ws + lay.dot, p.total_tokens, p.h_q, p.head_dim, stream)) != LIBRA_OK) return st;
+  if ((st = launch_transpose(k, ws + lay.kt, p.total_tokens, p.h_kv, p.head_dim, stream)) != LIBRA_OK) return st;
+
+  BwdArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.dout = static_cast<const uint16_t *>(dout);
+  a.qt = reinterpret_cast<const uint16_t *>(ws + lay.qt);
+  a.dot = reinterpret_cast<const uint16_t *>(ws + lay.dot);
+  a.kt = reinterpret_cast<const uint16_t *>(ws + lay.kt);
+  a.lse = lse;
+  a.dvec = reinterpret_cast<const float *>(ws + lay.dvec);
+  a.cu = cu_dev;
+  a.dq = static_cast<uint16_t *>(dq);
+  a.dk = static_cast<uint16_t *>(dk);
+  a.dv = static_cast<uint16_t *>(dv);
+  a.records = records;
+  a.n_samples = p.num_samples;
+  a.L = p.total_tokens;
+  a.Lp = (int)round_up64(p.total_tokens, 64);
+  a.h_q = p.h_q;
+  a.h_kv = p.h_kv;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * kLog2e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char *pd = static_cast<const char *>(plan_dev);
+  return p.head_dim == 128 ? launch_bwd<128>(h, a, pd, o, s) : launch_bwd<64>(h, a, pd, o, s);
 }

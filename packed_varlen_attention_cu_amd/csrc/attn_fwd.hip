@@ -297,7 +297,8 @@ size_t transposed_bytes(int64_t heads, int64_t d, int64_t L) {
   return (size_t)round_up(heads * d * round_up(L, kTileTok) * 2, 256);
 }
 
-libra_status launch_transpose(const void *src, void *dst, int L, int H, int D, hipStream_t s) {
+libra_status launch_transpose(const void *src, void *dst, int L, int H, int D, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
   const int Lp = (int)round_up(L, kTileTok);
   dim3 grid(Lp / kTileTok, H);
   if (D == 128)
@@ -341,7 +342,7 @@ extern "C" libra_status libra_attn_fwd(const void *plan, const void *plan_dev, c
   if (workspace_bytes < need) return LIBRA_ESIZE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  libra_status st = launch_transpose(v, workspace, p.total_tokens, p.h_kv, p.head_dim, s);
+  libra_status st = launch_transpose(v, workspace, p.total_tokens, p.h_kv, p.head_dim, stream);
   if (st != LIBRA_OK) return st;
 
   FwdArgs a;
