@@ -1,0 +1,364 @@
+"""Benchmark of the packed varlen causal attention hot path on one MI355X.
+
+One step = plan the pack on the host (SH-Tiles, eq. 8 pair counts, Algorithm 2
+placement onto the CUs), upload the plan, run the forward (V transpose +
+persistent kernel) and the backward (transposes + rowsum, dK/dV kernel, dQ
+kernel), with per-CU busy records.  Inputs (q, k, v, dout) are resident in
+HBM before timing starts.  Throughput counts only unmasked causal pairs:
+FLOPs_fwd = 4 d h_q sum_j l_j (l_j + 1) / 2, FLOPs_bwd = 2.5 FLOPs_fwd.
+
+Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6       # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "packed varlen causal attn TFLOP/s (fwd, fwd+bwd), % bf16 MFMA peak, CU max/mean"
+DEVICE_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "device_common.h"]
+# Algorithmic FLOPs per unmasked (query, key, head) pair for each kernel:
+#   forward: QK^T and PV (2 x 2d); dK/dV pass: S recompute, dP, dV, dK (4 x 2d);
+#   dQ pass: dQ (2d) -- its S and dP recomputations are not algorithmic work.
+KERNEL_FLOPS_PER_PAIR = {"fwd_main": 4, "bwd_dkdv": 8, "bwd_dq": 2}
+KERNEL_SYMBOL = {"fwd_main": "attn_fwd_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel",
+                 "bwd_dq": "attn_bwd_dq_kernel"}
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in DEVICE_SOURCES:
+        with open(os.path.join(ROOT, "packed_varlen_attention_cu_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def causal_pairs(cu) -> int:
+    lens = np.diff(np.asarray(cu, dtype=np.int64))
+    return int((lens * (lens + 1) // 2).sum())
+
+
+def cu_busy_ratio(rec_bytes, num_cus):
+    import packed_varlen_attention_cu_amd as lib
+    r = rec_bytes.view(lib.RECORD_DTYPE)[:num_cus]
+    busy = (r["t_end"] - r["t_start"]).astype(np.float64)
+    ran = r["n_items"] > 0
+    if not ran.any():
+        return None, None
+    # key of the physical CU: XCC id, SE id, SH id, CU id
+    hw = r["hw_id"].astype(np.int64)
+    key = (r["xcc_id"].astype(np.int64) & 0xF) << 16 | ((hw >> 13) & 0x7) << 8 | ((hw >> 12) & 1) << 4 | ((hw >> 8) & 0xF)
+    per_cu = {}
+    for k_, b, ok in zip(key, busy, ran):
+        if ok:
+            per_cu[int(k_)] = per_cu.get(int(k_), 0.0) + b
+    vals = np.array(list(per_cu.values()))
+    return float(vals.max() / vals.mean()), len(per_cu)
+
+
+def cpu_baseline(w, cu, tensors, scale, with_bwd=True, budget_s=15.0):
+    """The fp64 oracle's forward (+ backward) on a bounded sample of the same pack."""
+    from concurrent.futures import ThreadPoolExecutor, FIRST_COMPLETED, wait
+    import oracle.attention as A
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:          # pragma: no cover
+        threadpool_limits = None
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    g = w.h_q // w.h_kv
+    lens = np.diff(np.asarray(cu, dtype=np.int64))
+    rng = np.random.default_rng(0)
+    units = []
+    for j in np.argsort(-lens):                          # longest samples first: their tails
+        if lens[j] > 512:
+            units.append((int(j), int(rng.integers(0, w.h_kv)), int(lens[j]) - 256))
+    for j in range(len(lens)):
+        if 0 < lens[j] <= 512:
+            units.append((j, int(rng.integers(0, w.h_kv)), 0))
+
+    def run(unit):
+        j, kv, first = unit
+        s, e = int(cu[j]), int(cu[j + 1])
+        q = A.widen_bf16(tensors["q"][s:e])
+        k = A.widen_bf16(tensors["k"][s:e])
+        v = A.widen_bf16(tensors["v"][s:e])
+        do = A.widen_bf16(tensors["dout"][s:e]) if with_bwd else None
+        for h in range(kv * g, (kv + 1) * g):
+            A.head_rows(q, k, v, 0, e - s, h, kv, first, e - s, scale)
+        if with_bwd:
+            A.backward_tail(q, k, v, do, 0, e - s, kv, first, scale)
+        n = e - s
+        return g * ((n * (n + 1) - first * (first + 1)) // 2)
+
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    pairs = 0
+    done = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        pending = set()
+        it = iter(units)
+        for _ in range(cores):
+            u = next(it, None)
+            if u is not None:
+                pending.add(ex.submit(run, u))
+        while pending:
+            fin, pending = wait(pending, return_when=FIRST_COMPLETED)
+            for f in fin:
+                pairs += f.result()
+                done += 1
+            if time.perf_counter() - t0 < budget_s:
+                u = next(it, None)
+                if u is not None:
+                    pending.add(ex.submit(run, u))
+    elapsed = time.perf_counter() - t0
+    if ctx is not None:
+        ctx.restore_original_limits()
+    flops = (3.5 if with_bwd else 1.0) * 4 * w.head_dim * pairs
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 numpy oracle {'fwd+bwd' if with_bwd else 'fwd'} on {done} (sample, KV head) units of the same pack "
+                      f"(tails of 256 query rows of the longest samples, whole short samples; "
+                      f"{pairs} causal pairs) in {elapsed:.1f} s"}
+
+
+def traffic_for(kernel, workload, launches_bytes_fn):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return launches_bytes_fn(t)
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, copy_bytes):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic_*.json."""
+    import csv
+
+    def read(d, counter):
+        rows = []
+        for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(p) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") == counter:
+                        rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return rows
+
+    fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
+
+    def per_kernel(rows, sym):
+        v = [x for name, x in rows if sym in name]
+        return float(np.mean(v)) if v else None
+
+    def copy_value(rows):
+        v = [x for name, x in rows if "copy" in name.lower() or "elementwise" in name.lower()]
+        return max(v) if v else None
+
+    fc, wc = copy_value(fetch), copy_value(write)
+    out = []
+    for kernel, sym in KERNEL_SYMBOL.items():
+        f_kib, w_kib = per_kernel(fetch, sym), per_kernel(write, sym)
+        if f_kib is None or w_kib is None or not fc or not wc:
+            continue
+        rec = {"kernel": kernel, "symbol": sym, "workload": workload, "source_hash": source_hash(),
+               "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
+               "copy_bytes": copy_bytes, "copy_fetch_kib": fc, "copy_write_kib": wc,
+               "fetch_bytes_per_kib": copy_bytes / fc, "write_bytes_per_kib": copy_bytes / wc}
+        rec["hbm_bytes_per_launch"] = f_kib * rec["fetch_bytes_per_kib"] + w_kib * rec["write_bytes_per_kib"]
+        path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        out.append(path)
+    print(json.dumps({"written": out}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="train_256k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--assign", type=int, default=0, help="0: Algorithm 2 placement, 1: round-robin")
+    ap.add_argument("--fwd-only", action="store_true", help="time the forward only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
+                    help="run one plain device copy of this size first (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                      args.calibrate_copy * (1 << 20))
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU sharding of this "
+              "path is a design note, not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import packed_varlen_attention_cu_amd as lib
+
+    w = synth.WORKLOADS[args.workload]
+    do_bwd = not args.fwd_only
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lengths = synth.make_lengths(w, args.seed)
+    cu = synth.cu_seqlens(lengths)
+    names = ("q", "k", "v", "dout") if do_bwd else ("q", "k", "v")
+    t_gen = time.perf_counter()
+    host = synth.make_tensors(w, args.seed, names=names)
+    t_gen = time.perf_counter() - t_gen
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = up(host["q"]), up(host["k"]), up(host["v"])
+    dout = up(host["dout"]) if do_bwd else None
+    L, d = w.total_tokens, w.head_dim
+    scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.h_q, L), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if do_bwd else (None,) * 3
+
+    plan_kw = dict(total_tokens=L, h_q=w.h_q, h_kv=w.h_kv, head_dim=d, tile_tokens=w.tile_tokens,
+                   tile_heads=w.tile_heads, assign=args.assign)
+    plan0 = lib.Plan(cu, **plan_kw)
+    ncu = plan0.info.num_cus
+    ws_f = torch.empty(lib.libra_attn_fwd_workspace(plan0.host), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, lib.libra_attn_bwd_workspace(plan0.host)), dtype=torch.uint8, device=dev)
+    rec = torch.zeros(3 * ncu * lib.RECORD_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+    rec_f, rec_kv, rec_q = rec[:ncu * 32], rec[ncu * 32:2 * ncu * 32], rec[2 * ncu * 32:]
+    cu_dev = torch.from_numpy(cu.copy()).to(dev)
+    plan_dev = torch.empty(plan0.host.nbytes, dtype=torch.uint8, device=dev)
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        a_ = torch.empty(n, dtype=torch.uint8, device=dev)
+        b_ = torch.empty(n, dtype=torch.uint8, device=dev)
+        b_.copy_(a_)
+        torch.cuda.synchronize()
+        del a_, b_
+
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    ev = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for n in ("fwd_prepare", "fwd_main", "bwd_prepare", "bwd_dkdv", "bwd_dq")}
+    times = {n: [] for n in ev}
+    plan_ms = []
+
+    def step(record):
+        t0 = time.perf_counter()
+        plan = lib.Plan(cu, **plan_kw)                                  # host planner (a1-a3)
+        plan_ms.append((time.perf_counter() - t0) * 1e3)
+        plan_dev.copy_(torch.from_numpy(plan.host))                      # plan upload
+        wsf, wsb = ws_f.numel(), ws_b.numel()
+
+        def timed(name, fn):
+            if record:
+                ev[name][0].record(stream)
+            fn()
+            if record:
+                ev[name][1].record(stream)
+
+        timed("fwd_prepare", lambda: lib.libra_attn_fwd_prepare(plan.host, v, ws_f, wsf, sh))
+        timed("fwd_main", lambda: lib.libra_attn_fwd_main(plan.host, plan_dev, q, k, cu_dev, o, lse, scale,
+                                                          ws_f, wsf, rec_f, sh))
+        if do_bwd:
+            timed("bwd_prepare", lambda: lib.libra_attn_bwd_prepare(plan.host, q, k, o, dout, ws_b, wsb, sh))
+            timed("bwd_dkdv", lambda: lib.libra_attn_bwd_dkdv(plan.host, plan_dev, q, k, v, dout, lse, cu_dev,
+                                                              dk, dv, scale, ws_b, wsb, rec_kv, sh))
+            timed("bwd_dq", lambda: lib.libra_attn_bwd_dq(plan.host, plan_dev, q, k, v, dout, lse, cu_dev, dq,
+                                                          scale, ws_b, wsb, rec_q, sh))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    plan_ms.clear()
+
+    wall = 0.0
+    busy = {"fwd_main": [], "bwd_dkdv": [], "bwd_dq": []}
+    for i in range(args.steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step(True)
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - t0
+        for n, (a_, b_) in ev.items():
+            if n.startswith("bwd") and not do_bwd:
+                continue
+            times[n].append(a_.elapsed_time(b_))
+        for n, r in (("fwd_main", rec_f), ("bwd_dkdv", rec_kv), ("bwd_dq", rec_q)):
+            if n.startswith("bwd") and not do_bwd:
+                continue
+            ratio, _ = cu_busy_ratio(r.cpu().numpy(), ncu)
+            busy[n].append(ratio)
+        print(f"step {i + 1}/{args.steps}: {(time.perf_counter() - t0) * 1e3:.2f} ms", file=sys.stderr,
+              flush=True)
+
+    ms_step = wall / args.steps * 1e3
+    pairs = causal_pairs(cu) * w.h_q
+    assert pairs == plan0.info.total_pairs, "planner pair count disagrees with the closed form"
+    fwd_flops = 4.0 * d * pairs
+    total_flops = fwd_flops * (3.5 if do_bwd else 1.0)
+    avg = {n: float(np.mean(t)) for n, t in times.items() if t}
+    fwd_ms = avg["fwd_prepare"] + avg["fwd_main"]
+    kernels = {n: avg[n] for n in KERNEL_FLOPS_PER_PAIR if n in avg}
+    dom = max(kernels, key=kernels.get)
+    achieved = KERNEL_FLOPS_PER_PAIR[dom] * d * pairs / (kernels[dom] * 1e-3) / 1e12
+    traffic = traffic_for(dom, args.workload, lambda t: t["hbm_bytes_per_launch"])
+
+    out = {
+        "metric": METRIC,
+        "value": round(total_flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "total_tokens": L, "h_q": w.h_q, "h_kv": w.h_kv,
+                   "head_dim": d, "sh_tile": [w.tile_tokens, w.tile_heads], "samples": int(len(lengths)),
+                   "max_sample": int(lengths.max()), "seed": args.seed, "pass": "fwd+bwd" if do_bwd else "fwd",
+                   "placement": "algorithm2" if args.assign == 0 else "round_robin", "num_cus": ncu},
+        "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
+        "fwd_main_tflops": round(fwd_flops / (avg["fwd_main"] * 1e-3) / 1e12, 2),
+        "fwd_frac_peak": round(fwd_flops / (avg["fwd_main"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernel_ms": {n: round(t, 4) for n, t in avg.items()},
+        "plan_ms": round(float(np.mean(plan_ms)), 3),
+        "cu_busy_max_over_mean": {n: round(float(np.mean(b)), 4) for n, b in busy.items() if b},
+        "plan_load_max_over_mean": round(plan0.info.load_max / (plan0.info.load_sum / ncu), 5),
+        "flops_fwd": fwd_flops,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if do_bwd:
+        bwd_ms = avg["bwd_prepare"] + avg["bwd_dkdv"] + avg["bwd_dq"]
+        out["bwd_tflops"] = round(2.5 * fwd_flops / (bwd_ms * 1e-3) / 1e12, 2)
+        out["fwd_bwd_kernels_tflops"] = round(3.5 * fwd_flops / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 2)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, cu, host, scale, with_bwd=do_bwd)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -159,6 +159,18 @@ libra_status libra_attn_fwd(const void *plan, const void *plan_dev,
                             float softmax_scale, void *workspace, size_t workspace_bytes,
                             libra_cu_record *records, void *stream);
 
+/* The forward in two phases on the same stream (libra_attn_fwd enqueues both):
+ * _prepare transposes V into the workspace; _main runs the persistent kernel
+ * and reads only the workspace written by a preceding _prepare of the same v.
+ * Arguments and errors as for libra_attn_fwd. */
+libra_status libra_attn_fwd_prepare(const void *plan, const void *v, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+libra_status libra_attn_fwd_main(const void *plan, const void *plan_dev,
+                                 const void *q, const void *k, const int32_t *cu_seqlens_dev,
+                                 void *o, float *lse, float softmax_scale,
+                                 const void *workspace, size_t workspace_bytes,
+                                 libra_cu_record *records, void *stream);
+
 /* Device workspace the backward needs, in bytes. */
 libra_status libra_attn_bwd_workspace(const void *plan, size_t *bytes);
 
@@ -174,6 +186,31 @@ libra_status libra_attn_bwd(const void *plan, const void *plan_dev,
                             void *dq, void *dk, void *dv, float softmax_scale,
                             void *workspace, size_t workspace_bytes,
                             libra_cu_record *records, void *stream);
+
+/* The backward in three phases on the same stream (libra_attn_bwd enqueues
+ * all three, in this order):
+ *   _prepare: transposes q, dout and k into the workspace and computes
+ *             D = rowsum(dout * o) (fp32);
+ *   _dkdv:    the key-major persistent kernel writing dk and dv
+ *             (records: NULL or libra_cu_record[num_cus]);
+ *   _dq:      the query-major persistent kernel writing dq
+ *             (records: NULL or libra_cu_record[num_cus]).
+ * _dkdv and _dq read the workspace a preceding _prepare filled from the same
+ * tensors.  Arguments and errors as for libra_attn_bwd. */
+libra_status libra_attn_bwd_prepare(const void *plan, const void *q, const void *k,
+                                    const void *o, const void *dout, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+libra_status libra_attn_bwd_dkdv(const void *plan, const void *plan_dev,
+                                 const void *q, const void *k, const void *v,
+                                 const void *dout, const float *lse,
+                                 const int32_t *cu_seqlens_dev, void *dk, void *dv,
+                                 float softmax_scale, const void *workspace,
+                                 size_t workspace_bytes, libra_cu_record *records, void *stream);
+libra_status libra_attn_bwd_dq(const void *plan, const void *plan_dev,
+                               const void *q, const void *k, const void *v, const void *dout,
+                               const float *lse, const int32_t *cu_seqlens_dev, void *dq,
+                               float softmax_scale, const void *workspace,
+                               size_t workspace_bytes, libra_cu_record *records, void *stream);
 
 /* Frequency of the clock in libra_cu_record, for the current device. */
 libra_status libra_device_clock_khz(int32_t *khz);

@@ -66,7 +66,7 @@ assert TILE_DTYPE.itemsize == 48 and ITEM_DTYPE.itemsize == 48 and RECORD_DTYPE.
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m packed_varlen_attention_cu_amd.build`")
+                          "`python packed_varlen_attention_cu_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     lib.libra_plan.argtypes = [vp, ctypes.POINTER(PlanParams), vp, ctypes.POINTER(sz)]
@@ -76,11 +76,17 @@ def _load():
     lib.libra_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
     lib.libra_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
                                    vp, sz, vp, vp]
+    lib.libra_attn_fwd_prepare.argtypes = [vp, vp, vp, sz, vp]
+    lib.libra_attn_fwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
+    lib.libra_attn_bwd_prepare.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.libra_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
+    lib.libra_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
     lib.libra_device_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int32)]
     lib.libra_status_str.argtypes = [ctypes.c_int]
     lib.libra_status_str.restype = ctypes.c_char_p
     for name in ("libra_plan", "libra_plan_check", "libra_attn_fwd_workspace", "libra_attn_bwd_workspace",
-                 "libra_attn_fwd", "libra_attn_bwd", "libra_device_clock_khz"):
+                 "libra_attn_fwd", "libra_attn_bwd", "libra_device_clock_khz", "libra_attn_fwd_prepare",
+                 "libra_attn_fwd_main", "libra_attn_bwd_prepare", "libra_attn_bwd_dkdv", "libra_attn_bwd_dq"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -153,6 +159,41 @@ def libra_attn_bwd(plan_host, plan_dev, q, k, v, o, dout, lse, cu_seqlens_dev, d
                                float(softmax_scale), _ptr(workspace), int(workspace_bytes),
                                _ptr(records), stream),
            "libra_attn_bwd")
+
+
+def libra_attn_fwd_prepare(plan_host, v, workspace, workspace_bytes, stream):
+    _check(_lib.libra_attn_fwd_prepare(_ptr(plan_host), _ptr(v), _ptr(workspace), int(workspace_bytes), stream),
+           "libra_attn_fwd_prepare")
+
+
+def libra_attn_fwd_main(plan_host, plan_dev, q, k, cu_seqlens_dev, o, lse, softmax_scale, workspace,
+                        workspace_bytes, records, stream):
+    _check(_lib.libra_attn_fwd_main(_ptr(plan_host), _ptr(plan_dev), _ptr(q), _ptr(k), _ptr(cu_seqlens_dev),
+                                    _ptr(o), _ptr(lse), float(softmax_scale), _ptr(workspace),
+                                    int(workspace_bytes), _ptr(records), stream),
+           "libra_attn_fwd_main")
+
+
+def libra_attn_bwd_prepare(plan_host, q, k, o, dout, workspace, workspace_bytes, stream):
+    _check(_lib.libra_attn_bwd_prepare(_ptr(plan_host), _ptr(q), _ptr(k), _ptr(o), _ptr(dout), _ptr(workspace),
+                                       int(workspace_bytes), stream),
+           "libra_attn_bwd_prepare")
+
+
+def libra_attn_bwd_dkdv(plan_host, plan_dev, q, k, v, dout, lse, cu_seqlens_dev, dk, dv, softmax_scale,
+                        workspace, workspace_bytes, records, stream):
+    _check(_lib.libra_attn_bwd_dkdv(_ptr(plan_host), _ptr(plan_dev), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                    _ptr(lse), _ptr(cu_seqlens_dev), _ptr(dk), _ptr(dv), float(softmax_scale),
+                                    _ptr(workspace), int(workspace_bytes), _ptr(records), stream),
+           "libra_attn_bwd_dkdv")
+
+
+def libra_attn_bwd_dq(plan_host, plan_dev, q, k, v, dout, lse, cu_seqlens_dev, dq, softmax_scale, workspace,
+                      workspace_bytes, records, stream):
+    _check(_lib.libra_attn_bwd_dq(_ptr(plan_host), _ptr(plan_dev), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                  _ptr(cu_seqlens_dev), _ptr(dq), float(softmax_scale), _ptr(workspace),
+                                  int(workspace_bytes), _ptr(records), stream),
+           "libra_attn_bwd_dq")
 
 
 def libra_device_clock_khz() -> int:

@@ -21,6 +21,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <initializer_list>
 
 #include "device_common.h"
 #include "libra.h"
@@ -418,24 +419,127 @@ BwdLayout bwd_layout(const libra_plan_params &p) {
   return l;
 }
 
-template <int D>
-libra_status launch_bwd(const libra_plan_info &h, BwdArgs a, const char *plan_dev, const void *o,
-                        hipStream_t s) {
+libra_status check_header(const void *plan, libra_plan_info *h) {
+  if (plan_header(plan, h) != LIBRA_OK) return LIBRA_EINVAL;
+  if (h->params.head_dim != 64 && h->params.head_dim != 128) return LIBRA_EUNSUPPORTED;
+  return LIBRA_OK;
+}
+
+bool any_null(std::initializer_list<const void *> ps) {
+  for (const void *p : ps)
+    if (!p) return true;
+  return false;
+}
+
+bool any_misaligned(std::initializer_list<const void *> ps, uintptr_t a) {
+  for (const void *p : ps)
+    if (misaligned(p, a)) return true;
+  return false;
+}
+
+libra_status check_workspace(const libra_plan_info &h, const void *ws, size_t bytes) {
+  if (!ws || misaligned(ws, 256)) return LIBRA_EINVAL;
+  return bytes < bwd_layout(h.params).total ? LIBRA_ESIZE : LIBRA_OK;
+}
+
+libra_status check_prepare(const libra_plan_info &h, const void *q, const void *k, const void *o,
+                           const void *dout, const void *ws, size_t bytes) {
+  if (h.params.total_tokens == 0) return LIBRA_OK;
+  if (any_null({q, k, o, dout}) || any_misaligned({q, k, o, dout}, 16)) return LIBRA_EINVAL;
+  return check_workspace(h, ws, bytes);
+}
+
+libra_status check_pass(const libra_plan_info &h, const void *plan_dev,
+                        std::initializer_list<const void *> tensors, const float *lse,
+                        const int32_t *cu_dev, float scale, const void *ws, size_t bytes,
+                        const void *records) {
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return LIBRA_EINVAL;
+  if (h.params.total_tokens == 0) return LIBRA_OK;
+  if (!plan_dev || !lse || !cu_dev || any_null(tensors)) return LIBRA_EINVAL;
+  if (misaligned(plan_dev, 16) || any_misaligned(tensors, 16) || misaligned(lse, 4) ||
+      misaligned(cu_dev, 4) || misaligned(records, 16))
+    return LIBRA_EINVAL;
+  return check_workspace(h, ws, bytes);
+}
+
+BwdArgs make_args(const libra_plan_info &h, const void *q, const void *k, const void *v,
+                  const void *dout, const float *lse, const int32_t *cu_dev, const void *ws,
+                  float scale) {
   const libra_plan_params &p = h.params;
+  const BwdLayout lay = bwd_layout(p);
+  const char *w = static_cast<const char *>(ws);
+  BwdArgs a{};
+  a.q = static_cast<const uint16_t *>(q);
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.dout = static_cast<const uint16_t *>(dout);
+  a.qt = reinterpret_cast<const uint16_t *>(w + lay.qt);
+  a.dot = reinterpret_cast<const uint16_t *>(w + lay.dot);
+  a.kt = reinterpret_cast<const uint16_t *>(w + lay.kt);
+  a.lse = lse;
+  a.dvec = reinterpret_cast<const float *>(w + lay.dvec);
+  a.cu = cu_dev;
+  a.n_samples = p.num_samples;
+  a.L = p.total_tokens;
+  a.Lp = (int)round_up64(p.total_tokens, 64);
+  a.h_q = p.h_q;
+  a.h_kv = p.h_kv;
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  return a;
+}
+
+libra_status launch_prepare(const libra_plan_info &h, const void *q, const void *k, const void *o,
+                            const void *dout, void *ws, void *stream) {
+  const libra_plan_params &p = h.params;
+  const BwdLayout lay = bwd_layout(p);
+  char *w = static_cast<char *>(ws);
+  libra_status st;
+  if ((st = launch_transpose(q, w + lay.qt, p.total_tokens, p.h_q, p.head_dim, stream)) != LIBRA_OK) return st;
+  if ((st = launch_transpose(dout, w + lay.dot, p.total_tokens, p.h_q, p.head_dim, stream)) != LIBRA_OK) return st;
+  if ((st = launch_transpose(k, w + lay.kt, p.total_tokens, p.h_kv, p.head_dim, stream)) != LIBRA_OK) return st;
   const int64_t rows = (int64_t)p.total_tokens * p.h_q;
-  const int rows_per_block = kThreads / (D / 8);
-  hipLaunchKernelGGL(rowdot_kernel<D>, dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
-                     dim3(kThreads), 0, s, static_cast<const uint16_t *>(o), a.dout,
-                     const_cast<float *>(a.dvec), p.total_tokens, p.h_q);
-  BwdArgs kvargs = a;
-  kvargs.items = reinterpret_cast<const libra_item *>(plan_dev + h.off_kv_items);
-  kvargs.cu_off = reinterpret_cast<const int32_t *>(plan_dev + h.off_kv_cu_off);
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(h.num_cus), dim3(kThreads), 0, s, kvargs);
-  BwdArgs qargs = a;
-  qargs.items = reinterpret_cast<const libra_item *>(plan_dev + h.off_items);
-  qargs.cu_off = reinterpret_cast<const int32_t *>(plan_dev + h.off_cu_off);
-  if (a.records) qargs.records = a.records + h.num_cus;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(h.num_cus), dim3(kThreads), 0, s, qargs);
+  const int rows_per_block = kThreads / (p.head_dim / 8);
+  const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float *dvec = reinterpret_cast<float *>(w + lay.dvec);
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL(rowdot_kernel<128>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t *>(o),
+                       static_cast<const uint16_t *>(dout), dvec, p.total_tokens, p.h_q);
+  else
+    hipLaunchKernelGGL(rowdot_kernel<64>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t *>(o),
+                       static_cast<const uint16_t *>(dout), dvec, p.total_tokens, p.h_q);
+  return hipGetLastError() == hipSuccess ? LIBRA_OK : LIBRA_EHIP;
+}
+
+libra_status launch_dkdv(const libra_plan_info &h, BwdArgs a, const void *plan_dev, void *dk, void *dv,
+                         libra_cu_record *records, void *stream) {
+  const char *pd = static_cast<const char *>(plan_dev);
+  a.items = reinterpret_cast<const libra_item *>(pd + h.off_kv_items);
+  a.cu_off = reinterpret_cast<const int32_t *>(pd + h.off_kv_cu_off);
+  a.dk = static_cast<uint16_t *>(dk);
+  a.dv = static_cast<uint16_t *>(dv);
+  a.records = records;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (h.params.head_dim == 128)
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? LIBRA_OK : LIBRA_EHIP;
+}
+
+libra_status launch_dq(const libra_plan_info &h, BwdArgs a, const void *plan_dev, void *dq,
+                       libra_cu_record *records, void *stream) {
+  const char *pd = static_cast<const char *>(plan_dev);
+  a.items = reinterpret_cast<const libra_item *>(pd + h.off_items);
+  a.cu_off = reinterpret_cast<const int32_t *>(pd + h.off_cu_off);
+  a.dq = static_cast<uint16_t *>(dq);
+  a.records = records;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (h.params.head_dim == 128)
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? LIBRA_OK : LIBRA_EHIP;
 }
 
@@ -451,56 +555,61 @@ extern "C" libra_status libra_attn_bwd_workspace(const void *plan, size_t *bytes
   return LIBRA_OK;
 }
 
+extern "C" libra_status libra_attn_bwd_prepare(const void *plan, const void *q, const void *k,
+                                               const void *o, const void *dout, void *workspace,
+                                               size_t workspace_bytes, void *stream) {
+  libra_plan_info h;
+  libra_status st = check_header(plan, &h);
+  if (st == LIBRA_OK) st = check_prepare(h, q, k, o, dout, workspace, workspace_bytes);
+  if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
+  return launch_prepare(h, q, k, o, dout, workspace, stream);
+}
+
+extern "C" libra_status libra_attn_bwd_dkdv(const void *plan, const void *plan_dev, const void *q,
+                                            const void *k, const void *v, const void *dout,
+                                            const float *lse, const int32_t *cu_dev, void *dk, void *dv,
+                                            float softmax_scale, const void *workspace,
+                                            size_t workspace_bytes, libra_cu_record *records,
+                                            void *stream) {
+  libra_plan_info h;
+  libra_status st = check_header(plan, &h);
+  if (st == LIBRA_OK)
+    st = check_pass(h, plan_dev, {q, k, v, dout, dk, dv}, lse, cu_dev, softmax_scale, workspace,
+                    workspace_bytes, records);
+  if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
+  return launch_dkdv(h, make_args(h, q, k, v, dout, lse, cu_dev, workspace, softmax_scale), plan_dev,
+                     dk, dv, records, stream);
+}
+
+extern "C" libra_status libra_attn_bwd_dq(const void *plan, const void *plan_dev, const void *q,
+                                          const void *k, const void *v, const void *dout, const float *lse,
+                                          const int32_t *cu_dev, void *dq, float softmax_scale,
+                                          const void *workspace, size_t workspace_bytes,
+                                          libra_cu_record *records, void *stream) {
+  libra_plan_info h;
+  libra_status st = check_header(plan, &h);
+  if (st == LIBRA_OK)
+    st = check_pass(h, plan_dev, {q, k, v, dout, dq}, lse, cu_dev, softmax_scale, workspace,
+                    workspace_bytes, records);
+  if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
+  return launch_dq(h, make_args(h, q, k, v, dout, lse, cu_dev, workspace, softmax_scale), plan_dev,
+                   dq, records, stream);
+}
+
 extern "C" libra_status libra_attn_bwd(const void *plan, const void *plan_dev, const void *q,
                                        const void *k, const void *v, const void *o, const void *dout,
                                        const float *lse, const int32_t *cu_dev, void *dq, void *dk,
                                        void *dv, float softmax_scale, void *workspace,
                                        size_t workspace_bytes, libra_cu_record *records, void *stream) {
   libra_plan_info h;
-  if (plan_header(plan, &h) != LIBRA_OK) return LIBRA_EINVAL;
-  const libra_plan_params &p = h.params;
-  if (p.head_dim != 64 && p.head_dim != 128) return LIBRA_EUNSUPPORTED;
-  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return LIBRA_EINVAL;
-  if (p.total_tokens == 0) return LIBRA_OK;
-  if (!plan_dev || !q || !k || !v || !o || !dout || !lse || !cu_dev || !dq || !dk || !dv || !workspace)
-    return LIBRA_EINVAL;
-  if (misaligned(plan_dev, 16) || misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) ||
-      misaligned(o, 16) || misaligned(dout, 16) || misaligned(lse, 4) || misaligned(cu_dev, 4) ||
-      misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) || misaligned(workspace, 256) ||
-      misaligned(records, 16))
-    return LIBRA_EINVAL;
-  const BwdLayout lay = bwd_layout(p);
-  if (workspace_bytes < lay.total) return LIBRA_ESIZE;
-
-  char *ws = static_cast<char *>(workspace);
-  libra_status st;
-  if ((st = launch_transpose(q, ws + lay.qt, p.total_tokens, p.h_q, p.head_dim, stream)) != LIBRA_OK) return st;
-  if ((st = launch_transpose(dout, ws + lay.dot, p.total_tokens, p.h_q, p.head_dim, stream)) != LIBRA_OK) return st;
-  if ((st = launch_transpose(k, ws + lay.kt, p.total_tokens, p.h_kv, p.head_dim, stream)) != LIBRA_OK) return st;
-
-  BwdArgs a{};
-  a.q = static_cast<const uint16_t *>(q);
-  a.k = static_cast<const uint16_t *>(k);
-  a.v = static_cast<const uint16_t *>(v);
-  a.dout = static_cast<const uint16_t *>(dout);
-  a.qt = reinterpret_cast<const uint16_t *>(ws + lay.qt);
-  a.dot = reinterpret_cast<const uint16_t *>(ws + lay.dot);
-  a.kt = reinterpret_cast<const uint16_t *>(ws + lay.kt);
-  a.lse = lse;
-  a.dvec = reinterpret_cast<const float *>(ws + lay.dvec);
-  a.cu = cu_dev;
-  a.dq = static_cast<uint16_t *>(dq);
-  a.dk = static_cast<uint16_t *>(dk);
-  a.dv = static_cast<uint16_t *>(dv);
-  a.records = records;
-  a.n_samples = p.num_samples;
-  a.L = p.total_tokens;
-  a.Lp = (int)round_up64(p.total_tokens, 64);
-  a.h_q = p.h_q;
-  a.h_kv = p.h_kv;
-  a.scale = softmax_scale;
-  a.scale_log2 = softmax_scale * kLog2e;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const char *pd = static_cast<const char *>(plan_dev);
-  return p.head_dim == 128 ? launch_bwd<128>(h, a, pd, o, s) : launch_bwd<64>(h, a, pd, o, s);
+  libra_status st = check_header(plan, &h);
+  if (st == LIBRA_OK) st = check_prepare(h, q, k, o, dout, workspace, workspace_bytes);
+  if (st == LIBRA_OK)
+    st = check_pass(h, plan_dev, {q, k, v, dout, dq, dk, dv}, lse, cu_dev, softmax_scale, workspace,
+                    workspace_bytes, records);
+  if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
+  if ((st = launch_prepare(h, q, k, o, dout, workspace, stream)) != LIBRA_OK) return st;
+  const BwdArgs a = make_args(h, q, k, v, dout, lse, cu_dev, workspace, softmax_scale);
+  if ((st = launch_dkdv(h, a, plan_dev, dk, dv, records, stream)) != LIBRA_OK) return st;
+  return launch_dq(h, a, plan_dev, dq, records ? records + h.num_cus : nullptr, stream);
 }

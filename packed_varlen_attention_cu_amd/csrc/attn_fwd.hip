@@ -323,28 +323,41 @@ extern "C" libra_status libra_attn_fwd_workspace(const void *plan, size_t *bytes
   return LIBRA_OK;
 }
 
-extern "C" libra_status libra_attn_fwd(const void *plan, const void *plan_dev, const void *q,
-                                       const void *k, const void *v, const int32_t *cu_dev, void *o,
-                                       float *lse, float softmax_scale, void *workspace,
-                                       size_t workspace_bytes, libra_cu_record *records, void *stream) {
-  libra_plan_info h;
-  if (plan_header(plan, &h) != LIBRA_OK) return LIBRA_EINVAL;
+namespace {
+
+libra_status check_header(const void *plan, libra_plan_info *h) {
+  if (plan_header(plan, h) != LIBRA_OK) return LIBRA_EINVAL;
+  if (h->params.head_dim != 64 && h->params.head_dim != 128) return LIBRA_EUNSUPPORTED;
+  return LIBRA_OK;
+}
+
+libra_status check_prepare(const libra_plan_info &h, const void *v, const void *workspace,
+                           size_t workspace_bytes) {
   const libra_plan_params &p = h.params;
-  if (p.head_dim != 64 && p.head_dim != 128) return LIBRA_EUNSUPPORTED;
-  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return LIBRA_EINVAL;
   if (p.total_tokens == 0) return LIBRA_OK;
-  if (!plan_dev || !q || !k || !v || !cu_dev || !o || !lse || !workspace) return LIBRA_EINVAL;
-  if (misaligned(plan_dev, 16) || misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) ||
-      misaligned(o, 16) || misaligned(lse, 4) || misaligned(cu_dev, 4) || misaligned(workspace, 16) ||
-      misaligned(records, 16))
+  if (!v || !workspace || misaligned(v, 16) || misaligned(workspace, 16)) return LIBRA_EINVAL;
+  if (workspace_bytes < transposed_bytes(p.h_kv, p.head_dim, p.total_tokens)) return LIBRA_ESIZE;
+  return LIBRA_OK;
+}
+
+libra_status check_main(const libra_plan_info &h, const void *plan_dev, const void *q, const void *k,
+                        const int32_t *cu_dev, const void *o, const float *lse, float scale,
+                        const void *workspace, size_t workspace_bytes, const void *records) {
+  const libra_plan_params &p = h.params;
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return LIBRA_EINVAL;
+  if (p.total_tokens == 0) return LIBRA_OK;
+  if (!plan_dev || !q || !k || !cu_dev || !o || !lse || !workspace) return LIBRA_EINVAL;
+  if (misaligned(plan_dev, 16) || misaligned(q, 16) || misaligned(k, 16) || misaligned(o, 16) ||
+      misaligned(lse, 4) || misaligned(cu_dev, 4) || misaligned(workspace, 16) || misaligned(records, 16))
     return LIBRA_EINVAL;
-  const size_t need = transposed_bytes(p.h_kv, p.head_dim, p.total_tokens);
-  if (workspace_bytes < need) return LIBRA_ESIZE;
+  if (workspace_bytes < transposed_bytes(p.h_kv, p.head_dim, p.total_tokens)) return LIBRA_ESIZE;
+  return LIBRA_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  libra_status st = launch_transpose(v, workspace, p.total_tokens, p.h_kv, p.head_dim, stream);
-  if (st != LIBRA_OK) return st;
-
+libra_status launch_main(const libra_plan_info &h, const void *plan_dev, const void *q, const void *k,
+                         const int32_t *cu_dev, void *o, float *lse, float scale, const void *workspace,
+                         libra_cu_record *records, void *stream) {
+  const libra_plan_params &p = h.params;
   FwdArgs a;
   const char *pd = static_cast<const char *>(plan_dev);
   a.items = reinterpret_cast<const libra_item *>(pd + h.off_items);
@@ -361,12 +374,52 @@ extern "C" libra_status libra_attn_fwd(const void *plan, const void *plan_dev, c
   a.Lp = (int)round_up(p.total_tokens, kTileTok);
   a.h_q = p.h_q;
   a.h_kv = p.h_kv;
-  a.scale_log2 = softmax_scale * kLog2e;
+  a.scale_log2 = scale * kLog2e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.head_dim == 128)
     hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? LIBRA_OK : LIBRA_EHIP;
+}
+
+}  // namespace
+
+extern "C" libra_status libra_attn_fwd_prepare(const void *plan, const void *v, void *workspace,
+                                               size_t workspace_bytes, void *stream) {
+  libra_plan_info h;
+  libra_status st = check_header(plan, &h);
+  if (st == LIBRA_OK) st = check_prepare(h, v, workspace, workspace_bytes);
+  if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
+  return launch_transpose(v, workspace, h.params.total_tokens, h.params.h_kv, h.params.head_dim, stream);
+}
+
+extern "C" libra_status libra_attn_fwd_main(const void *plan, const void *plan_dev, const void *q,
+                                            const void *k, const int32_t *cu_dev, void *o, float *lse,
+                                            float softmax_scale, const void *workspace,
+                                            size_t workspace_bytes, libra_cu_record *records,
+                                            void *stream) {
+  libra_plan_info h;
+  libra_status st = check_header(plan, &h);
+  if (st == LIBRA_OK)
+    st = check_main(h, plan_dev, q, k, cu_dev, o, lse, softmax_scale, workspace, workspace_bytes, records);
+  if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
+  return launch_main(h, plan_dev, q, k, cu_dev, o, lse, softmax_scale, workspace, records, stream);
+}
+
+extern "C" libra_status libra_attn_fwd(const void *plan, const void *plan_dev, const void *q,
+                                       const void *k, const void *v, const int32_t *cu_dev, void *o,
+                                       float *lse, float softmax_scale, void *workspace,
+                                       size_t workspace_bytes, libra_cu_record *records, void *stream) {
+  libra_plan_info h;
+  libra_status st = check_header(plan, &h);
+  if (st == LIBRA_OK) st = check_prepare(h, v, workspace, workspace_bytes);
+  if (st == LIBRA_OK)
+    st = check_main(h, plan_dev, q, k, cu_dev, o, lse, softmax_scale, workspace, workspace_bytes, records);
+  if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
+  st = launch_transpose(v, workspace, h.params.total_tokens, h.params.h_kv, h.params.head_dim, stream);
+  if (st != LIBRA_OK) return st;
+  return launch_main(h, plan_dev, q, k, cu_dev, o, lse, softmax_scale, workspace, records, stream);
 }
 
 extern "C" libra_status libra_device_clock_khz(int32_t *khz) {

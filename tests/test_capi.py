@@ -1,0 +1,270 @@
+"""C-ABI tests that need no GPU: exports, planner parity with the oracle, host validation.
+
+The library is loaded on the CPU machine (the HIP runtime loads without a device);
+every call here returns before anything would be enqueued.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import packed_varlen_attention_cu_amd as lib
+from oracle import plan as P
+import synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "libra.h")
+FAKE = 0x100000           # a well-aligned address that is never dereferenced on the host
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:libra_status|const char \*|size_t)\s*\*?\s*(libra_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 13
+    handle = ctypes.CDLL(lib.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), n
+
+
+def make_plan(lens, h_q, h_kv, d, B, W, **kw):
+    cu = synth.cu_seqlens(lens)
+    return lib.Plan(cu, total_tokens=int(sum(lens)), h_q=h_q, h_kv=h_kv, head_dim=d, tile_tokens=B,
+                    tile_heads=W, **kw), cu
+
+
+CASES = [
+    ([1024, 512, 256, 256], 4, 4, 64, 256, 2, {}),
+    ([1024, 512, 256, 256], 4, 4, 64, 384, 1, {"num_cus": 16}),
+    ([5, 0, 3, 9, 0], 4, 2, 128, 6, 2, {"num_cus": 3}),
+    (list(synth.make_lengths(synth.WORKLOADS["gqa_32k"].with_tokens(9000), 0)), 32, 8, 128, 4096, 8, {}),
+    (list(synth.make_lengths(synth.WORKLOADS["train_256k"].with_tokens(7000), 1)), 32, 4, 128, 1000, 4,
+     {"num_cus": 64, "item_overhead": 4096}),
+    (list(synth.make_lengths(synth.WORKLOADS["share_1m"].with_tokens(6000, (4000,)), 2)), 8, 1, 128, 512, 2,
+     {"num_cus": 32}),
+    ([7, 300, 1, 1, 250], 12, 4, 64, 100, 6, {"num_cus": 9}),
+    ([400, 600], 8, 2, 128, 128, 8, {"assign": 1, "num_cus": 7}),
+]
+
+
+@pytest.mark.parametrize("lens,h_q,h_kv,d,B,W,kw", CASES)
+def test_planner_matches_oracle(lens, h_q, h_kv, d, B, W, kw):
+    plan, cu = make_plan(lens, h_q, h_kv, d, B, W, **kw)
+    L = int(sum(lens))
+    info = plan.info
+    ncu = kw.get("num_cus", 0) or 256
+    assert info.num_cus == ncu
+    # tiles (eq. 6-8)
+    ref_tiles = P.sh_tiles(cu, L, h_q, B, W)
+    got = plan.tiles
+    assert len(got) == len(ref_tiles)
+    for g_, r in zip(got, ref_tiles):
+        for f in ("tile_id", "block", "shard", "tok_begin", "tok_end", "head_begin", "head_count",
+                  "sample_first", "sample_last", "pairs"):
+            assert int(g_[f]) == r[f], f
+    assert info.total_pairs == sum(t["pairs"] for t in ref_tiles)
+    # forward items and their placement
+    mode = "rr" if kw.get("assign", 0) == 1 else "lpt"
+    ov = kw.get("item_overhead", 0)
+    items = P.fwd_items(cu, L, h_q, h_kv, B, W, overhead=ov)
+    offsets, ids, load = P.queue([it["cost"] for it in items], ncu, 0.03, mode)
+    assert list(plan.cu_off) == offsets
+    got_items = plan.items
+    assert [int(x) for x in got_items["id"]] == ids
+    for g_, i in zip(got_items, ids):
+        r = items[i]
+        for f in ("row0", "nrows", "kv_head", "head0", "nheads", "tile_id", "cost", "pairs"):
+            assert int(g_[f]) == r[f], f
+    assert info.load_max == max(load) and info.load_sum == sum(load)
+    assert [int(t["n_items"]) for t in got] == [sum(1 for it in items if it["tile_id"] == t["tile_id"])
+                                               for t in ref_tiles]
+    # key-major dK/dV items and their placement
+    kv = P.kv_items(cu, L, h_q, h_kv, overhead=ov)
+    offsets, ids, load = P.queue([it["cost"] for it in kv], ncu, 0.03, mode)
+    assert list(plan.kv_cu_off) == offsets
+    got_kv = plan.kv_items
+    assert [int(x) for x in got_kv["id"]] == ids
+    for g_, i in zip(got_kv, ids):
+        r = kv[i]
+        for f in ("row0", "nrows", "kv_head", "head0", "nheads", "tile_id", "cost", "pairs"):
+            assert int(g_[f]) == r[f], f
+    assert info.kv_load_max == max(load) and info.kv_load_sum == sum(load)
+
+
+def test_plan_is_bitwise_deterministic():
+    lens = list(synth.make_lengths(synth.WORKLOADS["train_256k"], 0))
+    a, _ = make_plan(lens, 32, 4, 128, 8192, 4)
+    b, _ = make_plan(lens, 32, 4, 128, 8192, 4)
+    assert np.array_equal(a.host, b.host)
+
+
+def test_full_size_plans_match_closed_form_and_balance():
+    for name in ("gqa_32k", "skew_128k_a", "skew_128k_b", "share_1m", "train_256k"):
+        w = synth.WORKLOADS[name]
+        lens = synth.make_lengths(w, 0)
+        plan, cu = make_plan(list(lens), w.h_q, w.h_kv, w.head_dim, w.tile_tokens, w.tile_heads)
+        assert plan.info.total_pairs == w.h_q * int((lens * (lens + 1) // 2).sum())
+        assert plan.info.load_sum == plan.info.total_pairs        # no overhead: cost == pairs
+        assert plan.info.load_max / (plan.info.load_sum / 256) < 1.01, name
+
+
+def test_plan_check_rejects_corruption():
+    plan, _ = make_plan([100, 200], 4, 2, 128, 64, 2)
+    lib.libra_plan_check(plan.host)
+    bad = plan.host.copy()
+    bad[plan.info.off_items + 5] ^= 0x40
+    with pytest.raises(lib.LibraError) as e:
+        lib.libra_plan_check(bad)
+    assert e.value.status == lib.LIBRA_EINVAL
+    with pytest.raises(lib.LibraError):
+        lib.libra_plan_check(plan.host[:-8].copy())
+
+
+def _params(**over):
+    p = dict(total_tokens=10, num_samples=2, h_q=4, h_kv=2, head_dim=128, tile_tokens=4, tile_heads=2,
+             num_cus=0, tau=0.03, assign=0, item_overhead=0)
+    p.update(over)
+    return lib.PlanParams(*[p[f] for f, _ in lib.PlanParams._fields_])
+
+
+def _plan_status(cu, params, capacity=None):
+    cu = np.asarray(cu, dtype=np.int32)
+    need = ctypes.c_size_t(0)
+    st = lib._lib.libra_plan(cu.ctypes.data, ctypes.byref(params), None, ctypes.byref(need))
+    if st != 0 or capacity is None:
+        return st, need.value
+    buf = np.zeros(capacity // 8 + 1, dtype=np.uint64)
+    cap = ctypes.c_size_t(capacity)
+    st = lib._lib.libra_plan(cu.ctypes.data, ctypes.byref(params), buf.ctypes.data, ctypes.byref(cap))
+    return st, cap.value
+
+
+@pytest.mark.parametrize("cu,over,status", [
+    ([1, 4, 10], {}, lib.LIBRA_EINVAL),                       # cu[0] != 0
+    ([0, 6, 4], {}, lib.LIBRA_EINVAL),                        # decreasing
+    ([0, 4, 9], {}, lib.LIBRA_EINVAL),                        # cu[n] != L
+    ([0, 4, 10], {"h_q": 5}, lib.LIBRA_EINVAL),               # h_q % h_kv
+    ([0, 4, 10], {"tile_heads": 3}, lib.LIBRA_EINVAL),        # W does not divide h_q
+    ([0, 4, 10], {"tile_tokens": 0}, lib.LIBRA_EINVAL),
+    ([0, 4, 10], {"num_cus": -1}, lib.LIBRA_EINVAL),
+    ([0, 4, 10], {"assign": 7}, lib.LIBRA_EINVAL),
+    ([0, 4, 10], {"tau": float("nan")}, lib.LIBRA_EINVAL),
+    ([0, 4, 10], {"item_overhead": -1}, lib.LIBRA_EINVAL),
+    ([0, 4, 10], {"head_dim": 96}, lib.LIBRA_EUNSUPPORTED),
+    ([0, 4, 10], {}, lib.LIBRA_OK),
+])
+def test_plan_errors(cu, over, status):
+    assert _plan_status(cu, _params(**over))[0] == status
+
+
+def test_plan_reports_size_when_buffer_too_small():
+    st, need = _plan_status([0, 4, 10], _params())
+    assert st == 0 and need > 0
+    st, got = _plan_status([0, 4, 10], _params(), capacity=need - 8)
+    assert st == lib.LIBRA_ESIZE and got == need
+
+
+def test_empty_pack_plans_and_runs_nothing():
+    plan = lib.Plan(np.array([0], dtype=np.int32), total_tokens=0, h_q=4, h_kv=2, head_dim=128,
+                    tile_tokens=64, tile_heads=2)
+    assert plan.info.n_tiles == 0 and plan.info.n_items == 0 and plan.info.n_kv_items == 0
+    # L = 0: every entry point returns OK before touching any pointer or the device
+    lib.libra_attn_fwd(plan.host, None, None, None, None, None, None, None, 0.1, None, 0, None, None)
+    lib.libra_attn_bwd(plan.host, None, None, None, None, None, None, None, None, None, None, None, 0.1,
+                       None, 0, None, None)
+
+
+# ------------------------------------------------------------- forward / backward validation
+@pytest.fixture(scope="module")
+def small_plan():
+    plan, cu = make_plan([100, 28], 4, 2, 128, 64, 2)
+    return plan
+
+
+def fwd_args(plan, **over):
+    ws = lib.libra_attn_fwd_workspace(plan.host)
+    a = dict(plan_host=plan.host, plan_dev=FAKE, q=FAKE, k=FAKE, v=FAKE, cu=FAKE, o=FAKE, lse=FAKE,
+             scale=0.1, ws=FAKE, ws_bytes=ws, rec=None, stream=None)
+    a.update(over)
+    return a
+
+
+def call_fwd(a):
+    return lib._lib.libra_attn_fwd(a["plan_host"].ctypes.data, a["plan_dev"], a["q"], a["k"], a["v"], a["cu"],
+                                   a["o"], a["lse"], a["scale"], a["ws"], a["ws_bytes"], a["rec"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"q": None}, lib.LIBRA_EINVAL), ({"k": None}, lib.LIBRA_EINVAL), ({"v": None}, lib.LIBRA_EINVAL),
+    ({"o": None}, lib.LIBRA_EINVAL), ({"lse": None}, lib.LIBRA_EINVAL), ({"cu": None}, lib.LIBRA_EINVAL),
+    ({"plan_dev": None}, lib.LIBRA_EINVAL), ({"ws": None}, lib.LIBRA_EINVAL),
+    ({"q": FAKE + 8}, lib.LIBRA_EINVAL), ({"rec": FAKE + 4}, lib.LIBRA_EINVAL),
+    ({"scale": 0.0}, lib.LIBRA_EINVAL), ({"scale": float("nan")}, lib.LIBRA_EINVAL),
+    ({"scale": -1.0}, lib.LIBRA_EINVAL), ({"ws_bytes": 16}, lib.LIBRA_ESIZE),
+])
+def test_fwd_validation(small_plan, over, status):
+    assert call_fwd(fwd_args(small_plan, **over)) == status
+
+
+def test_fwd_rejects_foreign_plan(small_plan):
+    bad = small_plan.host.copy()
+    bad[0] ^= 1
+    assert call_fwd(fwd_args(small_plan, plan_host=bad)) == lib.LIBRA_EINVAL
+
+
+def test_phase_entry_points_validate(small_plan):
+    h = small_plan.host.ctypes.data
+    fws = lib.libra_attn_fwd_workspace(small_plan.host)
+    bws = lib.libra_attn_bwd_workspace(small_plan.host)
+    L_ = lib._lib
+    assert L_.libra_attn_fwd_prepare(h, None, FAKE, fws, None) == lib.LIBRA_EINVAL
+    assert L_.libra_attn_fwd_prepare(h, FAKE, FAKE, fws - 1, None) == lib.LIBRA_ESIZE
+    assert L_.libra_attn_fwd_main(h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, 0, None, None) == lib.LIBRA_ESIZE
+    assert L_.libra_attn_fwd_main(h, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, fws, None, None) == lib.LIBRA_EINVAL
+    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, None, FAKE, FAKE, bws, None) == lib.LIBRA_EINVAL
+    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE, FAKE + 16, bws, None) == lib.LIBRA_EINVAL
+    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE, FAKE, bws - 1, None) == lib.LIBRA_ESIZE
+    dkdv = [h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, bws, None, None]
+    for i in (2, 3, 4, 5, 6, 7, 8, 9):           # q k v dout lse cu dk dv
+        args = list(dkdv)
+        args[i] = None
+        assert L_.libra_attn_bwd_dkdv(*args) == lib.LIBRA_EINVAL, i
+    dq = [h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, bws, None, None]
+    for i in (2, 3, 4, 5, 6, 7, 8):              # q k v dout lse cu dq: v is read by the dQ kernel
+        args = list(dq)
+        args[i] = None
+        assert L_.libra_attn_bwd_dq(*args) == lib.LIBRA_EINVAL, i
+    args = list(dq)
+    args[9] = ctypes.c_float(float("inf"))
+    assert L_.libra_attn_bwd_dq(*args) == lib.LIBRA_EINVAL
+
+
+def test_bwd_validation(small_plan):
+    h = small_plan.host.ctypes.data
+    bws = lib.libra_attn_bwd_workspace(small_plan.host)
+    full = [h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, bws,
+            None, None]
+    for i in range(1, 12):
+        args = list(full)
+        args[i] = None
+        assert lib._lib.libra_attn_bwd(*args) == lib.LIBRA_EINVAL, i
+    args = list(full)
+    args[14] = bws - 1
+    assert lib._lib.libra_attn_bwd(*args) == lib.LIBRA_ESIZE
+
+
+def test_workspace_sizes(small_plan):
+    Lp = 128
+    assert lib.libra_attn_fwd_workspace(small_plan.host) == 2 * 128 * Lp * 2
+    # Q^T and dO^T (h_q), K^T (h_kv), D (fp32 [h_q][L])
+    assert lib.libra_attn_bwd_workspace(small_plan.host) == 2 * (4 * 128 * Lp * 2) + 2 * 128 * Lp * 2 + 2048
+
+
+def test_status_strings():
+    assert lib.libra_status_str(0) == "ok"
+    assert lib.libra_status_str(-2) == "buffer too small"
+    assert lib.libra_status_str(123) == "unknown status"
