@@ -145,26 +145,28 @@ def traffic_for(kernel, workload, launches_bytes_fn):
 
 
 def summarize_pmc(fetch_dir, write_dir, workload, copy_bytes):
-    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic_*.json."""
-    import csv
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic_*.json.
+
+    Each counter is scaled by what it reads for the calibration copy of
+    ``copy_bytes`` (a plain device-to-device copy run by --calibrate-copy)."""
+    import sqlite3
 
     def read(d, counter):
         rows = []
-        for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            with open(p) as f:
-                for r in csv.DictReader(f):
-                    if r.get("Counter_Name") == counter:
-                        rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        for p in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+            con = sqlite3.connect(p)
+            rows += list(con.execute("select kernel_name, value from counters_collection where counter_name = ?",
+                                     (counter,)))
         return rows
 
     fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
 
     def per_kernel(rows, sym):
-        v = [x for name, x in rows if sym in name]
+        v = [x for name, x in rows if sym + "<" in name]
         return float(np.mean(v)) if v else None
 
     def copy_value(rows):
-        v = [x for name, x in rows if "copy" in name.lower() or "elementwise" in name.lower()]
+        v = [x for name, x in rows if "copyBuffer" in name]
         return max(v) if v else None
 
     fc, wc = copy_value(fetch), copy_value(write)
