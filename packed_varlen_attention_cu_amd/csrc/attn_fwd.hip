@@ -26,6 +26,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <type_traits>
 
 #include "device_common.h"
 #include "libra.h"
@@ -90,19 +91,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void attn_fwd_kernel(FwdArgs a) {
   constexpr int NS = D / 16;                    // reduction slabs of d
   constexpr int ND = D / 32;                    // 32-row tiles of d in O^T
-  constexpr int KS = D + 8;                     // K row stride in LDS (elements)
-  constexpr int VS = kBN + 8;                   // V^T row stride in LDS (elements)
-  constexpr int KCH = kBN * D / 8 / kThreads;   // 16-byte chunks per thread, K block
-  constexpr int VCH = D * kBN / 8 / kThreads;   // 16-byte chunks per thread, V^T block
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * VS];
+  constexpr int CH = D / 8;                     // 16-byte chunks per K row
+  constexpr int KJ = kBN * CH / 64 / 4;         // LDS-DMA instructions per wave, K block
+  constexpr int VJ = D * (kBN / 8) / 64 / 4;    // LDS-DMA instructions per wave, V^T block
+  // Two buffers of K [kBN][D] and V^T [D][kBN], rows unpadded; 16-byte chunk c
+  // of row r sits at position c ^ (r mod chunks-per-row) so operand reads hit
+  // distinct banks.
+  // Distinct arrays per buffer let the compiler see that a copy in flight into
+  // one buffer cannot alias reads of the other, so it adds no waits for it.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds1[kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[D * kBN];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[D * kBN];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int half = lane >> 5, col = lane & 31;
   const int w = blockIdx.x;
   const uint64_t t_start = wall_clock64();
   const int beg = a.cu_off[w], end = a.cu_off[w + 1];
   const float sl2 = a.scale_log2;
+  const uint32_t kl0 = lds_addr(k_lds0), kl1 = lds_addr(k_lds1);
+  const uint32_t vl0 = lds_addr(v_lds0), vl1 = lds_addr(v_lds1);
   const float NEG_INF = -__builtin_inff();
 
   for (int it = beg; it < end; ++it) {
@@ -138,42 +147,39 @@ void attn_fwd_kernel(FwdArgs a) {
       for (int dt = 0; dt < ND; ++dt) oacc[qt][dt] = zero16();
     float m_run[2] = {NEG_INF, NEG_INF}, l_run[2] = {0.0f, 0.0f};
 
-    u32x4 kreg[KCH], vreg[VCH];
-    auto gload = [&](int k0) {
+    // Queue the K and V^T blocks at key k0 into LDS buffer BUF (no registers).
+    auto issue = [&](int k0, auto bufc) {
+      const uint32_t kdst = decltype(bufc)::value == 0 ? kl0 : kl1;
+      const uint32_t vdst = decltype(bufc)::value == 0 ? vl0 : vl1;
 #pragma unroll
-      for (int j = 0; j < KCH; ++j) {
-        const int c = tid + kThreads * j;
-        const int r = c / (D / 8), cc = c % (D / 8);
-        const int key = k0 + r;
-        kreg[j] = key < a.L ? *reinterpret_cast<const u32x4 *>(a.k + ((int64_t)key * a.h_kv + kvh) * D + cc * 8)
-                            : zero_u32x4();
+      for (int j = 0; j < KJ; ++j) {
+        const int slot = (wave * KJ + j) * 64 + lane;
+        const int r = slot / CH, c = (slot % CH) ^ (r & (CH - 1));
+        const int key = min(k0 + r, a.L - 1);     // rows past L are masked; keep the address valid
+        lds_dma16(a.k + ((int64_t)key * a.h_kv + kvh) * D + c * 8, kdst + (wave * KJ + j) * 1024);
       }
 #pragma unroll
-      for (int j = 0; j < VCH; ++j) {
-        const int c = tid + kThreads * j;
-        const int d = c / (kBN / 8), cc = c % (kBN / 8);
-        vreg[j] = *reinterpret_cast<const u32x4 *>(a.vt + ((int64_t)kvh * D + d) * a.Lp + k0 + cc * 8);
-      }
-    };
-    auto lstore = [&]() {
-#pragma unroll
-      for (int j = 0; j < KCH; ++j) {
-        const int c = tid + kThreads * j;
-        *reinterpret_cast<u32x4 *>(k_lds + (c / (D / 8)) * KS + (c % (D / 8)) * 8) = kreg[j];
-      }
-#pragma unroll
-      for (int j = 0; j < VCH; ++j) {
-        const int c = tid + kThreads * j;
-        *reinterpret_cast<u32x4 *>(v_lds + (c / (kBN / 8)) * VS + (c % (kBN / 8)) * 8) = vreg[j];
+      for (int j = 0; j < VJ; ++j) {
+        const int slot = (wave * VJ + j) * 64 + lane;
+        const int d = slot / (kBN / 8), c = (slot % (kBN / 8)) ^ (d & 7);
+        lds_dma16(a.vt + ((int64_t)kvh * D + d) * a.Lp + k0 + c * 8, vdst + (wave * VJ + j) * 1024);
       }
     };
 
-    if (nblk > 0) gload(kstart);
-    for (int b = 0; b < nblk; ++b) {
+    // One key block: wait for its copies (the next block's are queued first),
+    // then compute from buffer BUF.
+    auto block = [&](int b, auto bufc) {
+      constexpr int BUF = decltype(bufc)::value;
       const int k0 = kstart + b * kBN;
-      lstore();
-      __syncthreads();
-      if (b + 1 < nblk) gload(k0 + kBN);
+      if (b + 1 < nblk) {
+        issue(k0 + kBN, std::integral_constant<int, BUF ^ 1>{});
+        wait_vmem<KJ + VJ>();       // this block's copies have landed; the next block's fly on
+      } else {
+        wait_vmem<0>();
+      }
+      block_barrier();
+      const uint16_t *kb = BUF == 0 ? k_lds0 : k_lds1;
+      const uint16_t *vb = BUF == 0 ? v_lds0 : v_lds1;
 
       bool touch = false, partial = false;
 #pragma unroll
@@ -192,8 +198,9 @@ void attn_fwd_kernel(FwdArgs a) {
           sacc[kt][1] = zero16();
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
+            const int row = kt * 32 + sigma_row(col);
             const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                k_lds + (kt * 32 + sigma_row(col)) * KS + 16 * s + 8 * half));
+                kb + row * D + (((2 * s + half) ^ (row & (CH - 1))) * 8)));
             sacc[kt][0] = mfma32x32x16(ka, qop[0][s], sacc[kt][0]);
             sacc[kt][1] = mfma32x32x16(ka, qop[1][s], sacc[kt][1]);
           }
@@ -251,13 +258,22 @@ void attn_fwd_kernel(FwdArgs a) {
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
+              const int row = dt * 32 + col;
               const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                  v_lds + (dt * 32 + col) * VS + kt * 32 + 16 * t + 8 * half));
+                  vb + row * kBN + (((kt * 4 + 2 * t + half) ^ (row & 7)) * 8)));
               oacc[0][dt] = mfma32x32x16(va, as_bf16x8(pw[0][kt][t]), oacc[0][dt]);
               oacc[1][dt] = mfma32x32x16(va, as_bf16x8(pw[1][kt][t]), oacc[1][dt]);
             }
       }
-      __syncthreads();
+      wait_lds();                   // every read of this buffer is done before it is refilled
+      block_barrier();
+    };
+
+    wait_vmem<0>();                 // nothing else in flight: the counts in `block` are exact
+    if (nblk > 0) issue(kstart, std::integral_constant<int, 0>{});
+    for (int b = 0; b < nblk; b += 2) {
+      block(b, std::integral_constant<int, 0>{});
+      if (b + 1 < nblk) block(b + 1, std::integral_constant<int, 1>{});
     }
 
 #pragma unroll

@@ -98,6 +98,41 @@ __device__ __forceinline__ uint32_t xcc_id_reg() {
   return __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 20);   // HW_REG_XCC_ID
 }
 
+// Direct global -> LDS copy of 16 bytes per lane: lane i of the wave writes
+// lds_base + 16 * i (lds_base is made wave-uniform); lanes switched off by
+// control flow write nothing.  The copy is issued from inline assembly so the
+// compiler does not track it: callers account for every copy themselves with
+// wait_vmem (the vector-memory counter retires in issue order) and a barrier
+// before another wave reads the data.
+__device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gsrc) : "memory", "m0");
+}
+
+// Byte address of a __shared__ object in the LDS aperture.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Index of the calling wave in its workgroup, as a wave-uniform value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Wait until this wave's LDS reads and writes have completed.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier that keeps the compiler from moving memory accesses across
+// it but adds no memory-counter waits: the kernels wait explicitly (wait_vmem
+// for their LDS-DMA copies, wait_lds before a buffer is refilled), so copies
+// for the next block stay in flight across the barrier.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // Row m of a 32-row C tile produced from A rows loaded in the order sigma:
 // sigma swaps bits 2 and 3, so C registers 8t..8t+7 of lane half h hold
 // A rows 16t + 8h + 0..7 (contiguous), ready to be a B operand.
