@@ -215,6 +215,11 @@ libra_status libra_attn_bwd_dq(const void *plan, const void *plan_dev,
 /* Frequency of the clock in libra_cu_record, for the current device. */
 libra_status libra_device_clock_khz(int32_t *khz);
 
+/* Name of the HIP error behind the calling thread's most recent LIBRA_EHIP
+ * (e.g. "hipErrorInvalidDeviceFunction"), or "" if this thread has had none.
+ * The string is static; the call never fails. */
+const char *libra_last_hip_error(void);
+
 /* Static description of a status code. */
 const char *libra_status_str(libra_status status);
 

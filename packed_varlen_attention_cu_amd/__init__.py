@@ -26,7 +26,8 @@ PLAN_MAGIC, PLAN_VERSION = 0x4152424C, 1
 class LibraError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
-        super().__init__(f"{what}: {libra_status_str(status)} ({status})")
+        detail = f" [{libra_last_hip_error()}]" if status == LIBRA_EHIP else ""
+        super().__init__(f"{what}: {libra_status_str(status)} ({status}){detail}")
 
 
 class PlanParams(ctypes.Structure):
@@ -67,6 +68,13 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python packed_varlen_attention_cu_amd/build.py`")
+    # torch ships its own HIP runtime under the same soname as the system one.
+    # Loading torch first makes the dynamic loader resolve this library's HIP
+    # dependency to that already-loaded runtime, so the process holds exactly
+    # one HIP runtime and torch's device pointers and streams are valid here.
+    # (Loaded the other way round, two runtimes coexist and the second one
+    # does not see the device.)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     lib.libra_plan.argtypes = [vp, ctypes.POINTER(PlanParams), vp, ctypes.POINTER(sz)]
@@ -84,6 +92,8 @@ def _load():
     lib.libra_device_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int32)]
     lib.libra_status_str.argtypes = [ctypes.c_int]
     lib.libra_status_str.restype = ctypes.c_char_p
+    lib.libra_last_hip_error.argtypes = []
+    lib.libra_last_hip_error.restype = ctypes.c_char_p
     for name in ("libra_plan", "libra_plan_check", "libra_attn_fwd_workspace", "libra_attn_bwd_workspace",
                  "libra_attn_fwd", "libra_attn_bwd", "libra_device_clock_khz", "libra_attn_fwd_prepare",
                  "libra_attn_fwd_main", "libra_attn_bwd_prepare", "libra_attn_bwd_dkdv", "libra_attn_bwd_dq"):
@@ -111,6 +121,10 @@ def _ptr(t):
 # ----------------------------------------------------------------- C entry points
 def libra_status_str(status: int) -> str:
     return _lib.libra_status_str(int(status)).decode()
+
+
+def libra_last_hip_error() -> str:
+    return _lib.libra_last_hip_error().decode()
 
 
 def libra_plan(cu_seqlens, params: PlanParams) -> np.ndarray:

@@ -503,13 +503,14 @@ libra_status launch_prepare(const libra_plan_info &h, const void *q, const void 
   const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
   hipStream_t s = static_cast<hipStream_t>(stream);
   float *dvec = reinterpret_cast<float *>(w + lay.dvec);
+  clear_hip_error();
   if (p.head_dim == 128)
     hipLaunchKernelGGL(rowdot_kernel<128>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t *>(o),
                        static_cast<const uint16_t *>(dout), dvec, p.total_tokens, p.h_q);
   else
     hipLaunchKernelGGL(rowdot_kernel<64>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t *>(o),
                        static_cast<const uint16_t *>(dout), dvec, p.total_tokens, p.h_q);
-  return hipGetLastError() == hipSuccess ? LIBRA_OK : LIBRA_EHIP;
+  return launch_status();
 }
 
 libra_status launch_dkdv(const libra_plan_info &h, BwdArgs a, const void *plan_dev, void *dk, void *dv,
@@ -521,11 +522,12 @@ libra_status launch_dkdv(const libra_plan_info &h, BwdArgs a, const void *plan_d
   a.dv = static_cast<uint16_t *>(dv);
   a.records = records;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  clear_hip_error();
   if (h.params.head_dim == 128)
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
-  return hipGetLastError() == hipSuccess ? LIBRA_OK : LIBRA_EHIP;
+  return launch_status();
 }
 
 libra_status launch_dq(const libra_plan_info &h, BwdArgs a, const void *plan_dev, void *dq,
@@ -536,11 +538,12 @@ libra_status launch_dq(const libra_plan_info &h, BwdArgs a, const void *plan_dev
   a.dq = static_cast<uint16_t *>(dq);
   a.records = records;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  clear_hip_error();
   if (h.params.head_dim == 128)
     hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
-  return hipGetLastError() == hipSuccess ? LIBRA_OK : LIBRA_EHIP;
+  return launch_status();
 }
 
 }  // namespace

@@ -317,16 +317,30 @@ libra_status launch_transpose(const void *src, void *dst, int L, int H, int D, v
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int Lp = (int)round_up(L, kTileTok);
   dim3 grid(Lp / kTileTok, H);
+  clear_hip_error();
   if (D == 128)
     hipLaunchKernelGGL(transpose_heads_kernel<128>, grid, dim3(kThreads), 0, s,
                        static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst), L, H, Lp);
   else
     hipLaunchKernelGGL(transpose_heads_kernel<64>, grid, dim3(kThreads), 0, s,
                        static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst), L, H, Lp);
-  return hipGetLastError() == hipSuccess ? LIBRA_OK : LIBRA_EHIP;
+  return launch_status();
 }
 
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+namespace {
+thread_local hipError_t g_last_hip_error = hipSuccess;
+}
+
+void clear_hip_error() { (void)hipGetLastError(); }
+
+libra_status launch_status() {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return LIBRA_OK;
+  g_last_hip_error = e;
+  return LIBRA_EHIP;
+}
 
 }  // namespace libra
 
@@ -392,11 +406,12 @@ libra_status launch_main(const libra_plan_info &h, const void *plan_dev, const v
   a.h_kv = p.h_kv;
   a.scale_log2 = scale * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  clear_hip_error();
   if (p.head_dim == 128)
     hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
-  return hipGetLastError() == hipSuccess ? LIBRA_OK : LIBRA_EHIP;
+  return launch_status();
 }
 
 }  // namespace
@@ -436,6 +451,11 @@ extern "C" libra_status libra_attn_fwd(const void *plan, const void *plan_dev, c
   st = launch_transpose(v, workspace, h.params.total_tokens, h.params.h_kv, h.params.head_dim, stream);
   if (st != LIBRA_OK) return st;
   return launch_main(h, plan_dev, q, k, cu_dev, o, lse, softmax_scale, workspace, records, stream);
+}
+
+extern "C" const char *libra_last_hip_error(void) {
+  const hipError_t e = g_last_hip_error;
+  return e == hipSuccess ? "" : hipGetErrorName(e);
 }
 
 extern "C" libra_status libra_device_clock_khz(int32_t *khz) {

@@ -25,4 +25,12 @@ libra_status launch_transpose(const void *src, void *dst, int L, int H, int D, v
 
 bool misaligned(const void *p, uintptr_t a);
 
+// Clear the calling thread's pending HIP error before a launch, so that the
+// status taken after it belongs to that launch alone.
+void clear_hip_error();
+
+// LIBRA_OK if the launches since clear_hip_error() were accepted; otherwise
+// remember the HIP error for libra_last_hip_error() and return LIBRA_EHIP.
+libra_status launch_status();
+
 }  // namespace libra

@@ -268,3 +268,19 @@ def test_status_strings():
     assert lib.libra_status_str(0) == "ok"
     assert lib.libra_status_str(-2) == "buffer too small"
     assert lib.libra_status_str(123) == "unknown status"
+
+
+def test_last_hip_error_is_empty_without_a_failed_launch():
+    import threading
+    got = []
+    t = threading.Thread(target=lambda: got.append(lib.libra_last_hip_error()))
+    t.start()
+    t.join()
+    assert got == [""]
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Exactly one HIP runtime is mapped once the package is imported."""
+    maps = open(f"/proc/{os.getpid()}/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) == 1, paths
