@@ -16,7 +16,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_lib", "liblibra.so")
+# LIBRA_LIB may name another build of the same library (e.g. one compiled
+# with different tuning macros); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("LIBRA_LIB") or os.path.join(_HERE, "_lib", "liblibra.so")
 
 LIBRA_OK, LIBRA_EINVAL, LIBRA_ESIZE, LIBRA_EUNSUPPORTED, LIBRA_EHIP = 0, -1, -2, -3, -4
 ASSIGN_PLACER, ASSIGN_ROUND_ROBIN = 0, 1

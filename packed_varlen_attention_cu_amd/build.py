@@ -39,9 +39,11 @@ def _run(cmd):
     return r
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(LIBDIR, exist_ok=True)
-    objdir = os.path.join(LIBDIR, "obj")
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source and link ``out``; ``defines`` are extra -D macros."""
+    libdir = os.path.dirname(os.path.abspath(out))
+    os.makedirs(libdir, exist_ok=True)
+    objdir = os.path.join(libdir, "obj_" + os.path.basename(out))
     shutil.rmtree(objdir, ignore_errors=True)
     os.makedirs(objdir)
     jobs = []
@@ -49,18 +51,18 @@ def build(verbose: bool = False) -> str:
         jobs.append([HIPCC, *COMMON, "-x", "c++", "-c", os.path.join(CSRC, src),
                      "-o", os.path.join(objdir, src + ".o")])
     for src in DEVICE_SOURCES:
-        jobs.append([HIPCC, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src),
+        jobs.append([HIPCC, *COMMON, *DEVICE_FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
                      "-o", os.path.join(objdir, src + ".o")])
     with ThreadPoolExecutor(min(8, len(jobs))) as ex:
         for r in ex.map(_run, jobs):
             if verbose and (r.stdout or r.stderr):
                 print(r.stdout, r.stderr, file=sys.stderr)
     objs = [os.path.join(objdir, s + ".o") for s in HOST_SOURCES + DEVICE_SOURCES]
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     shutil.rmtree(objdir, ignore_errors=True)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":

@@ -86,14 +86,33 @@ struct FwdArgs {
   float scale_log2;
 };
 
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+// Workgroup shape of the forward kernel: kFwdWaves waves, each owning
+// 32 * kFwdQT query positions of one head, so a workgroup covers the 256 query
+// columns of one work item.  Eight waves of 32 queries run two waves per SIMD,
+// so one wave's softmax (VALU) overlaps the other's matrix products (MFMA).
+#ifndef LIBRA_FWD_WAVES
+#define LIBRA_FWD_WAVES 8
+#endif
+constexpr int kFwdWaves = LIBRA_FWD_WAVES;
+constexpr int kFwdQT = 8 / kFwdWaves;             // 32-query tiles per wave
+static_assert(kFwdWaves * 32 * kFwdQT == 256, "a work item is 256 query columns");
+
+// Exponent slack of the online softmax: the running maximum m (log2 units)
+// is only raised when a block's maximum exceeds it by more than this, so O is
+// rescaled rarely; in between, P = 2^(s c - m) stays below 2^kRescaleSlack.
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D, int QT, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void attn_fwd_kernel(FwdArgs a) {
+  constexpr int QW = 32 * QT;                   // query positions per wave
   constexpr int NS = D / 16;                    // reduction slabs of d
   constexpr int ND = D / 32;                    // 32-row tiles of d in O^T
   constexpr int CH = D / 8;                     // 16-byte chunks per K row
-  constexpr int KJ = kBN * CH / 64 / 4;         // LDS-DMA instructions per wave, K block
-  constexpr int VJ = D * (kBN / 8) / 64 / 4;    // LDS-DMA instructions per wave, V^T block
+  constexpr int KJ = kBN * CH / 64 / NW;        // LDS-DMA instructions per wave, K block
+  constexpr int VJ = D * (kBN / 8) / 64 / NW;   // LDS-DMA instructions per wave, V^T block
+  static_assert(KJ >= 1 && VJ >= 1 && KJ * NW * 64 == kBN * CH && VJ * NW * 64 == D * kBN / 8,
+                "the waves split each block copy evenly");
   // Two buffers of K [kBN][D] and V^T [D][kBN], rows unpadded; 16-byte chunk c
   // of row r sits at position c ^ (r mod chunks-per-row) so operand reads hit
   // distinct banks.
@@ -113,20 +132,21 @@ void attn_fwd_kernel(FwdArgs a) {
   const uint32_t kl0 = lds_addr(k_lds0), kl1 = lds_addr(k_lds1);
   const uint32_t vl0 = lds_addr(v_lds0), vl1 = lds_addr(v_lds1);
   const float NEG_INF = -__builtin_inff();
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
     const int row0 = item.row0, nrows = item.nrows, kvh = item.kv_head, nh = item.nheads;
     const int head = item.head0 + (wave % nh);
     const int sub = wave / nh;
-    const int wrow0 = row0 + sub * 64;
-    const int wrows = min(64, nrows - sub * 64);
+    const int wrow0 = row0 + sub * QW;
+    const int wrows = min(QW, nrows - sub * QW);
 
-    int qpos[2], qss[2];
-    bool qok[2];
-    bf16x8 qop[2][NS];
+    int qpos[QT], qss[QT];
+    bool qok[QT];
+    bf16x8 qop[QT][NS];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       const int r = qt * 32 + col;
       qok[qt] = r < wrows;
       qpos[qt] = wrow0 + r;
@@ -140,12 +160,17 @@ void attn_fwd_kernel(FwdArgs a) {
     const int kend = row0 + nrows;
     const int nblk = (kend - kstart + kBN - 1) / kBN;
 
-    f32x16 oacc[2][ND];
+    f32x16 oacc[QT][ND];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) oacc[qt][dt] = zero16();
-    float m_run[2] = {NEG_INF, NEG_INF}, l_run[2] = {0.0f, 0.0f};
+    float m_run[QT], l_run[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      m_run[qt] = NEG_INF;
+      l_run[qt] = 0.0f;
+    }
 
     // Queue the K and V^T blocks at key k0 into LDS buffer BUF (no registers).
     auto issue = [&](int k0, auto bufc) {
@@ -183,7 +208,7 @@ void attn_fwd_kernel(FwdArgs a) {
 
       bool touch = false, partial = false;
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < QT; ++qt) {
         if (qok[qt]) {
           touch |= (k0 <= qpos[qt]) && (k0 + kBN - 1 >= qss[qt]);
           partial |= !((k0 >= qss[qt]) && (k0 + kBN - 1 <= qpos[qt]));
@@ -191,25 +216,23 @@ void attn_fwd_kernel(FwdArgs a) {
       }
       if (wave_any(touch)) {
         const bool masked = wave_any(partial);
-        f32x16 sacc[2][2];   // [key tile][query tile]
+        f32x16 sacc[2][QT];   // [key tile][query tile]: S^T, one query column per lane
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          sacc[kt][0] = zero16();
-          sacc[kt][1] = zero16();
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = zero16();
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
             const int row = kt * 32 + sigma_row(col);
             const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(
                 kb + row * D + (((2 * s + half) ^ (row & (CH - 1))) * 8)));
-            sacc[kt][0] = mfma32x32x16(ka, qop[0][s], sacc[kt][0]);
-            sacc[kt][1] = mfma32x32x16(ka, qop[1][s], sacc[kt][1]);
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = mfma32x32x16(ka, qop[qt][s], sacc[kt][qt]);
           }
         }
-        u32x4 pw[2][2][2];   // [query tile][key tile][16-key slab]: bf16 P^T operands
-        float alpha[2];
+        if (masked) {
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          if (masked) {
+          for (int qt = 0; qt < QT; ++qt) {
             const int lo = qok[qt] ? qss[qt] : 1, hi = qok[qt] ? qpos[qt] : 0;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -219,17 +242,39 @@ void attn_fwd_kernel(FwdArgs a) {
                 if (key < lo || key > hi) sacc[kt][qt][r] = NEG_INF;
               }
           }
+        }
+        // Block maximum per query; raise the running maximum only when it is
+        // exceeded by more than the slack (then rescale O and l).
+        float mxs[QT];
+        bool grow = false;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
           float mx = NEG_INF;
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][qt][r]);
-          mx = halves_max(mx);
-          const float m_new = fmaxf(m_run[qt], mx * sl2);
-          const float m_use = m_new == NEG_INF ? 0.0f : m_new;
-          alpha[qt] = exp2_fast(m_run[qt] - m_use);
-          m_run[qt] = m_new;
-          float psum = 0.0f;
+          mxs[qt] = halves_max(mx) * sl2;
+          grow |= mxs[qt] > m_run[qt] + kRescaleSlack;
+        }
+        if (wave_any(grow)) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            const float m_new = fmaxf(m_run[qt], mxs[qt]);
+            const float alpha = exp2_fast(m_run[qt] - (m_new == NEG_INF ? 0.0f : m_new));
+            m_run[qt] = m_new;
+            l_run[qt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) oacc[qt][dt][r] *= alpha;
+          }
+        }
+        u32x4 pw[QT][2][2];   // [query tile][key tile][16-key slab]: bf16 P^T operands
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const float m_use = m_run[qt] == NEG_INF ? 0.0f : m_run[qt];
+          float psum = l_run[qt];
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -239,18 +284,10 @@ void attn_fwd_kernel(FwdArgs a) {
                 const float p0 = exp2_fast(fmaf(sacc[kt][qt][8 * t + 2 * i], sl2, -m_use));
                 const float p1 = exp2_fast(fmaf(sacc[kt][qt][8 * t + 2 * i + 1], sl2, -m_use));
                 const uint32_t wv = pack_bf16x2(p0, p1);
-                psum += bf16_lo(wv) + bf16_hi(wv);
+                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv), ones, psum, false);
                 pw[qt][kt][t][i] = wv;
               }
-          l_run[qt] = l_run[qt] * alpha[qt] + psum;
-        }
-        if (wave_any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) oacc[qt][dt][r] *= alpha[qt];
+          l_run[qt] = psum;
         }
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
@@ -261,8 +298,9 @@ void attn_fwd_kernel(FwdArgs a) {
               const int row = dt * 32 + col;
               const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(
                   vb + row * kBN + (((kt * 4 + 2 * t + half) ^ (row & 7)) * 8)));
-              oacc[0][dt] = mfma32x32x16(va, as_bf16x8(pw[0][kt][t]), oacc[0][dt]);
-              oacc[1][dt] = mfma32x32x16(va, as_bf16x8(pw[1][kt][t]), oacc[1][dt]);
+#pragma unroll
+              for (int qt = 0; qt < QT; ++qt)
+                oacc[qt][dt] = mfma32x32x16(va, as_bf16x8(pw[qt][kt][t]), oacc[qt][dt]);
             }
       }
       wait_lds();                   // every read of this buffer is done before it is refilled
@@ -277,7 +315,7 @@ void attn_fwd_kernel(FwdArgs a) {
     }
 
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
       const float lt = halves_sum(l_run[qt]);
       const float inv = 1.0f / lt;
       if (qok[qt]) {
@@ -408,9 +446,9 @@ libra_status launch_main(const libra_plan_info &h, const void *plan_dev, const v
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_hip_error();
   if (p.head_dim == 128)
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<128, kFwdQT, kFwdWaves>), dim3(h.num_cus), dim3(kFwdWaves * 64), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<64, kFwdQT, kFwdWaves>), dim3(h.num_cus), dim3(kFwdWaves * 64), 0, s, a);
   return launch_status();
 }
 
