@@ -281,7 +281,7 @@ def main():
         timed("fwd_main", lambda: lib.libra_attn_fwd_main(plan.host, plan_dev, q, k, cu_dev, o, lse, scale,
                                                           ws_f, wsf, rec_f, sh))
         if do_bwd:
-            timed("bwd_prepare", lambda: lib.libra_attn_bwd_prepare(plan.host, q, k, o, dout, ws_b, wsb, sh))
+            timed("bwd_prepare", lambda: lib.libra_attn_bwd_prepare(plan.host, q, k, o, dout, lse, ws_b, wsb, sh))
             timed("bwd_dkdv", lambda: lib.libra_attn_bwd_dkdv(plan.host, plan_dev, q, k, v, dout, lse, cu_dev,
                                                               dk, dv, scale, ws_b, wsb, rec_kv, sh))
             timed("bwd_dq", lambda: lib.libra_attn_bwd_dq(plan.host, plan_dev, q, k, v, dout, lse, cu_dev, dq,

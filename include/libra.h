@@ -190,7 +190,7 @@ libra_status libra_attn_bwd(const void *plan, const void *plan_dev,
 /* The backward in three phases on the same stream (libra_attn_bwd enqueues
  * all three, in this order):
  *   _prepare: transposes q, dout and k into the workspace and computes
- *             D = rowsum(dout * o) (fp32);
+ *             D = rowsum(dout * o) and LSE * log2(e) (fp32);
  *   _dkdv:    the key-major persistent kernel writing dk and dv
  *             (records: NULL or libra_cu_record[num_cus]);
  *   _dq:      the query-major persistent kernel writing dq
@@ -198,8 +198,8 @@ libra_status libra_attn_bwd(const void *plan, const void *plan_dev,
  * _dkdv and _dq read the workspace a preceding _prepare filled from the same
  * tensors.  Arguments and errors as for libra_attn_bwd. */
 libra_status libra_attn_bwd_prepare(const void *plan, const void *q, const void *k,
-                                    const void *o, const void *dout, void *workspace,
-                                    size_t workspace_bytes, void *stream);
+                                    const void *o, const void *dout, const float *lse,
+                                    void *workspace, size_t workspace_bytes, void *stream);
 libra_status libra_attn_bwd_dkdv(const void *plan, const void *plan_dev,
                                  const void *q, const void *k, const void *v,
                                  const void *dout, const float *lse,

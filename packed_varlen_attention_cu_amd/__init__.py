@@ -88,7 +88,7 @@ def _load():
                                    vp, sz, vp, vp]
     lib.libra_attn_fwd_prepare.argtypes = [vp, vp, vp, sz, vp]
     lib.libra_attn_fwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
-    lib.libra_attn_bwd_prepare.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.libra_attn_bwd_prepare.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.libra_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
     lib.libra_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
     lib.libra_device_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int32)]
@@ -190,9 +190,9 @@ def libra_attn_fwd_main(plan_host, plan_dev, q, k, cu_seqlens_dev, o, lse, softm
            "libra_attn_fwd_main")
 
 
-def libra_attn_bwd_prepare(plan_host, q, k, o, dout, workspace, workspace_bytes, stream):
-    _check(_lib.libra_attn_bwd_prepare(_ptr(plan_host), _ptr(q), _ptr(k), _ptr(o), _ptr(dout), _ptr(workspace),
-                                       int(workspace_bytes), stream),
+def libra_attn_bwd_prepare(plan_host, q, k, o, dout, lse, workspace, workspace_bytes, stream):
+    _check(_lib.libra_attn_bwd_prepare(_ptr(plan_host), _ptr(q), _ptr(k), _ptr(o), _ptr(dout), _ptr(lse),
+                                       _ptr(workspace), int(workspace_bytes), stream),
            "libra_attn_bwd_prepare")
 
 

@@ -22,6 +22,7 @@
 
 #include <cmath>
 #include <initializer_list>
+#include <type_traits>
 
 #include "device_common.h"
 #include "libra.h"
@@ -33,15 +34,18 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kQB = 64;      // query rows per block in the dK/dV pass
-constexpr int kKB = 32;      // key rows per block in the dQ pass
+constexpr int kKB = 64;      // key rows per block in the dQ pass
 
 inline int64_t round_up64(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// D[h][t] = sum_d dO[t][h][d] * O[t][h][d], one row per D/8 lanes.
+// D[h][t] = sum_d dO[t][h][d] * O[t][h][d], one row per D/8 lanes; also the
+// forward's LSE in log2 units, lse2[h][t] = LSE[h][t] * log2(e).
 template <int D>
 __global__ __launch_bounds__(kThreads) void rowdot_kernel(const uint16_t *__restrict__ o,
                                                           const uint16_t *__restrict__ dout,
-                                                          float *__restrict__ dvec, int L, int h_q) {
+                                                          const float *__restrict__ lse,
+                                                          float *__restrict__ dvec, float *__restrict__ lse2,
+                                                          int L, int h_q) {
   constexpr int LPR = D / 8;
   const int64_t row = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
   const int sub = threadIdx.x % LPR;
@@ -58,6 +62,7 @@ __global__ __launch_bounds__(kThreads) void rowdot_kernel(const uint16_t *__rest
   if (sub == 0 && row < rows) {
     const int64_t t = row / h_q, h = row % h_q;
     dvec[h * L + t] = acc;
+    lse2[h * L + t] = lse[h * L + t] * kLog2e;
   }
 }
 
@@ -66,7 +71,7 @@ struct BwdArgs {
   const int32_t *cu_off;
   const uint16_t *q, *k, *v, *dout;
   const uint16_t *qt, *dot, *kt;   // transposed [heads][D][Lp]
-  const float *lse, *dvec;         // [h_q][L]
+  const float *lse, *dvec, *lse2;  // [h_q][L]: LSE, D = rowsum(dO * O), LSE * log2(e)
   const int32_t *cu;
   uint16_t *dq, *dk, *dv;
   libra_cu_record *records;
@@ -86,26 +91,39 @@ __device__ __forceinline__ void write_record(const BwdArgs &a, int w, int n, uin
 }
 
 // ----------------------------------------------------------------- dK / dV pass
+// Per query block of kQB rows and one head, LDS holds Q and dO (row-major,
+// MFMA A operands of S and dP), Q^T and dO^T (A operands of dK^T and dV^T)
+// and the block's LSE and D values.  Two such buffers alternate: the copies
+// for the next (head, query block) step are queued before the current one is
+// computed.  16-byte chunk c of row r of a row-major block sits at position
+// c ^ (r mod chunks-per-row), and chunk c of row d of a transposed block at
+// c ^ (d mod 8), so the operand reads of a wave hit distinct banks.
+template <int D>
+struct DkdvLds {
+  static constexpr int kRow = kQB * D;        // elements of a row-major block
+  static constexpr int kBuf = 4 * kRow + 2 * kQB * 2;   // 4 blocks + LSE and D (fp32), in uint16 units
+};
+
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NS = D / 16, ND = D / 32;
-  constexpr int RS = D + 8;            // row stride of Q / dO blocks (elements)
-  constexpr int TS = kQB + 8;          // row stride of Q^T / dO^T blocks
-  constexpr int RCH = kQB * D / 8 / kThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kQB * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds[kQB * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t dot_lds[D * TS];
-  __shared__ __attribute__((aligned(16))) float lse_lds[kQB];
-  __shared__ __attribute__((aligned(16))) float dd_lds[kQB];
+  constexpr int CH = D / 8;                        // 16-byte chunks per row-major row
+  constexpr int RJ = kQB * CH / 64 / 4;            // DMA instructions per wave, row-major block
+  constexpr int TJ = D * (kQB / 8) / 64 / 4;       // DMA instructions per wave, transposed block
+  constexpr int NDMA = 2 * RJ + 2 * TJ + 1;        // per wave and step (4 blocks + LSE/D)
+  static_assert(RJ * 256 == kQB * CH && TJ * 256 == D * kQB / 8, "copies split evenly over 4 waves");
+  constexpr int ROW = DkdvLds<D>::kRow;
+  __shared__ __attribute__((aligned(16))) uint16_t buf0[DkdvLds<D>::kBuf];
+  __shared__ __attribute__((aligned(16))) uint16_t buf1[DkdvLds<D>::kBuf];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int half = lane >> 5, col = lane & 31;
   const int w = blockIdx.x;
   const uint64_t t_start = wall_clock64();
   const int beg = a.cu_off[w], end = a.cu_off[w + 1];
   const float c = a.scale_log2;
+  const uint32_t bl0 = lds_addr(buf0), bl1 = lds_addr(buf1);
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -127,6 +145,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
     const int qstart = row0 & ~(kQB - 1);
     const int qend = segment_end(a.cu, a.n_samples, row0 + nrows - 1);
     const int nqb = (qend - qstart + kQB - 1) / kQB;
+    const int nsteps = nqb * item.nheads;
 
     f32x16 dkacc[ND], dvacc[ND];
 #pragma unroll
@@ -135,50 +154,68 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
       dvacc[dt] = zero16();
     }
 
-    for (int hh = 0; hh < item.nheads; ++hh) {
-      const int h = item.head0 + hh;
-      for (int qb = 0; qb < nqb; ++qb) {
-        const int q0 = qstart + qb * kQB;
-        __syncthreads();
+    // Queue the copies of step i (head head0 + i / nqb, query block i % nqb).
+    auto issue = [&](int i, uint32_t dst) {
+      const int h = item.head0 + i / nqb;
+      const int q0 = qstart + (i % nqb) * kQB;
 #pragma unroll
-        for (int j = 0; j < RCH; ++j) {
-          const int cidx = tid + kThreads * j;
-          const int r = cidx / (D / 8), cc = cidx % (D / 8);
-          const int qq = q0 + r;
-          const int64_t g = ((int64_t)qq * a.h_q + h) * D + cc * 8;
-          const bool ok = qq < a.L;
-          *reinterpret_cast<u32x4 *>(q_lds + r * RS + cc * 8) =
-              ok ? *reinterpret_cast<const u32x4 *>(a.q + g) : zero_u32x4();
-          *reinterpret_cast<u32x4 *>(do_lds + r * RS + cc * 8) =
-              ok ? *reinterpret_cast<const u32x4 *>(a.dout + g) : zero_u32x4();
-          const int d = cidx / (kQB / 8), tc = cidx % (kQB / 8);
-          const int64_t gt = ((int64_t)h * D + d) * a.Lp + q0 + tc * 8;
-          *reinterpret_cast<u32x4 *>(qt_lds + d * TS + tc * 8) = *reinterpret_cast<const u32x4 *>(a.qt + gt);
-          *reinterpret_cast<u32x4 *>(dot_lds + d * TS + tc * 8) = *reinterpret_cast<const u32x4 *>(a.dot + gt);
-        }
-        if (tid < kQB) {
-          const int qq = q0 + tid;
-          const bool ok = qq < a.L;
-          lse_lds[tid] = ok ? a.lse[(int64_t)h * a.L + qq] * kLog2e : 0.0f;
-          dd_lds[tid] = ok ? a.dvec[(int64_t)h * a.L + qq] : 0.0f;
-        }
-        __syncthreads();
+      for (int j = 0; j < RJ; ++j) {
+        const int slot = (wave * RJ + j) * 64 + lane;
+        const int r = slot / CH, cc = (slot % CH) ^ (r & (CH - 1));
+        const int64_t g = ((int64_t)min(q0 + r, a.L - 1) * a.h_q + h) * D + cc * 8;   // rows past L are masked
+        const uint32_t off = (wave * RJ + j) * 1024;
+        lds_dma16(a.q + g, dst + off);
+        lds_dma16(a.dout + g, dst + 2 * ROW + off);     // byte offsets: a block is 2 * ROW bytes
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int slot = (wave * TJ + j) * 64 + lane;
+        const int d = slot / (kQB / 8), cc = (slot % (kQB / 8)) ^ (d & 7);
+        const int64_t g = ((int64_t)h * D + d) * a.Lp + q0 + cc * 8;
+        const uint32_t off = (wave * TJ + j) * 1024;
+        lds_dma16(a.qt + g, dst + 4 * ROW + off);
+        lds_dma16(a.dot + g, dst + 6 * ROW + off);
+      }
+      // LSE then D of the block's queries: lanes 0..31 of each wave copy 32 values.
+      if (lane < 32) {
+        const int e = wave * 32 + lane;             // 0..127
+        const int qq = min(q0 + (e & (kQB - 1)), a.L - 1);
+        const float *src = (e < kQB ? a.lse2 : a.dvec) + (int64_t)h * a.L + qq;
+        lds_dma4(src, dst + 8 * ROW + wave * 128);
+      }
+    };
 
-        const bool touch = kok && (q0 + kQB - 1 >= key) && (q0 < kend);
-        const bool full = !kok || ((key <= q0) && (q0 + kQB - 1 < kend));
-        if (!wave_any(touch)) continue;
+    // One step: wait for its copies (the next step's are queued first), compute.
+    auto step = [&](int i, auto bufc) {
+      constexpr int BUF = decltype(bufc)::value;
+      const uint16_t *bq = BUF == 0 ? buf0 : buf1;
+      if (i + 1 < nsteps) {
+        issue(i + 1, BUF == 0 ? bl1 : bl0);
+        wait_vmem<NDMA>();
+      } else {
+        wait_vmem<0>();
+      }
+      block_barrier();
+      const int q0 = qstart + (i % nqb) * kQB;
+      const bool touch = kok && (q0 + kQB - 1 >= key) && (q0 < kend);
+      const bool full = !kok || ((key <= q0) && (q0 + kQB - 1 < kend));
+      if (wave_any(touch)) {
         const bool masked = wave_any(!full);
+        const uint16_t *q_l = bq, *do_l = bq + ROW, *qt_l = bq + 2 * ROW, *dot_l = bq + 3 * ROW;
+        const float *lse_l = reinterpret_cast<const float *>(bq + 4 * ROW);   // LSE * log2(e)
+        const float *dd_l = lse_l + kQB;
 
         f32x16 sacc[2], pacc[2];   // per 32-query tile: S and dP, C layout (lane = key)
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           sacc[qt] = zero16();
           pacc[qt] = zero16();
-          const int arow = (qt * 32 + sigma_row(col)) * RS + 8 * half;
+          const int row = qt * 32 + sigma_row(col);
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
-            const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4 *>(q_lds + arow + 16 * s));
-            const bf16x8 da = as_bf16x8(*reinterpret_cast<const u32x4 *>(do_lds + arow + 16 * s));
+            const int off = row * D + (((2 * s + half) ^ (row & (CH - 1))) * 8);
+            const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4 *>(q_l + off));
+            const bf16x8 da = as_bf16x8(*reinterpret_cast<const u32x4 *>(do_l + off));
             sacc[qt] = mfma32x32x16(qa, kop[s], sacc[qt]);
             pacc[qt] = mfma32x32x16(da, vop[s], pacc[qt]);
           }
@@ -189,28 +226,28 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const int ql = qt * 32 + 16 * t + 8 * half;   // first of 8 consecutive queries
-            const float4 l0 = *reinterpret_cast<const float4 *>(lse_lds + ql);
-            const float4 l1 = *reinterpret_cast<const float4 *>(lse_lds + ql + 4);
-            const float4 d0 = *reinterpret_cast<const float4 *>(dd_lds + ql);
-            const float4 d1 = *reinterpret_cast<const float4 *>(dd_lds + ql + 4);
+            const float4 l0 = *reinterpret_cast<const float4 *>(lse_l + ql);
+            const float4 l1 = *reinterpret_cast<const float4 *>(lse_l + ql + 4);
+            const float4 d0 = *reinterpret_cast<const float4 *>(dd_l + ql);
+            const float4 d1 = *reinterpret_cast<const float4 *>(dd_l + ql + 4);
             const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
             const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
             float p[8], ds[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int r = 8 * t + i;
-              float pv = exp2_fast(fmaf(sacc[qt][r], c, -lv[i]));
+            for (int e = 0; e < 8; ++e) {
+              const int r = 8 * t + e;
+              float pv = exp2_fast(fmaf(sacc[qt][r], c, -lv[e]));
               if (masked) {
-                const int qq = q0 + ql + i;
+                const int qq = q0 + ql + e;
                 if (!(kok && key <= qq && qq < kend)) pv = 0.0f;
               }
-              p[i] = pv;
-              ds[i] = pv * (pacc[qt][r] - dv8[i]);
+              p[e] = pv;
+              ds[e] = pv * (pacc[qt][r] - dv8[e]);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              pw[qt][t][i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
-              dsw[qt][t][i] = pack_bf16x2(ds[2 * i], ds[2 * i + 1]);
+            for (int e = 0; e < 4; ++e) {
+              pw[qt][t][e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+              dsw[qt][t][e] = pack_bf16x2(ds[2 * e], ds[2 * e + 1]);
             }
           }
 #pragma unroll
@@ -219,13 +256,23 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
           for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-              const int off = (dt * 32 + col) * TS + qt * 32 + 16 * t + 8 * half;
-              const bf16x8 oa = as_bf16x8(*reinterpret_cast<const u32x4 *>(dot_lds + off));
-              const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4 *>(qt_lds + off));
+              const int d = dt * 32 + col;
+              const int off = d * kQB + (((qt * 4 + 2 * t + half) ^ (d & 7)) * 8);
+              const bf16x8 oa = as_bf16x8(*reinterpret_cast<const u32x4 *>(dot_l + off));
+              const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4 *>(qt_l + off));
               dvacc[dt] = mfma32x32x16(oa, as_bf16x8(pw[qt][t]), dvacc[dt]);
               dkacc[dt] = mfma32x32x16(qa, as_bf16x8(dsw[qt][t]), dkacc[dt]);
             }
       }
+      wait_lds();                   // every read of this buffer is done before it is refilled
+      block_barrier();
+    };
+
+    wait_vmem<0>();                 // nothing else in flight: the counts in `step` are exact
+    if (nsteps > 0) issue(0, bl0);
+    for (int i = 0; i < nsteps; i += 2) {
+      step(i, std::integral_constant<int, 0>{});
+      if (i + 1 < nsteps) step(i + 1, std::integral_constant<int, 1>{});
     }
 
     if (kok) {
@@ -250,153 +297,160 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------- dQ pass
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
-void attn_bwd_dq_kernel(BwdArgs a) {
-  constexpr int NS = D / 16, ND = D / 32;
-  constexpr int RS = D + 8;            // K / V block row stride
-  constexpr int TS = kKB + 8;          // K^T block row stride
-  constexpr int RCH = kKB * D / 8 / kThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKB * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kKB * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[D * TS];
+// Eight waves of 32 query positions each cover the 256 query columns of a
+// forward work item (two waves per SIMD).  Per key block of kKB keys, LDS
+// holds K and V (row-major, A operands of S^T and dP^T) and K^T (A operand of
+// dQ^T), double-buffered like the forward; all query heads of the item's KV
+// head read the same copy.
+constexpr int kDqWaves = 8;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(kDqWaves * 64, kDqWaves * 64), amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_kernel(BwdArgs a) {
+  constexpr int NW = kDqWaves;
+  constexpr int NS = D / 16, ND = D / 32;
+  constexpr int CH = D / 8;
+  constexpr int RJ = kKB * CH / 64 / NW;           // DMA instructions per wave, K or V block
+  constexpr int TJ = D * (kKB / 8) / 64 / NW;      // DMA instructions per wave, K^T block
+  constexpr int NDMA = 2 * RJ + TJ;
+  static_assert(RJ * NW * 64 == kKB * CH && TJ * NW * 64 == D * kKB / 8, "copies split evenly");
+  constexpr int BLK = kKB * D;                     // elements of one block
+  __shared__ __attribute__((aligned(16))) uint16_t buf0[3 * BLK];
+  __shared__ __attribute__((aligned(16))) uint16_t buf1[3 * BLK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int half = lane >> 5, col = lane & 31;
   const int w = blockIdx.x;
   const uint64_t t_start = wall_clock64();
   const int beg = a.cu_off[w], end = a.cu_off[w + 1];
   const float c = a.scale_log2;
+  const uint32_t bl0 = lds_addr(buf0), bl1 = lds_addr(buf1);
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
     const int row0 = item.row0, nrows = item.nrows, kvh = item.kv_head, nh = item.nheads;
     const int head = item.head0 + (wave % nh);
     const int sub = wave / nh;
-    const int wrow0 = row0 + sub * 64;
-    const int wrows = min(64, nrows - sub * 64);
-
-    int qpos[2], qss[2];
-    bool qok[2];
-    float lse2[2], dd[2];
-    bf16x8 qop[2][NS], dop[2][NS];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const int r = qt * 32 + col;
-      qok[qt] = r < wrows;
-      qpos[qt] = wrow0 + r;
-      qss[qt] = qok[qt] ? segment_start(a.cu, a.n_samples, qpos[qt]) : 0;
-      lse2[qt] = qok[qt] ? a.lse[(int64_t)head * a.L + qpos[qt]] * kLog2e : 0.0f;
-      dd[qt] = qok[qt] ? a.dvec[(int64_t)head * a.L + qpos[qt]] : 0.0f;
-      const int64_t base = ((int64_t)qpos[qt] * a.h_q + head) * D + 8 * half;
+    const int r = sub * 32 + col;
+    const bool qok = r < nrows;
+    const int qpos = row0 + r;
+    const int qss = qok ? segment_start(a.cu, a.n_samples, qpos) : 0;
+    const float lse2 = qok ? a.lse2[(int64_t)head * a.L + qpos] : 0.0f;
+    const float dd = qok ? a.dvec[(int64_t)head * a.L + qpos] : 0.0f;
+    bf16x8 qop[NS], dop[NS];
+    {
+      const int64_t base = ((int64_t)qpos * a.h_q + head) * D + 8 * half;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        qop[qt][s] = as_bf16x8(qok[qt] ? *reinterpret_cast<const u32x4 *>(a.q + base + 16 * s) : zero_u32x4());
-        dop[qt][s] = as_bf16x8(qok[qt] ? *reinterpret_cast<const u32x4 *>(a.dout + base + 16 * s) : zero_u32x4());
+        qop[s] = as_bf16x8(qok ? *reinterpret_cast<const u32x4 *>(a.q + base + 16 * s) : zero_u32x4());
+        dop[s] = as_bf16x8(qok ? *reinterpret_cast<const u32x4 *>(a.dout + base + 16 * s) : zero_u32x4());
       }
     }
     const int kstart = segment_start(a.cu, a.n_samples, row0) & ~(kKB - 1);
     const int kend = row0 + nrows;
     const int nkb = (kend - kstart + kKB - 1) / kKB;
 
-    f32x16 dqacc[2][ND];
+    f32x16 dqacc[ND];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) dqacc[qt][dt] = zero16();
+    for (int dt = 0; dt < ND; ++dt) dqacc[dt] = zero16();
 
-    for (int b = 0; b < nkb; ++b) {
+    auto issue = [&](int k0, uint32_t dst) {
+#pragma unroll
+      for (int j = 0; j < RJ; ++j) {
+        const int slot = (wave * RJ + j) * 64 + lane;
+        const int rr = slot / CH, cc = (slot % CH) ^ (rr & (CH - 1));
+        const int64_t g = ((int64_t)min(k0 + rr, a.L - 1) * a.h_kv + kvh) * D + cc * 8;   // rows past L are masked
+        const uint32_t off = (wave * RJ + j) * 1024;
+        lds_dma16(a.k + g, dst + off);
+        lds_dma16(a.v + g, dst + 2 * BLK + off);     // byte offsets: a block is 2 * BLK bytes
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int slot = (wave * TJ + j) * 64 + lane;
+        const int d = slot / (kKB / 8), cc = (slot % (kKB / 8)) ^ (d & 7);
+        lds_dma16(a.kt + ((int64_t)kvh * D + d) * a.Lp + k0 + cc * 8, dst + 4 * BLK + (wave * TJ + j) * 1024);
+      }
+    };
+
+    auto block = [&](int b, auto bufc) {
+      constexpr int BUF = decltype(bufc)::value;
+      const uint16_t *bk = BUF == 0 ? buf0 : buf1;
       const int k0 = kstart + b * kKB;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < RCH; ++j) {
-        const int cidx = tid + kThreads * j;
-        const int r = cidx / (D / 8), cc = cidx % (D / 8);
-        const int kk = k0 + r;
-        const int64_t g = ((int64_t)kk * a.h_kv + kvh) * D + cc * 8;
-        const bool ok = kk < a.L;
-        *reinterpret_cast<u32x4 *>(k_lds + r * RS + cc * 8) =
-            ok ? *reinterpret_cast<const u32x4 *>(a.k + g) : zero_u32x4();
-        *reinterpret_cast<u32x4 *>(v_lds + r * RS + cc * 8) =
-            ok ? *reinterpret_cast<const u32x4 *>(a.v + g) : zero_u32x4();
-        const int d = cidx / (kKB / 8), tc = cidx % (kKB / 8);
-        *reinterpret_cast<u32x4 *>(kt_lds + d * TS + tc * 8) =
-            *reinterpret_cast<const u32x4 *>(a.kt + ((int64_t)kvh * D + d) * a.Lp + k0 + tc * 8);
+      if (b + 1 < nkb) {
+        issue(k0 + kKB, BUF == 0 ? bl1 : bl0);
+        wait_vmem<NDMA>();
+      } else {
+        wait_vmem<0>();
       }
-      __syncthreads();
-
-      bool touch = false, partial = false;
+      block_barrier();
+      const bool touch = qok && (k0 <= qpos) && (k0 + kKB - 1 >= qss);
+      const bool partial = qok && !((k0 >= qss) && (k0 + kKB - 1 <= qpos));
+      if (wave_any(touch)) {
+        const bool masked = wave_any(partial);
+        const uint16_t *k_l = bk, *v_l = bk + BLK, *kt_l = bk + 2 * BLK;
+        const int lo = qok ? qss : 1, hi = qok ? qpos : 0;
+        // One 32-key tile at a time keeps S^T, dP^T and dS^T of a single tile live.
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        if (qok[qt]) {
-          touch |= (k0 <= qpos[qt]) && (k0 + kKB - 1 >= qss[qt]);
-          partial |= !((k0 >= qss[qt]) && (k0 + kKB - 1 <= qpos[qt]));
-        }
-      }
-      if (!wave_any(touch)) continue;
-      const bool masked = wave_any(partial);
-
-      const int arow = sigma_row(col) * RS + 8 * half;
-      f32x16 sacc[2], pacc[2];   // S^T and dP^T per query tile (lane = query)
+        for (int kt = 0; kt < kKB / 32; ++kt) {
+          f32x16 sacc = zero16(), pacc = zero16();   // S^T and dP^T (lane = query)
+          const int row = kt * 32 + sigma_row(col);
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        sacc[qt] = zero16();
-        pacc[qt] = zero16();
-      }
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(k_lds + arow + 16 * s));
-        const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(v_lds + arow + 16 * s));
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          sacc[qt] = mfma32x32x16(ka, qop[qt][s], sacc[qt]);
-          pacc[qt] = mfma32x32x16(va, dop[qt][s], pacc[qt]);
-        }
-      }
-      u32x4 dsw[2][2];   // [query tile][16-key slab]
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const int lo = qok[qt] ? qss[qt] : 1, hi = qok[qt] ? qpos[qt] : 0;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float ds2[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int r = 8 * t + 2 * i + e;
-              float pv = exp2_fast(fmaf(sacc[qt][r], c, -lse2[qt]));
-              if (masked) {
-                const int kk = k0 + 16 * t + 8 * half + 2 * i + e;
-                if (kk < lo || kk > hi) pv = 0.0f;
-              }
-              ds2[e] = pv * (pacc[qt][r] - dd[qt]);
-            }
-            dsw[qt][t][i] = pack_bf16x2(ds2[0], ds2[1]);
+          for (int s = 0; s < NS; ++s) {
+            const int off = row * D + (((2 * s + half) ^ (row & (CH - 1))) * 8);
+            const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(k_l + off));
+            const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(v_l + off));
+            sacc = mfma32x32x16(ka, qop[s], sacc);
+            pacc = mfma32x32x16(va, dop[s], pacc);
           }
-      }
+          u32x4 dsw[2];   // [16-key slab]: bf16 dS^T operands
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt)
+          for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-              kt_lds + (dt * 32 + col) * TS + 16 * t + 8 * half));
+            for (int i = 0; i < 4; ++i) {
+              float ds2[2];
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt) dqacc[qt][dt] = mfma32x32x16(ka, as_bf16x8(dsw[qt][t]), dqacc[qt][dt]);
+              for (int e = 0; e < 2; ++e) {
+                const int rr = 8 * t + 2 * i + e;
+                float pv = exp2_fast(fmaf(sacc[rr], c, -lse2));
+                if (masked) {
+                  const int kk = k0 + kt * 32 + 16 * t + 8 * half + 2 * i + e;
+                  if (kk < lo || kk > hi) pv = 0.0f;
+                }
+                ds2[e] = pv * (pacc[rr] - dd);
+              }
+              dsw[t][i] = pack_bf16x2(ds2[0], ds2[1]);
+            }
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int d = dt * 32 + col;
+              const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+                  kt_l + d * kKB + (((kt * 4 + 2 * t + half) ^ (d & 7)) * 8)));
+              dqacc[dt] = mfma32x32x16(ka, as_bf16x8(dsw[t]), dqacc[dt]);
+            }
         }
+      }
+      wait_lds();
+      block_barrier();
+    };
+
+    wait_vmem<0>();
+    if (nkb > 0) issue(kstart, bl0);
+    for (int b = 0; b < nkb; b += 2) {
+      block(b, std::integral_constant<int, 0>{});
+      if (b + 1 < nkb) block(b + 1, std::integral_constant<int, 1>{});
     }
 
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      if (!qok[qt]) continue;
-      uint16_t *op = a.dq + ((int64_t)qpos[qt] * a.h_q + head) * D;
+    if (qok) {
+      uint16_t *op = a.dq + ((int64_t)qpos * a.h_q + head) * D;
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
           u32x2 pk;
-          pk[0] = pack_bf16x2(dqacc[qt][dt][4 * cc] * a.scale, dqacc[qt][dt][4 * cc + 1] * a.scale);
-          pk[1] = pack_bf16x2(dqacc[qt][dt][4 * cc + 2] * a.scale, dqacc[qt][dt][4 * cc + 3] * a.scale);
+          pk[0] = pack_bf16x2(dqacc[dt][4 * cc] * a.scale, dqacc[dt][4 * cc + 1] * a.scale);
+          pk[1] = pack_bf16x2(dqacc[dt][4 * cc + 2] * a.scale, dqacc[dt][4 * cc + 3] * a.scale);
           *reinterpret_cast<u32x2 *>(op + dt * 32 + 8 * cc + 4 * half) = pk;
         }
     }
@@ -406,7 +460,7 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 struct BwdLayout {
-  size_t qt, dot, kt, dvec, total;
+  size_t qt, dot, kt, dvec, lse2, total;
 };
 
 BwdLayout bwd_layout(const libra_plan_params &p) {
@@ -415,7 +469,8 @@ BwdLayout bwd_layout(const libra_plan_params &p) {
   l.dot = l.qt + transposed_bytes(p.h_q, p.head_dim, p.total_tokens);
   l.kt = l.dot + transposed_bytes(p.h_q, p.head_dim, p.total_tokens);
   l.dvec = l.kt + transposed_bytes(p.h_kv, p.head_dim, p.total_tokens);
-  l.total = l.dvec + (size_t)round_up64((int64_t)p.h_q * p.total_tokens * 4, 256);
+  l.lse2 = l.dvec + (size_t)round_up64((int64_t)p.h_q * p.total_tokens * 4, 256);
+  l.total = l.lse2 + (size_t)round_up64((int64_t)p.h_q * p.total_tokens * 4, 256);
   return l;
 }
 
@@ -443,9 +498,10 @@ libra_status check_workspace(const libra_plan_info &h, const void *ws, size_t by
 }
 
 libra_status check_prepare(const libra_plan_info &h, const void *q, const void *k, const void *o,
-                           const void *dout, const void *ws, size_t bytes) {
+                           const void *dout, const float *lse, const void *ws, size_t bytes) {
   if (h.params.total_tokens == 0) return LIBRA_OK;
-  if (any_null({q, k, o, dout}) || any_misaligned({q, k, o, dout}, 16)) return LIBRA_EINVAL;
+  if (any_null({q, k, o, dout, lse}) || any_misaligned({q, k, o, dout}, 16) || misaligned(lse, 4))
+    return LIBRA_EINVAL;
   return check_workspace(h, ws, bytes);
 }
 
@@ -478,6 +534,7 @@ BwdArgs make_args(const libra_plan_info &h, const void *q, const void *k, const 
   a.kt = reinterpret_cast<const uint16_t *>(w + lay.kt);
   a.lse = lse;
   a.dvec = reinterpret_cast<const float *>(w + lay.dvec);
+  a.lse2 = reinterpret_cast<const float *>(w + lay.lse2);
   a.cu = cu_dev;
   a.n_samples = p.num_samples;
   a.L = p.total_tokens;
@@ -490,7 +547,7 @@ BwdArgs make_args(const libra_plan_info &h, const void *q, const void *k, const 
 }
 
 libra_status launch_prepare(const libra_plan_info &h, const void *q, const void *k, const void *o,
-                            const void *dout, void *ws, void *stream) {
+                            const void *dout, const float *lse, void *ws, void *stream) {
   const libra_plan_params &p = h.params;
   const BwdLayout lay = bwd_layout(p);
   char *w = static_cast<char *>(ws);
@@ -503,13 +560,14 @@ libra_status launch_prepare(const libra_plan_info &h, const void *q, const void 
   const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
   hipStream_t s = static_cast<hipStream_t>(stream);
   float *dvec = reinterpret_cast<float *>(w + lay.dvec);
+  float *lse2 = reinterpret_cast<float *>(w + lay.lse2);
   clear_hip_error();
   if (p.head_dim == 128)
     hipLaunchKernelGGL(rowdot_kernel<128>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t *>(o),
-                       static_cast<const uint16_t *>(dout), dvec, p.total_tokens, p.h_q);
+                       static_cast<const uint16_t *>(dout), lse, dvec, lse2, p.total_tokens, p.h_q);
   else
     hipLaunchKernelGGL(rowdot_kernel<64>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t *>(o),
-                       static_cast<const uint16_t *>(dout), dvec, p.total_tokens, p.h_q);
+                       static_cast<const uint16_t *>(dout), lse, dvec, lse2, p.total_tokens, p.h_q);
   return launch_status();
 }
 
@@ -540,9 +598,9 @@ libra_status launch_dq(const libra_plan_info &h, BwdArgs a, const void *plan_dev
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_hip_error();
   if (h.params.head_dim == 128)
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(h.num_cus), dim3(kDqWaves * 64), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(h.num_cus), dim3(kDqWaves * 64), 0, s, a);
   return launch_status();
 }
 
@@ -559,13 +617,13 @@ extern "C" libra_status libra_attn_bwd_workspace(const void *plan, size_t *bytes
 }
 
 extern "C" libra_status libra_attn_bwd_prepare(const void *plan, const void *q, const void *k,
-                                               const void *o, const void *dout, void *workspace,
-                                               size_t workspace_bytes, void *stream) {
+                                               const void *o, const void *dout, const float *lse,
+                                               void *workspace, size_t workspace_bytes, void *stream) {
   libra_plan_info h;
   libra_status st = check_header(plan, &h);
-  if (st == LIBRA_OK) st = check_prepare(h, q, k, o, dout, workspace, workspace_bytes);
+  if (st == LIBRA_OK) st = check_prepare(h, q, k, o, dout, lse, workspace, workspace_bytes);
   if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
-  return launch_prepare(h, q, k, o, dout, workspace, stream);
+  return launch_prepare(h, q, k, o, dout, lse, workspace, stream);
 }
 
 extern "C" libra_status libra_attn_bwd_dkdv(const void *plan, const void *plan_dev, const void *q,
@@ -606,12 +664,12 @@ extern "C" libra_status libra_attn_bwd(const void *plan, const void *plan_dev, c
                                        size_t workspace_bytes, libra_cu_record *records, void *stream) {
   libra_plan_info h;
   libra_status st = check_header(plan, &h);
-  if (st == LIBRA_OK) st = check_prepare(h, q, k, o, dout, workspace, workspace_bytes);
+  if (st == LIBRA_OK) st = check_prepare(h, q, k, o, dout, lse, workspace, workspace_bytes);
   if (st == LIBRA_OK)
     st = check_pass(h, plan_dev, {q, k, v, dout, dq, dk, dv}, lse, cu_dev, softmax_scale, workspace,
                     workspace_bytes, records);
   if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
-  if ((st = launch_prepare(h, q, k, o, dout, workspace, stream)) != LIBRA_OK) return st;
+  if ((st = launch_prepare(h, q, k, o, dout, lse, workspace, stream)) != LIBRA_OK) return st;
   const BwdArgs a = make_args(h, q, k, v, dout, lse, cu_dev, workspace, softmax_scale);
   if ((st = launch_dkdv(h, a, plan_dev, dk, dv, records, stream)) != LIBRA_OK) return st;
   return launch_dq(h, a, plan_dev, dq, records ? records + h.num_cus : nullptr, stream);

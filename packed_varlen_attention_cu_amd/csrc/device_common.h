@@ -109,6 +109,12 @@ __device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gsrc) : "memory", "m0");
 }
 
+// The same for 4 bytes per lane: lane i writes lds_base + 4 * i.
+__device__ __forceinline__ void lds_dma4(const void *gsrc, uint32_t lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gsrc) : "memory", "m0");
+}
+
 // Byte address of a __shared__ object in the LDS aperture.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;

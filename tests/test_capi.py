@@ -225,9 +225,11 @@ def test_phase_entry_points_validate(small_plan):
     assert L_.libra_attn_fwd_prepare(h, FAKE, FAKE, fws - 1, None) == lib.LIBRA_ESIZE
     assert L_.libra_attn_fwd_main(h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, 0, None, None) == lib.LIBRA_ESIZE
     assert L_.libra_attn_fwd_main(h, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, fws, None, None) == lib.LIBRA_EINVAL
-    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, None, FAKE, FAKE, bws, None) == lib.LIBRA_EINVAL
-    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE, FAKE + 16, bws, None) == lib.LIBRA_EINVAL
-    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE, FAKE, bws - 1, None) == lib.LIBRA_ESIZE
+    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, None, FAKE, FAKE, FAKE, bws, None) == lib.LIBRA_EINVAL
+    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE, None, FAKE, bws, None) == lib.LIBRA_EINVAL
+    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE, bws, None) == lib.LIBRA_EINVAL
+    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, bws, None) == lib.LIBRA_EINVAL
+    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, bws - 1, None) == lib.LIBRA_ESIZE
     dkdv = [h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, bws, None, None]
     for i in (2, 3, 4, 5, 6, 7, 8, 9):           # q k v dout lse cu dk dv
         args = list(dkdv)
@@ -260,8 +262,8 @@ def test_bwd_validation(small_plan):
 def test_workspace_sizes(small_plan):
     Lp = 128
     assert lib.libra_attn_fwd_workspace(small_plan.host) == 2 * 128 * Lp * 2
-    # Q^T and dO^T (h_q), K^T (h_kv), D (fp32 [h_q][L])
-    assert lib.libra_attn_bwd_workspace(small_plan.host) == 2 * (4 * 128 * Lp * 2) + 2 * 128 * Lp * 2 + 2048
+    # Q^T and dO^T (h_q), K^T (h_kv), D and LSE * log2(e) (fp32 [h_q][L] each)
+    assert lib.libra_attn_bwd_workspace(small_plan.host) == 2 * (4 * 128 * Lp * 2) + 2 * 128 * Lp * 2 + 2 * 2048
 
 
 def test_status_strings():

@@ -39,7 +39,7 @@ def test_phases_match_one_call_entry_points():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     lib.libra_attn_fwd_prepare(plan.host, v, wf, fws, sh)
     lib.libra_attn_fwd_main(plan.host, plan_dev, q, k, cu_dev, o2, l2, scale, wf, fws, rec[:ncu * 32], sh)
-    lib.libra_attn_bwd_prepare(plan.host, q, k, o2, do, wb, bws, sh)
+    lib.libra_attn_bwd_prepare(plan.host, q, k, o2, do, l2, wb, bws, sh)
     lib.libra_attn_bwd_dkdv(plan.host, plan_dev, q, k, v, do, l2, cu_dev, dk, dv, scale, wb, bws,
                             rec[ncu * 32:2 * ncu * 32], sh)
     lib.libra_attn_bwd_dq(plan.host, plan_dev, q, k, v, do, l2, cu_dev, dq, scale, wb, bws,
