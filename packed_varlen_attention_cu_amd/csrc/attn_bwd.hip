@@ -111,7 +111,6 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int CH = D / 8;                        // 16-byte chunks per row-major row
   constexpr int RJ = kQB * CH / 64 / 4;            // DMA instructions per wave, row-major block
   constexpr int TJ = D * (kQB / 8) / 64 / 4;       // DMA instructions per wave, transposed block
-  constexpr int NDMA = 2 * RJ + 2 * TJ + 1;        // per wave and step (4 blocks + LSE/D)
   static_assert(RJ * 256 == kQB * CH && TJ * 256 == D * kQB / 8, "copies split evenly over 4 waves");
   constexpr int ROW = DkdvLds<D>::kRow;
   __shared__ __attribute__((aligned(16))) uint16_t buf0[DkdvLds<D>::kBuf];
@@ -185,17 +184,14 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
       }
     };
 
-    // One step: wait for its copies (the next step's are queued first), compute.
+    // One step: once every wave's copies for it have landed and its reads of
+    // the other buffer are done (one barrier), queue step i + 1 there and compute.
     auto step = [&](int i, auto bufc) {
       constexpr int BUF = decltype(bufc)::value;
       const uint16_t *bq = BUF == 0 ? buf0 : buf1;
-      if (i + 1 < nsteps) {
-        issue(i + 1, BUF == 0 ? bl1 : bl0);
-        wait_vmem<NDMA>();
-      } else {
-        wait_vmem<0>();
-      }
+      wait_vmem_lds();
       block_barrier();
+      if (i + 1 < nsteps) issue(i + 1, BUF == 0 ? bl1 : bl0);
       const int q0 = qstart + (i % nqb) * kQB;
       const bool touch = kok && (q0 + kQB - 1 >= key) && (q0 < kend);
       const bool full = !kok || ((key <= q0) && (q0 + kQB - 1 < kend));
@@ -220,6 +216,15 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
             pacc[qt] = mfma32x32x16(da, vop[s], pacc[qt]);
           }
         }
+        if (masked) {               // rare: blocks on a sample start or the diagonal
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int qq = q0 + qt * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
+              if (!(kok && key <= qq && qq < kend)) sacc[qt][r] = -__builtin_inff();
+            }
+        }
         u32x4 pw[2][2], dsw[2][2];   // [query tile][16-query slab]
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
@@ -236,11 +241,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int r = 8 * t + e;
-              float pv = exp2_fast(fmaf(sacc[qt][r], c, -lv[e]));
-              if (masked) {
-                const int qq = q0 + ql + e;
-                if (!(kok && key <= qq && qq < kend)) pv = 0.0f;
-              }
+              const float pv = exp2_fast(fmaf(sacc[qt][r], c, -lv[e]));   // masked: 2^-inf = 0
               p[e] = pv;
               ds[e] = pv * (pacc[qt][r] - dv8[e]);
             }
@@ -264,11 +265,10 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
               dkacc[dt] = mfma32x32x16(qa, as_bf16x8(dsw[qt][t]), dkacc[dt]);
             }
       }
-      wait_lds();                   // every read of this buffer is done before it is refilled
-      block_barrier();
     };
 
-    wait_vmem<0>();                 // nothing else in flight: the counts in `step` are exact
+    wait_vmem_lds();
+    block_barrier();                // the previous item's reads of buffer 0 are done
     if (nsteps > 0) issue(0, bl0);
     for (int i = 0; i < nsteps; i += 2) {
       step(i, std::integral_constant<int, 0>{});
@@ -312,7 +312,6 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int CH = D / 8;
   constexpr int RJ = kKB * CH / 64 / NW;           // DMA instructions per wave, K or V block
   constexpr int TJ = D * (kKB / 8) / 64 / NW;      // DMA instructions per wave, K^T block
-  constexpr int NDMA = 2 * RJ + TJ;
   static_assert(RJ * NW * 64 == kKB * CH && TJ * NW * 64 == D * kKB / 8, "copies split evenly");
   constexpr int BLK = kKB * D;                     // elements of one block
   __shared__ __attribute__((aligned(16))) uint16_t buf0[3 * BLK];
@@ -376,13 +375,9 @@ void attn_bwd_dq_kernel(BwdArgs a) {
       constexpr int BUF = decltype(bufc)::value;
       const uint16_t *bk = BUF == 0 ? buf0 : buf1;
       const int k0 = kstart + b * kKB;
-      if (b + 1 < nkb) {
-        issue(k0 + kKB, BUF == 0 ? bl1 : bl0);
-        wait_vmem<NDMA>();
-      } else {
-        wait_vmem<0>();
-      }
+      wait_vmem_lds();
       block_barrier();
+      if (b + 1 < nkb) issue(k0 + kKB, BUF == 0 ? bl1 : bl0);
       const bool touch = qok && (k0 <= qpos) && (k0 + kKB - 1 >= qss);
       const bool partial = qok && !((k0 >= qss) && (k0 + kKB - 1 <= qpos));
       if (wave_any(touch)) {
@@ -402,6 +397,13 @@ void attn_bwd_dq_kernel(BwdArgs a) {
             sacc = mfma32x32x16(ka, qop[s], sacc);
             pacc = mfma32x32x16(va, dop[s], pacc);
           }
+          if (masked) {             // rare: blocks on a sample start or the diagonal
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+              const int kk = k0 + kt * 32 + 16 * (rr >> 3) + 8 * half + (rr & 7);
+              if (kk < lo || kk > hi) sacc[rr] = -__builtin_inff();
+            }
+          }
           u32x4 dsw[2];   // [16-key slab]: bf16 dS^T operands
 #pragma unroll
           for (int t = 0; t < 2; ++t)
@@ -411,11 +413,7 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
               for (int e = 0; e < 2; ++e) {
                 const int rr = 8 * t + 2 * i + e;
-                float pv = exp2_fast(fmaf(sacc[rr], c, -lse2));
-                if (masked) {
-                  const int kk = k0 + kt * 32 + 16 * t + 8 * half + 2 * i + e;
-                  if (kk < lo || kk > hi) pv = 0.0f;
-                }
+                const float pv = exp2_fast(fmaf(sacc[rr], c, -lse2));   // masked: 2^-inf = 0
                 ds2[e] = pv * (pacc[rr] - dd);
               }
               dsw[t][i] = pack_bf16x2(ds2[0], ds2[1]);
@@ -431,11 +429,10 @@ void attn_bwd_dq_kernel(BwdArgs a) {
             }
         }
       }
-      wait_lds();
-      block_barrier();
     };
 
-    wait_vmem<0>();
+    wait_vmem_lds();
+    block_barrier();
     if (nkb > 0) issue(kstart, bl0);
     for (int b = 0; b < nkb; b += 2) {
       block(b, std::integral_constant<int, 0>{});

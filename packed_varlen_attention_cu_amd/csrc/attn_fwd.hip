@@ -191,18 +191,16 @@ void attn_fwd_kernel(FwdArgs a) {
       }
     };
 
-    // One key block: wait for its copies (the next block's are queued first),
-    // then compute from buffer BUF.
+    // One key block.  After this wave's copies of block b have landed and its
+    // reads of the other buffer (block b - 1) have completed, one barrier makes
+    // both true for every wave; then block b + 1 is queued into the other
+    // buffer and block b is computed while it flies.
     auto block = [&](int b, auto bufc) {
       constexpr int BUF = decltype(bufc)::value;
       const int k0 = kstart + b * kBN;
-      if (b + 1 < nblk) {
-        issue(k0 + kBN, std::integral_constant<int, BUF ^ 1>{});
-        wait_vmem<KJ + VJ>();       // this block's copies have landed; the next block's fly on
-      } else {
-        wait_vmem<0>();
-      }
+      wait_vmem_lds();
       block_barrier();
+      if (b + 1 < nblk) issue(k0 + kBN, std::integral_constant<int, BUF ^ 1>{});
       const uint16_t *kb = BUF == 0 ? k_lds0 : k_lds1;
       const uint16_t *vb = BUF == 0 ? v_lds0 : v_lds1;
 
@@ -303,11 +301,10 @@ void attn_fwd_kernel(FwdArgs a) {
                 oacc[qt][dt] = mfma32x32x16(va, as_bf16x8(pw[qt][kt][t]), oacc[qt][dt]);
             }
       }
-      wait_lds();                   // every read of this buffer is done before it is refilled
-      block_barrier();
     };
 
-    wait_vmem<0>();                 // nothing else in flight: the counts in `block` are exact
+    wait_vmem_lds();
+    block_barrier();                // the previous item's reads of buffer 0 are done
     if (nblk > 0) issue(kstart, std::integral_constant<int, 0>{});
     for (int b = 0; b < nblk; b += 2) {
       block(b, std::integral_constant<int, 0>{});

@@ -133,6 +133,10 @@ __device__ __forceinline__ void wait_vmem() {
 // Wait until this wave's LDS reads and writes have completed.
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// Both: no vector-memory operation (including LDS-DMA copies) and no LDS
+// access of this wave is outstanding.
+__device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }
+
 // Workgroup barrier that keeps the compiler from moving memory accesses across
 // it but adds no memory-counter waits: the kernels wait explicitly (wait_vmem
 // for their LDS-DMA copies, wait_lds before a buffer is refilled), so copies
