@@ -91,67 +91,81 @@ __device__ __forceinline__ void write_record(const BwdArgs &a, int w, int n, uin
 }
 
 // ----------------------------------------------------------------- dK / dV pass
+// Eight waves, two per SIMD.  The 128 keys of an item are split into four
+// groups of 32; each group has a P wave (waves 0-3: S = Q K^T, P, dV^T +=
+// dO^T P) and a dS wave (waves 4-7: dP = dO V^T, dS = P * (dP - D),
+// dK^T += Q^T dS) on the same SIMD.  The P wave publishes its bf16 P through
+// LDS halfway through each step, so while one wave of a SIMD runs matrix
+// products the other runs its element-wise work.  Only the P wave applies the
+// block-diagonal mask: masked P is 0, hence masked dS is 0 too.
+//
 // Per query block of kQB rows and one head, LDS holds Q and dO (row-major,
-// MFMA A operands of S and dP), Q^T and dO^T (A operands of dK^T and dV^T)
-// and the block's LSE and D values.  Two such buffers alternate: the copies
-// for the next (head, query block) step are queued before the current one is
-// computed.  16-byte chunk c of row r of a row-major block sits at position
-// c ^ (r mod chunks-per-row), and chunk c of row d of a transposed block at
-// c ^ (d mod 8), so the operand reads of a wave hit distinct banks.
+// A operands of S and dP), Q^T and dO^T (A operands of dK^T and dV^T) and the
+// block's LSE * log2(e) and D values.  Two such buffers alternate: after one
+// barrier the copies for the next (head, query block) step are queued into
+// the other buffer, and the current one is computed while they fly.  16-byte
+// chunk c of row r of a row-major block sits at position c ^ (r mod
+// chunks-per-row), and chunk c of row d of a transposed block at c ^ (d mod 8),
+// so the operand reads of a wave hit distinct banks.
+constexpr int kDkdvWaves = 8;
+
 template <int D>
 struct DkdvLds {
   static constexpr int kRow = kQB * D;        // elements of a row-major block
   static constexpr int kBuf = 4 * kRow + 2 * kQB * 2;   // 4 blocks + LSE and D (fp32), in uint16 units
+  static constexpr int kP = 4 * 32 * kQB;     // bf16 P of the four key groups
 };
 
 template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kDkdvWaves * 64, kDkdvWaves * 64), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NW = kDkdvWaves;
   constexpr int NS = D / 16, ND = D / 32;
   constexpr int CH = D / 8;                        // 16-byte chunks per row-major row
-  constexpr int RJ = kQB * CH / 64 / 4;            // DMA instructions per wave, row-major block
-  constexpr int TJ = D * (kQB / 8) / 64 / 4;       // DMA instructions per wave, transposed block
-  static_assert(RJ * 256 == kQB * CH && TJ * 256 == D * kQB / 8, "copies split evenly over 4 waves");
+  constexpr int RJ = kQB * CH / 64 / NW;           // DMA instructions per wave, row-major block
+  constexpr int TJ = D * (kQB / 8) / 64 / NW;      // DMA instructions per wave, transposed block
+  static_assert(RJ * NW * 64 == kQB * CH && TJ * NW * 64 == D * kQB / 8, "copies split evenly");
+  static_assert(2 * kQB <= NW * 16, "LSE and D copies: 16 values per wave");
   constexpr int ROW = DkdvLds<D>::kRow;
   __shared__ __attribute__((aligned(16))) uint16_t buf0[DkdvLds<D>::kBuf];
   __shared__ __attribute__((aligned(16))) uint16_t buf1[DkdvLds<D>::kBuf];
+  __shared__ __attribute__((aligned(16))) uint16_t p_lds[DkdvLds<D>::kP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int half = lane >> 5, col = lane & 31;
+  const bool pwave = wave < 4;                     // wave-uniform role
+  const int kg = wave & 3;                         // key group
   const int w = blockIdx.x;
   const uint64_t t_start = wall_clock64();
   const int beg = a.cu_off[w], end = a.cu_off[w + 1];
   const float c = a.scale_log2;
   const uint32_t bl0 = lds_addr(buf0), bl1 = lds_addr(buf1);
+  u32x4 *p_mine = reinterpret_cast<u32x4 *>(p_lds + kg * 32 * kQB) + lane;   // [4 slabs][64 lanes]
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
     const int row0 = item.row0, nrows = item.nrows, kvh = item.kv_head;
-    const int kloc = wave * 32 + col;
+    const int kloc = kg * 32 + col;
     const bool kok = kloc < nrows;
     const int key = row0 + kloc;
     const int kend = kok ? segment_end(a.cu, a.n_samples, key) : 0;   // queries [key, kend)
 
-    bf16x8 kop[NS], vop[NS];
+    // B operand of this wave's first product: K (P wave) or V (dS wave).
+    bf16x8 bop[NS];
     {
-      const int64_t base = ((int64_t)key * a.h_kv + kvh) * D + 8 * half;
+      const uint16_t *src = (pwave ? a.k : a.v) + ((int64_t)key * a.h_kv + kvh) * D + 8 * half;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        kop[s] = as_bf16x8(kok ? *reinterpret_cast<const u32x4 *>(a.k + base + 16 * s) : zero_u32x4());
-        vop[s] = as_bf16x8(kok ? *reinterpret_cast<const u32x4 *>(a.v + base + 16 * s) : zero_u32x4());
-      }
+      for (int s = 0; s < NS; ++s)
+        bop[s] = as_bf16x8(kok ? *reinterpret_cast<const u32x4 *>(src + 16 * s) : zero_u32x4());
     }
     const int qstart = row0 & ~(kQB - 1);
     const int qend = segment_end(a.cu, a.n_samples, row0 + nrows - 1);
     const int nqb = (qend - qstart + kQB - 1) / kQB;
     const int nsteps = nqb * item.nheads;
 
-    f32x16 dkacc[ND], dvacc[ND];
+    f32x16 acc[ND];   // dV^T (P wave) or dK^T (dS wave), one key column per lane
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      dkacc[dt] = zero16();
-      dvacc[dt] = zero16();
-    }
+    for (int dt = 0; dt < ND; ++dt) acc[dt] = zero16();
 
     // Queue the copies of step i (head head0 + i / nqb, query block i % nqb).
     auto issue = [&](int i, uint32_t dst) {
@@ -175,82 +189,100 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
         lds_dma16(a.qt + g, dst + 4 * ROW + off);
         lds_dma16(a.dot + g, dst + 6 * ROW + off);
       }
-      // LSE then D of the block's queries: lanes 0..31 of each wave copy 32 values.
-      if (lane < 32) {
-        const int e = wave * 32 + lane;             // 0..127
+      // LSE * log2(e) then D of the block's queries: lanes 0..15 of each wave copy 16 values.
+      if (lane < 16) {
+        const int e = wave * 16 + lane;             // 0 .. 2 kQB - 1
         const int qq = min(q0 + (e & (kQB - 1)), a.L - 1);
         const float *src = (e < kQB ? a.lse2 : a.dvec) + (int64_t)h * a.L + qq;
-        lds_dma4(src, dst + 8 * ROW + wave * 128);
+        lds_dma4(src, dst + 8 * ROW + wave * 64);
       }
     };
 
-    // One step: once every wave's copies for it have landed and its reads of
-    // the other buffer are done (one barrier), queue step i + 1 there and compute.
     auto step = [&](int i, auto bufc) {
       constexpr int BUF = decltype(bufc)::value;
       const uint16_t *bq = BUF == 0 ? buf0 : buf1;
-      wait_vmem_lds();
+      wait_vmem_lds();              // own copies of step i landed, own LDS accesses of step i - 1 done
       block_barrier();
       if (i + 1 < nsteps) issue(i + 1, BUF == 0 ? bl1 : bl0);
       const int q0 = qstart + (i % nqb) * kQB;
       const bool touch = kok && (q0 + kQB - 1 >= key) && (q0 < kend);
       const bool full = !kok || ((key <= q0) && (q0 + kQB - 1 < kend));
-      if (wave_any(touch)) {
-        const bool masked = wave_any(!full);
-        const uint16_t *q_l = bq, *do_l = bq + ROW, *qt_l = bq + 2 * ROW, *dot_l = bq + 3 * ROW;
-        const float *lse_l = reinterpret_cast<const float *>(bq + 4 * ROW);   // LSE * log2(e)
-        const float *dd_l = lse_l + kQB;
+      const bool act = wave_any(touch);     // identical for the two waves of a key group
+      const uint16_t *q_l = bq, *do_l = bq + ROW, *qt_l = bq + 2 * ROW, *dot_l = bq + 3 * ROW;
+      const float *lse_l = reinterpret_cast<const float *>(bq + 4 * ROW);
+      const float *dd_l = lse_l + kQB;
 
-        f32x16 sacc[2], pacc[2];   // per 32-query tile: S and dP, C layout (lane = key)
+      // First product: S (P wave, A = Q) or dP (dS wave, A = dO); C layout, lane = key.
+      f32x16 sacc[2];
+      if (act) {
+        const uint16_t *a_l = pwave ? q_l : do_l;
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           sacc[qt] = zero16();
-          pacc[qt] = zero16();
           const int row = qt * 32 + sigma_row(col);
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
-            const int off = row * D + (((2 * s + half) ^ (row & (CH - 1))) * 8);
-            const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4 *>(q_l + off));
-            const bf16x8 da = as_bf16x8(*reinterpret_cast<const u32x4 *>(do_l + off));
-            sacc[qt] = mfma32x32x16(qa, kop[s], sacc[qt]);
-            pacc[qt] = mfma32x32x16(da, vop[s], pacc[qt]);
+            const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+                a_l + row * D + (((2 * s + half) ^ (row & (CH - 1))) * 8)));
+            sacc[qt] = mfma32x32x16(av, bop[s], sacc[qt]);
           }
         }
-        if (masked) {               // rare: blocks on a sample start or the diagonal
+      }
+      u32x4 pw[2][2];   // [query tile][16-query slab]: bf16 P (P wave) or dS (dS wave)
+      if (pwave) {
+        if (act) {
+          if (wave_any(!full)) {      // rare: blocks on a sample start or the diagonal
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int qq = q0 + qt * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
+                if (!(kok && key <= qq && qq < kend)) sacc[qt][r] = -__builtin_inff();
+              }
+          }
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int qq = q0 + qt * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
-              if (!(kok && key <= qq && qq < kend)) sacc[qt][r] = -__builtin_inff();
+            for (int t = 0; t < 2; ++t) {
+              const int ql = qt * 32 + 16 * t + 8 * half;   // first of 8 consecutive queries
+              const float4 l0 = *reinterpret_cast<const float4 *>(lse_l + ql);
+              const float4 l1 = *reinterpret_cast<const float4 *>(lse_l + ql + 4);
+              const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float p0 = exp2_fast(fmaf(sacc[qt][8 * t + 2 * e], c, -lv[2 * e]));   // masked: 0
+                const float p1 = exp2_fast(fmaf(sacc[qt][8 * t + 2 * e + 1], c, -lv[2 * e + 1]));
+                pw[qt][t][e] = pack_bf16x2(p0, p1);
+              }
+              p_mine[(qt * 2 + t) * 64] = pw[qt][t];
             }
         }
-        u32x4 pw[2][2], dsw[2][2];   // [query tile][16-query slab]
+        wait_lds();
+        block_barrier();              // P of every key group is in LDS
+      } else {
+        block_barrier();
+        if (act) {
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+          for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int ql = qt * 32 + 16 * t + 8 * half;   // first of 8 consecutive queries
-            const float4 l0 = *reinterpret_cast<const float4 *>(lse_l + ql);
-            const float4 l1 = *reinterpret_cast<const float4 *>(lse_l + ql + 4);
-            const float4 d0 = *reinterpret_cast<const float4 *>(dd_l + ql);
-            const float4 d1 = *reinterpret_cast<const float4 *>(dd_l + ql + 4);
-            const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-            const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-            float p[8], ds[8];
+            for (int t = 0; t < 2; ++t) {
+              const int ql = qt * 32 + 16 * t + 8 * half;
+              const float4 d0 = *reinterpret_cast<const float4 *>(dd_l + ql);
+              const float4 d1 = *reinterpret_cast<const float4 *>(dd_l + ql + 4);
+              const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+              const u32x4 pv = p_mine[(qt * 2 + t) * 64];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int r = 8 * t + e;
-              const float pv = exp2_fast(fmaf(sacc[qt][r], c, -lv[e]));   // masked: 2^-inf = 0
-              p[e] = pv;
-              ds[e] = pv * (pacc[qt][r] - dv8[e]);
+              for (int e = 0; e < 4; ++e) {
+                const float ds0 = bf16_lo(pv[e]) * (sacc[qt][8 * t + 2 * e] - dv8[2 * e]);
+                const float ds1 = bf16_hi(pv[e]) * (sacc[qt][8 * t + 2 * e + 1] - dv8[2 * e + 1]);
+                pw[qt][t][e] = pack_bf16x2(ds0, ds1);
+              }
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              pw[qt][t][e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
-              dsw[qt][t][e] = pack_bf16x2(ds[2 * e], ds[2 * e + 1]);
-            }
-          }
+        }
+      }
+      // Second product: dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave).
+      if (act) {
+        const uint16_t *t_l = pwave ? dot_l : qt_l;
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -258,17 +290,15 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
               const int d = dt * 32 + col;
-              const int off = d * kQB + (((qt * 4 + 2 * t + half) ^ (d & 7)) * 8);
-              const bf16x8 oa = as_bf16x8(*reinterpret_cast<const u32x4 *>(dot_l + off));
-              const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4 *>(qt_l + off));
-              dvacc[dt] = mfma32x32x16(oa, as_bf16x8(pw[qt][t]), dvacc[dt]);
-              dkacc[dt] = mfma32x32x16(qa, as_bf16x8(dsw[qt][t]), dkacc[dt]);
+              const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+                  t_l + d * kQB + (((qt * 4 + 2 * t + half) ^ (d & 7)) * 8)));
+              acc[dt] = mfma32x32x16(av, as_bf16x8(pw[qt][t]), acc[dt]);
             }
       }
     };
 
     wait_vmem_lds();
-    block_barrier();                // the previous item's reads of buffer 0 are done
+    block_barrier();                // the previous item's reads of buffer 0 and of P are done
     if (nsteps > 0) issue(0, bl0);
     for (int i = 0; i < nsteps; i += 2) {
       step(i, std::integral_constant<int, 0>{});
@@ -276,19 +306,16 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
     }
 
     if (kok) {
-      const int64_t base = ((int64_t)key * a.h_kv + kvh) * D;
+      uint16_t *dst = (pwave ? a.dv : a.dk) + ((int64_t)key * a.h_kv + kvh) * D;
+      const float sc = pwave ? 1.0f : a.scale;
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-          const int d = dt * 32 + 8 * cc + 4 * half;
-          u32x2 kk, vv;
-          kk[0] = pack_bf16x2(dkacc[dt][4 * cc] * a.scale, dkacc[dt][4 * cc + 1] * a.scale);
-          kk[1] = pack_bf16x2(dkacc[dt][4 * cc + 2] * a.scale, dkacc[dt][4 * cc + 3] * a.scale);
-          vv[0] = pack_bf16x2(dvacc[dt][4 * cc], dvacc[dt][4 * cc + 1]);
-          vv[1] = pack_bf16x2(dvacc[dt][4 * cc + 2], dvacc[dt][4 * cc + 3]);
-          *reinterpret_cast<u32x2 *>(a.dk + base + d) = kk;
-          *reinterpret_cast<u32x2 *>(a.dv + base + d) = vv;
+          u32x2 pk;
+          pk[0] = pack_bf16x2(acc[dt][4 * cc] * sc, acc[dt][4 * cc + 1] * sc);
+          pk[1] = pack_bf16x2(acc[dt][4 * cc + 2] * sc, acc[dt][4 * cc + 3] * sc);
+          *reinterpret_cast<u32x2 *>(dst + dt * 32 + 8 * cc + 4 * half) = pk;
         }
     }
   }
@@ -579,9 +606,9 @@ libra_status launch_dkdv(const libra_plan_info &h, BwdArgs a, const void *plan_d
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_hip_error();
   if (h.params.head_dim == 128)
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(h.num_cus), dim3(kDkdvWaves * 64), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, dim3(h.num_cus), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, dim3(h.num_cus), dim3(kDkdvWaves * 64), 0, s, a);
   return launch_status();
 }
 
