@@ -32,8 +32,8 @@ DEVICE_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "device_common.h"]
 # Algorithmic FLOPs per unmasked (query, key, head) pair for each kernel:
 #   forward: QK^T and PV (2 x 2d); dK/dV pass: S recompute, dP, dV, dK (4 x 2d);
 #   dQ pass: dQ (2d) -- its S and dP recomputations are not algorithmic work.
-KERNEL_FLOPS_PER_PAIR = {"fwd_main": 4, "bwd_dkdv": 8, "bwd_dq": 2}
-KERNEL_SYMBOL = {"fwd_main": "attn_fwd_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel",
+KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 2}
+KERNEL_SYMBOL = {"fwd": "attn_fwd_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel",
                  "bwd_dq": "attn_bwd_dq_kernel"}
 
 
@@ -241,7 +241,6 @@ def main():
                    tile_heads=w.tile_heads, assign=args.assign)
     plan0 = lib.Plan(cu, **plan_kw)
     ncu = plan0.info.num_cus
-    ws_f = torch.empty(lib.libra_attn_fwd_workspace(plan0.host), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(max(1, lib.libra_attn_bwd_workspace(plan0.host)), dtype=torch.uint8, device=dev)
     rec = torch.zeros(3 * ncu * lib.RECORD_DTYPE.itemsize, dtype=torch.uint8, device=dev)
     rec_f, rec_kv, rec_q = rec[:ncu * 32], rec[ncu * 32:2 * ncu * 32], rec[2 * ncu * 32:]
@@ -259,7 +258,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
     ev = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for n in ("fwd_prepare", "fwd_main", "bwd_prepare", "bwd_dkdv", "bwd_dq")}
+          for n in ("fwd", "bwd_prepare", "bwd_dkdv", "bwd_dq")}
     times = {n: [] for n in ev}
     plan_ms = []
 
@@ -268,7 +267,7 @@ def main():
         plan = lib.Plan(cu, **plan_kw)                                  # host planner (a1-a3)
         plan_ms.append((time.perf_counter() - t0) * 1e3)
         plan_dev.copy_(torch.from_numpy(plan.host))                      # plan upload
-        wsf, wsb = ws_f.numel(), ws_b.numel()
+        wsb = ws_b.numel()
 
         def timed(name, fn):
             if record:
@@ -277,11 +276,9 @@ def main():
             if record:
                 ev[name][1].record(stream)
 
-        timed("fwd_prepare", lambda: lib.libra_attn_fwd_prepare(plan.host, v, ws_f, wsf, sh))
-        timed("fwd_main", lambda: lib.libra_attn_fwd_main(plan.host, plan_dev, q, k, cu_dev, o, lse, scale,
-                                                          ws_f, wsf, rec_f, sh))
+        timed("fwd", lambda: lib.libra_attn_fwd(plan.host, plan_dev, q, k, v, cu_dev, o, lse, scale, rec_f, sh))
         if do_bwd:
-            timed("bwd_prepare", lambda: lib.libra_attn_bwd_prepare(plan.host, q, k, o, dout, lse, ws_b, wsb, sh))
+            timed("bwd_prepare", lambda: lib.libra_attn_bwd_prepare(plan.host, o, dout, lse, ws_b, wsb, sh))
             timed("bwd_dkdv", lambda: lib.libra_attn_bwd_dkdv(plan.host, plan_dev, q, k, v, dout, lse, cu_dev,
                                                               dk, dv, scale, ws_b, wsb, rec_kv, sh))
             timed("bwd_dq", lambda: lib.libra_attn_bwd_dq(plan.host, plan_dev, q, k, v, dout, lse, cu_dev, dq,
@@ -293,7 +290,7 @@ def main():
     plan_ms.clear()
 
     wall = 0.0
-    busy = {"fwd_main": [], "bwd_dkdv": [], "bwd_dq": []}
+    busy = {"fwd": [], "bwd_dkdv": [], "bwd_dq": []}
     for i in range(args.steps):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -304,7 +301,7 @@ def main():
             if n.startswith("bwd") and not do_bwd:
                 continue
             times[n].append(a_.elapsed_time(b_))
-        for n, r in (("fwd_main", rec_f), ("bwd_dkdv", rec_kv), ("bwd_dq", rec_q)):
+        for n, r in (("fwd", rec_f), ("bwd_dkdv", rec_kv), ("bwd_dq", rec_q)):
             if n.startswith("bwd") and not do_bwd:
                 continue
             ratio, _ = cu_busy_ratio(r.cpu().numpy(), ncu)
@@ -318,7 +315,7 @@ def main():
     fwd_flops = 4.0 * d * pairs
     total_flops = fwd_flops * (3.5 if do_bwd else 1.0)
     avg = {n: float(np.mean(t)) for n, t in times.items() if t}
-    fwd_ms = avg["fwd_prepare"] + avg["fwd_main"]
+    fwd_ms = avg["fwd"]
     kernels = {n: avg[n] for n in KERNEL_FLOPS_PER_PAIR if n in avg}
     dom = max(kernels, key=kernels.get)
     achieved = KERNEL_FLOPS_PER_PAIR[dom] * d * pairs / (kernels[dom] * 1e-3) / 1e12
@@ -342,8 +339,7 @@ def main():
                    "max_sample": int(lengths.max()), "seed": args.seed, "pass": "fwd+bwd" if do_bwd else "fwd",
                    "placement": "algorithm2" if args.assign == 0 else "round_robin", "num_cus": ncu},
         "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
-        "fwd_main_tflops": round(fwd_flops / (avg["fwd_main"] * 1e-3) / 1e12, 2),
-        "fwd_frac_peak": round(fwd_flops / (avg["fwd_main"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "fwd_frac_peak": round(fwd_flops / (avg["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": {n: round(t, 4) for n, t in avg.items()},
         "plan_ms": round(float(np.mean(plan_ms)), 3),
         "cu_busy_max_over_mean": {n: round(float(np.mean(b)), 4) for n, b in busy.items() if b},

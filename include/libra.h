@@ -142,36 +142,19 @@ libra_status libra_plan(const int32_t *cu_seqlens, const libra_plan_params *para
  * bounds, checksum) and copy its header to *info (may be NULL). */
 libra_status libra_plan_check(const void *plan, size_t bytes, libra_plan_info *info);
 
-/* Device workspace the forward needs (transposed V), in bytes. */
-libra_status libra_attn_fwd_workspace(const void *plan, size_t *bytes);
-
 /* Forward pass.  plan: host plan buffer; plan_dev: its byte copy on the
  * device.  Writes o [L, h_q, d] bf16 and lse [h_q, L] fp32.  softmax_scale > 0
- * (commonly 1/sqrt(head_dim)).  workspace: device buffer of at least
- * libra_attn_fwd_workspace bytes (contents need not be initialised).
- * records: NULL or device libra_cu_record[num_cus].
- * Enqueues a transpose of V and one persistent kernel of num_cus workgroups
- * that runs each CU's queue of work items (Libra technical review, section
- * 5.4: the placement decided on the host is only executed here). */
+ * (commonly 1/sqrt(head_dim)).  records: NULL or device
+ * libra_cu_record[num_cus].  Enqueues one persistent kernel of num_cus
+ * workgroups that runs each CU's queue of work items (Libra technical review,
+ * section 5.4: the placement decided on the host is only executed here). */
 libra_status libra_attn_fwd(const void *plan, const void *plan_dev,
                             const void *q, const void *k, const void *v,
                             const int32_t *cu_seqlens_dev, void *o, float *lse,
-                            float softmax_scale, void *workspace, size_t workspace_bytes,
-                            libra_cu_record *records, void *stream);
+                            float softmax_scale, libra_cu_record *records, void *stream);
 
-/* The forward in two phases on the same stream (libra_attn_fwd enqueues both):
- * _prepare transposes V into the workspace; _main runs the persistent kernel
- * and reads only the workspace written by a preceding _prepare of the same v.
- * Arguments and errors as for libra_attn_fwd. */
-libra_status libra_attn_fwd_prepare(const void *plan, const void *v, void *workspace,
-                                    size_t workspace_bytes, void *stream);
-libra_status libra_attn_fwd_main(const void *plan, const void *plan_dev,
-                                 const void *q, const void *k, const int32_t *cu_seqlens_dev,
-                                 void *o, float *lse, float softmax_scale,
-                                 const void *workspace, size_t workspace_bytes,
-                                 libra_cu_record *records, void *stream);
-
-/* Device workspace the backward needs, in bytes. */
+/* Device workspace the backward needs (D = rowsum(dout * o) and LSE * log2(e),
+ * fp32 [h_q, L] each), in bytes. */
 libra_status libra_attn_bwd_workspace(const void *plan, size_t *bytes);
 
 /* Backward pass: dq [L, h_q, d], dk and dv [L, h_kv, d] (bf16) from q, k, v,
@@ -189,17 +172,17 @@ libra_status libra_attn_bwd(const void *plan, const void *plan_dev,
 
 /* The backward in three phases on the same stream (libra_attn_bwd enqueues
  * all three, in this order):
- *   _prepare: transposes q, dout and k into the workspace and computes
- *             D = rowsum(dout * o) and LSE * log2(e) (fp32);
+ *   _prepare: computes D = rowsum(dout * o) and LSE * log2(e) (fp32) into the
+ *             workspace;
  *   _dkdv:    the key-major persistent kernel writing dk and dv
  *             (records: NULL or libra_cu_record[num_cus]);
  *   _dq:      the query-major persistent kernel writing dq
  *             (records: NULL or libra_cu_record[num_cus]).
  * _dkdv and _dq read the workspace a preceding _prepare filled from the same
  * tensors.  Arguments and errors as for libra_attn_bwd. */
-libra_status libra_attn_bwd_prepare(const void *plan, const void *q, const void *k,
-                                    const void *o, const void *dout, const float *lse,
-                                    void *workspace, size_t workspace_bytes, void *stream);
+libra_status libra_attn_bwd_prepare(const void *plan, const void *o, const void *dout,
+                                    const float *lse, void *workspace, size_t workspace_bytes,
+                                    void *stream);
 libra_status libra_attn_bwd_dkdv(const void *plan, const void *plan_dev,
                                  const void *q, const void *k, const void *v,
                                  const void *dout, const float *lse,

@@ -81,14 +81,11 @@ def _load():
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     lib.libra_plan.argtypes = [vp, ctypes.POINTER(PlanParams), vp, ctypes.POINTER(sz)]
     lib.libra_plan_check.argtypes = [vp, sz, ctypes.POINTER(PlanInfo)]
-    lib.libra_attn_fwd_workspace.argtypes = [vp, ctypes.POINTER(sz)]
     lib.libra_attn_bwd_workspace.argtypes = [vp, ctypes.POINTER(sz)]
-    lib.libra_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
+    lib.libra_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp]
     lib.libra_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
                                    vp, sz, vp, vp]
-    lib.libra_attn_fwd_prepare.argtypes = [vp, vp, vp, sz, vp]
-    lib.libra_attn_fwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
-    lib.libra_attn_bwd_prepare.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.libra_attn_bwd_prepare.argtypes = [vp, vp, vp, vp, vp, sz, vp]
     lib.libra_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
     lib.libra_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
     lib.libra_device_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int32)]
@@ -96,9 +93,9 @@ def _load():
     lib.libra_status_str.restype = ctypes.c_char_p
     lib.libra_last_hip_error.argtypes = []
     lib.libra_last_hip_error.restype = ctypes.c_char_p
-    for name in ("libra_plan", "libra_plan_check", "libra_attn_fwd_workspace", "libra_attn_bwd_workspace",
-                 "libra_attn_fwd", "libra_attn_bwd", "libra_device_clock_khz", "libra_attn_fwd_prepare",
-                 "libra_attn_fwd_main", "libra_attn_bwd_prepare", "libra_attn_bwd_dkdv", "libra_attn_bwd_dq"):
+    for name in ("libra_plan", "libra_plan_check", "libra_attn_bwd_workspace", "libra_attn_fwd",
+                 "libra_attn_bwd", "libra_device_clock_khz", "libra_attn_bwd_prepare", "libra_attn_bwd_dkdv",
+                 "libra_attn_bwd_dq"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -148,23 +145,16 @@ def libra_plan_check(buf: np.ndarray) -> PlanInfo:
     return info
 
 
-def libra_attn_fwd_workspace(plan_host: np.ndarray) -> int:
-    n = ctypes.c_size_t(0)
-    _check(_lib.libra_attn_fwd_workspace(plan_host.ctypes.data, ctypes.byref(n)), "libra_attn_fwd_workspace")
-    return n.value
-
-
 def libra_attn_bwd_workspace(plan_host: np.ndarray) -> int:
     n = ctypes.c_size_t(0)
     _check(_lib.libra_attn_bwd_workspace(plan_host.ctypes.data, ctypes.byref(n)), "libra_attn_bwd_workspace")
     return n.value
 
 
-def libra_attn_fwd(plan_host, plan_dev, q, k, v, cu_seqlens_dev, o, lse, softmax_scale, workspace,
-                   workspace_bytes, records, stream):
+def libra_attn_fwd(plan_host, plan_dev, q, k, v, cu_seqlens_dev, o, lse, softmax_scale, records, stream):
     _check(_lib.libra_attn_fwd(_ptr(plan_host), _ptr(plan_dev), _ptr(q), _ptr(k), _ptr(v),
                                _ptr(cu_seqlens_dev), _ptr(o), _ptr(lse), float(softmax_scale),
-                               _ptr(workspace), int(workspace_bytes), _ptr(records), stream),
+                               _ptr(records), stream),
            "libra_attn_fwd")
 
 
@@ -177,21 +167,8 @@ def libra_attn_bwd(plan_host, plan_dev, q, k, v, o, dout, lse, cu_seqlens_dev, d
            "libra_attn_bwd")
 
 
-def libra_attn_fwd_prepare(plan_host, v, workspace, workspace_bytes, stream):
-    _check(_lib.libra_attn_fwd_prepare(_ptr(plan_host), _ptr(v), _ptr(workspace), int(workspace_bytes), stream),
-           "libra_attn_fwd_prepare")
-
-
-def libra_attn_fwd_main(plan_host, plan_dev, q, k, cu_seqlens_dev, o, lse, softmax_scale, workspace,
-                        workspace_bytes, records, stream):
-    _check(_lib.libra_attn_fwd_main(_ptr(plan_host), _ptr(plan_dev), _ptr(q), _ptr(k), _ptr(cu_seqlens_dev),
-                                    _ptr(o), _ptr(lse), float(softmax_scale), _ptr(workspace),
-                                    int(workspace_bytes), _ptr(records), stream),
-           "libra_attn_fwd_main")
-
-
-def libra_attn_bwd_prepare(plan_host, q, k, o, dout, lse, workspace, workspace_bytes, stream):
-    _check(_lib.libra_attn_bwd_prepare(_ptr(plan_host), _ptr(q), _ptr(k), _ptr(o), _ptr(dout), _ptr(lse),
+def libra_attn_bwd_prepare(plan_host, o, dout, lse, workspace, workspace_bytes, stream):
+    _check(_lib.libra_attn_bwd_prepare(_ptr(plan_host), _ptr(o), _ptr(dout), _ptr(lse),
                                        _ptr(workspace), int(workspace_bytes), stream),
            "libra_attn_bwd_prepare")
 
@@ -272,8 +249,7 @@ def _stream_handle(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def attn_fwd(plan: Plan, q, k, v, softmax_scale=None, *, out=None, lse=None, workspace=None,
-             records=None):
+def attn_fwd(plan: Plan, q, k, v, softmax_scale=None, *, out=None, lse=None, records=None):
     """Forward pass on torch tensors (bf16, [L, h, d], contiguous); returns (o, lse)."""
     import torch
     p = plan.params
@@ -282,11 +258,7 @@ def attn_fwd(plan: Plan, q, k, v, softmax_scale=None, *, out=None, lse=None, wor
     plan_dev, cu_dev = plan.device(dev)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((p.h_q, p.total_tokens), dtype=torch.float32, device=dev) if lse is None else lse
-    ws_bytes = libra_attn_fwd_workspace(plan.host)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    libra_attn_fwd(plan.host, plan_dev, q, k, v, cu_dev, o, lse, scale, workspace, workspace.numel(),
-                   records, _stream_handle(dev))
+    libra_attn_fwd(plan.host, plan_dev, q, k, v, cu_dev, o, lse, scale, records, _stream_handle(dev))
     return o, lse
 
 

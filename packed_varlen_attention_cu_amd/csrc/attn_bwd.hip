@@ -9,15 +9,16 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Work is split into two deterministic persistent passes (no atomics):
-//   * key-major dK/dV: an item is 128 keys of one KV head; each wave owns 32
-//     keys and walks every query block of every query head of the group that
-//     can see them, accumulating dK^T and dV^T in registers (GQA heads are
-//     summed in place);
+//   * key-major dK/dV: an item is 128 keys of one KV head; pairs of waves own
+//     32 keys each and walk every query block of every query head of the group
+//     that can see them, accumulating dK^T and dV^T in registers (GQA heads
+//     are summed in place);
 //   * query-major dQ: the forward's items and CU assignment, each wave owning
-//     64 query positions of one head and walking its key blocks.
-// Q, dO and K are transposed once per call into the workspace so that every
-// MFMA operand is 16 contiguous bytes per lane in LDS; D = rowsum(dO * O)
-// (fp32) is computed first from the forward's bf16 O.
+//     32 query positions of one head and walking its key blocks.
+// Operand blocks are copied straight from HBM into LDS; operands that need
+// the transposed layout (Q^T, dO^T, K^T) come from transposing LDS reads of
+// the row-major blocks.  A first phase computes D = rowsum(dO * O) (fp32)
+// from the forward's bf16 O and the forward's LSE in log2 units.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -70,12 +71,11 @@ struct BwdArgs {
   const libra_item *items;     // dK/dV: key-major queue; dQ: forward queue
   const int32_t *cu_off;
   const uint16_t *q, *k, *v, *dout;
-  const uint16_t *qt, *dot, *kt;   // transposed [heads][D][Lp]
   const float *lse, *dvec, *lse2;  // [h_q][L]: LSE, D = rowsum(dO * O), LSE * log2(e)
   const int32_t *cu;
   uint16_t *dq, *dk, *dv;
   libra_cu_record *records;
-  int n_samples, L, Lp, h_q, h_kv;
+  int n_samples, L, h_q, h_kv;
   float scale, scale_log2;
 };
 
@@ -99,20 +99,19 @@ __device__ __forceinline__ void write_record(const BwdArgs &a, int w, int n, uin
 // products the other runs its element-wise work.  Only the P wave applies the
 // block-diagonal mask: masked P is 0, hence masked dS is 0 too.
 //
-// Per query block of kQB rows and one head, LDS holds Q and dO (row-major,
-// A operands of S and dP), Q^T and dO^T (A operands of dK^T and dV^T) and the
-// block's LSE * log2(e) and D values.  Two such buffers alternate: after one
-// barrier the copies for the next (head, query block) step are queued into
-// the other buffer, and the current one is computed while they fly.  16-byte
-// chunk c of row r of a row-major block sits at position c ^ (r mod
-// chunks-per-row), and chunk c of row d of a transposed block at c ^ (d mod 8),
-// so the operand reads of a wave hit distinct banks.
+// Per query block of kQB rows and one head, LDS holds Q and dO (row-major:
+// A operands of S and dP directly, and of dK^T and dV^T through transposing
+// reads) and the block's LSE * log2(e) and D values.  Two such buffers
+// alternate: after one barrier the copies for the next (head, query block)
+// step are queued into the other buffer, and the current one is computed
+// while they fly.  16-byte chunk c of row r sits at position c ^ (r mod
+// chunks-per-row), so the operand reads of a wave hit distinct banks.
 constexpr int kDkdvWaves = 8;
 
 template <int D>
 struct DkdvLds {
   static constexpr int kRow = kQB * D;        // elements of a row-major block
-  static constexpr int kBuf = 4 * kRow + 2 * kQB * 2;   // 4 blocks + LSE and D (fp32), in uint16 units
+  static constexpr int kBuf = 2 * kRow + 2 * kQB * 2;   // Q, dO + LSE and D (fp32), in uint16 units
   static constexpr int kP = 4 * 32 * kQB;     // bf16 P of the four key groups
 };
 
@@ -123,8 +122,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NS = D / 16, ND = D / 32;
   constexpr int CH = D / 8;                        // 16-byte chunks per row-major row
   constexpr int RJ = kQB * CH / 64 / NW;           // DMA instructions per wave, row-major block
-  constexpr int TJ = D * (kQB / 8) / 64 / NW;      // DMA instructions per wave, transposed block
-  static_assert(RJ * NW * 64 == kQB * CH && TJ * NW * 64 == D * kQB / 8, "copies split evenly");
+  static_assert(RJ * NW * 64 == kQB * CH, "copies split evenly");
   static_assert(2 * kQB <= NW * 16, "LSE and D copies: 16 values per wave");
   constexpr int ROW = DkdvLds<D>::kRow;
   __shared__ __attribute__((aligned(16))) uint16_t buf0[DkdvLds<D>::kBuf];
@@ -141,6 +139,12 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   const float c = a.scale_log2;
   const uint32_t bl0 = lds_addr(buf0), bl1 = lds_addr(buf1);
   u32x4 *p_mine = reinterpret_cast<u32x4 *>(p_lds + kg * 32 * kQB) + lane;   // [4 slabs][64 lanes]
+  int tro[ND][2];                                  // transposing-read offsets of dO^T / Q^T operands
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) {
+    tro[dt][0] = tr_lane_off<D>(lane, dt * 32, 0);
+    tro[dt][1] = tr_lane_off<D>(lane, dt * 32, 1);
+  }
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -180,21 +184,12 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
         lds_dma16(a.q + g, dst + off);
         lds_dma16(a.dout + g, dst + 2 * ROW + off);     // byte offsets: a block is 2 * ROW bytes
       }
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int slot = (wave * TJ + j) * 64 + lane;
-        const int d = slot / (kQB / 8), cc = (slot % (kQB / 8)) ^ (d & 7);
-        const int64_t g = ((int64_t)h * D + d) * a.Lp + q0 + cc * 8;
-        const uint32_t off = (wave * TJ + j) * 1024;
-        lds_dma16(a.qt + g, dst + 4 * ROW + off);
-        lds_dma16(a.dot + g, dst + 6 * ROW + off);
-      }
       // LSE * log2(e) then D of the block's queries: lanes 0..15 of each wave copy 16 values.
       if (lane < 16) {
         const int e = wave * 16 + lane;             // 0 .. 2 kQB - 1
         const int qq = min(q0 + (e & (kQB - 1)), a.L - 1);
         const float *src = (e < kQB ? a.lse2 : a.dvec) + (int64_t)h * a.L + qq;
-        lds_dma4(src, dst + 8 * ROW + wave * 64);
+        lds_dma4(src, dst + 4 * ROW + wave * 64);
       }
     };
 
@@ -208,8 +203,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
       const bool touch = kok && (q0 + kQB - 1 >= key) && (q0 < kend);
       const bool full = !kok || ((key <= q0) && (q0 + kQB - 1 < kend));
       const bool act = wave_any(touch);     // identical for the two waves of a key group
-      const uint16_t *q_l = bq, *do_l = bq + ROW, *qt_l = bq + 2 * ROW, *dot_l = bq + 3 * ROW;
-      const float *lse_l = reinterpret_cast<const float *>(bq + 4 * ROW);
+      const uint16_t *q_l = bq, *do_l = bq + ROW;
+      const float *lse_l = reinterpret_cast<const float *>(bq + 2 * ROW);
       const float *dd_l = lse_l + kQB;
 
       // First product: S (P wave, A = Q) or dP (dS wave, A = dO); C layout, lane = key.
@@ -280,18 +275,18 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
             }
         }
       }
-      // Second product: dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave).
+      // Second product: dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave); the
+      // transposed A operands are read from the row-major dO / Q blocks.
       if (act) {
-        const uint16_t *t_l = pwave ? dot_l : qt_l;
+        const uint16_t *t_l = pwave ? do_l : q_l;
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-              const int d = dt * 32 + col;
-              const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                  t_l + d * kQB + (((qt * 4 + 2 * t + half) ^ (d & 7)) * 8)));
+              const uint16_t *slab = t_l + (qt * 32 + 16 * t) * D;
+              const bf16x8 av = lds_tr_operand(slab, tro[dt][0], tro[dt][1]);
               acc[dt] = mfma32x32x16(av, as_bf16x8(pw[qt][t]), acc[dt]);
             }
       }
@@ -326,9 +321,9 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 // ----------------------------------------------------------------- dQ pass
 // Eight waves of 32 query positions each cover the 256 query columns of a
 // forward work item (two waves per SIMD).  Per key block of kKB keys, LDS
-// holds K and V (row-major, A operands of S^T and dP^T) and K^T (A operand of
-// dQ^T), double-buffered like the forward; all query heads of the item's KV
-// head read the same copy.
+// holds K and V (row-major: A operands of S^T and dP^T, and through
+// transposing reads the K^T operand of dQ^T), double-buffered like the
+// forward; all query heads of the item's KV head read the same copy.
 constexpr int kDqWaves = 8;
 
 template <int D>
@@ -338,11 +333,10 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int NS = D / 16, ND = D / 32;
   constexpr int CH = D / 8;
   constexpr int RJ = kKB * CH / 64 / NW;           // DMA instructions per wave, K or V block
-  constexpr int TJ = D * (kKB / 8) / 64 / NW;      // DMA instructions per wave, K^T block
-  static_assert(RJ * NW * 64 == kKB * CH && TJ * NW * 64 == D * kKB / 8, "copies split evenly");
+  static_assert(RJ * NW * 64 == kKB * CH, "copies split evenly");
   constexpr int BLK = kKB * D;                     // elements of one block
-  __shared__ __attribute__((aligned(16))) uint16_t buf0[3 * BLK];
-  __shared__ __attribute__((aligned(16))) uint16_t buf1[3 * BLK];
+  __shared__ __attribute__((aligned(16))) uint16_t buf0[2 * BLK];
+  __shared__ __attribute__((aligned(16))) uint16_t buf1[2 * BLK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int half = lane >> 5, col = lane & 31;
@@ -351,6 +345,12 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const int beg = a.cu_off[w], end = a.cu_off[w + 1];
   const float c = a.scale_log2;
   const uint32_t bl0 = lds_addr(buf0), bl1 = lds_addr(buf1);
+  int tro[ND][2];                                  // transposing-read offsets of K^T operands
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) {
+    tro[dt][0] = tr_lane_off<D>(lane, dt * 32, 0);
+    tro[dt][1] = tr_lane_off<D>(lane, dt * 32, 1);
+  }
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -390,12 +390,6 @@ void attn_bwd_dq_kernel(BwdArgs a) {
         lds_dma16(a.k + g, dst + off);
         lds_dma16(a.v + g, dst + 2 * BLK + off);     // byte offsets: a block is 2 * BLK bytes
       }
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int slot = (wave * TJ + j) * 64 + lane;
-        const int d = slot / (kKB / 8), cc = (slot % (kKB / 8)) ^ (d & 7);
-        lds_dma16(a.kt + ((int64_t)kvh * D + d) * a.Lp + k0 + cc * 8, dst + 4 * BLK + (wave * TJ + j) * 1024);
-      }
     };
 
     auto block = [&](int b, auto bufc) {
@@ -409,7 +403,7 @@ void attn_bwd_dq_kernel(BwdArgs a) {
       const bool partial = qok && !((k0 >= qss) && (k0 + kKB - 1 <= qpos));
       if (wave_any(touch)) {
         const bool masked = wave_any(partial);
-        const uint16_t *k_l = bk, *v_l = bk + BLK, *kt_l = bk + 2 * BLK;
+        const uint16_t *k_l = bk, *v_l = bk + BLK;
         const int lo = qok ? qss : 1, hi = qok ? qpos : 0;
         // One 32-key tile at a time keeps S^T, dP^T and dS^T of a single tile live.
 #pragma unroll
@@ -448,10 +442,9 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const int d = dt * 32 + col;
-              const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                  kt_l + d * kKB + (((kt * 4 + 2 * t + half) ^ (d & 7)) * 8)));
+            for (int t = 0; t < 2; ++t) {   // K^T operand read transposed from the row-major K block
+              const uint16_t *slab = k_l + (kt * 32 + 16 * t) * D;
+              const bf16x8 ka = lds_tr_operand(slab, tro[dt][0], tro[dt][1]);
               dqacc[dt] = mfma32x32x16(ka, as_bf16x8(dsw[t]), dqacc[dt]);
             }
         }
@@ -484,17 +477,15 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 struct BwdLayout {
-  size_t qt, dot, kt, dvec, lse2, total;
+  size_t dvec, lse2, total;
 };
 
 BwdLayout bwd_layout(const libra_plan_params &p) {
   BwdLayout l;
-  l.qt = 0;
-  l.dot = l.qt + transposed_bytes(p.h_q, p.head_dim, p.total_tokens);
-  l.kt = l.dot + transposed_bytes(p.h_q, p.head_dim, p.total_tokens);
-  l.dvec = l.kt + transposed_bytes(p.h_kv, p.head_dim, p.total_tokens);
-  l.lse2 = l.dvec + (size_t)round_up64((int64_t)p.h_q * p.total_tokens * 4, 256);
-  l.total = l.lse2 + (size_t)round_up64((int64_t)p.h_q * p.total_tokens * 4, 256);
+  const size_t rows = (size_t)round_up64((int64_t)p.h_q * p.total_tokens * 4, 256);
+  l.dvec = 0;
+  l.lse2 = rows;
+  l.total = 2 * rows;
   return l;
 }
 
@@ -521,11 +512,10 @@ libra_status check_workspace(const libra_plan_info &h, const void *ws, size_t by
   return bytes < bwd_layout(h.params).total ? LIBRA_ESIZE : LIBRA_OK;
 }
 
-libra_status check_prepare(const libra_plan_info &h, const void *q, const void *k, const void *o,
-                           const void *dout, const float *lse, const void *ws, size_t bytes) {
+libra_status check_prepare(const libra_plan_info &h, const void *o, const void *dout, const float *lse,
+                           const void *ws, size_t bytes) {
   if (h.params.total_tokens == 0) return LIBRA_OK;
-  if (any_null({q, k, o, dout, lse}) || any_misaligned({q, k, o, dout}, 16) || misaligned(lse, 4))
-    return LIBRA_EINVAL;
+  if (any_null({o, dout, lse}) || any_misaligned({o, dout}, 16) || misaligned(lse, 4)) return LIBRA_EINVAL;
   return check_workspace(h, ws, bytes);
 }
 
@@ -553,16 +543,12 @@ BwdArgs make_args(const libra_plan_info &h, const void *q, const void *k, const 
   a.k = static_cast<const uint16_t *>(k);
   a.v = static_cast<const uint16_t *>(v);
   a.dout = static_cast<const uint16_t *>(dout);
-  a.qt = reinterpret_cast<const uint16_t *>(w + lay.qt);
-  a.dot = reinterpret_cast<const uint16_t *>(w + lay.dot);
-  a.kt = reinterpret_cast<const uint16_t *>(w + lay.kt);
   a.lse = lse;
   a.dvec = reinterpret_cast<const float *>(w + lay.dvec);
   a.lse2 = reinterpret_cast<const float *>(w + lay.lse2);
   a.cu = cu_dev;
   a.n_samples = p.num_samples;
   a.L = p.total_tokens;
-  a.Lp = (int)round_up64(p.total_tokens, 64);
   a.h_q = p.h_q;
   a.h_kv = p.h_kv;
   a.scale = scale;
@@ -570,15 +556,11 @@ BwdArgs make_args(const libra_plan_info &h, const void *q, const void *k, const 
   return a;
 }
 
-libra_status launch_prepare(const libra_plan_info &h, const void *q, const void *k, const void *o,
-                            const void *dout, const float *lse, void *ws, void *stream) {
+libra_status launch_prepare(const libra_plan_info &h, const void *o, const void *dout, const float *lse,
+                            void *ws, void *stream) {
   const libra_plan_params &p = h.params;
   const BwdLayout lay = bwd_layout(p);
   char *w = static_cast<char *>(ws);
-  libra_status st;
-  if ((st = launch_transpose(q, w + lay.qt, p.total_tokens, p.h_q, p.head_dim, stream)) != LIBRA_OK) return st;
-  if ((st = launch_transpose(dout, w + lay.dot, p.total_tokens, p.h_q, p.head_dim, stream)) != LIBRA_OK) return st;
-  if ((st = launch_transpose(k, w + lay.kt, p.total_tokens, p.h_kv, p.head_dim, stream)) != LIBRA_OK) return st;
   const int64_t rows = (int64_t)p.total_tokens * p.h_q;
   const int rows_per_block = kThreads / (p.head_dim / 8);
   const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
@@ -640,14 +622,14 @@ extern "C" libra_status libra_attn_bwd_workspace(const void *plan, size_t *bytes
   return LIBRA_OK;
 }
 
-extern "C" libra_status libra_attn_bwd_prepare(const void *plan, const void *q, const void *k,
-                                               const void *o, const void *dout, const float *lse,
-                                               void *workspace, size_t workspace_bytes, void *stream) {
+extern "C" libra_status libra_attn_bwd_prepare(const void *plan, const void *o, const void *dout,
+                                               const float *lse, void *workspace, size_t workspace_bytes,
+                                               void *stream) {
   libra_plan_info h;
   libra_status st = check_header(plan, &h);
-  if (st == LIBRA_OK) st = check_prepare(h, q, k, o, dout, lse, workspace, workspace_bytes);
+  if (st == LIBRA_OK) st = check_prepare(h, o, dout, lse, workspace, workspace_bytes);
   if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
-  return launch_prepare(h, q, k, o, dout, lse, workspace, stream);
+  return launch_prepare(h, o, dout, lse, workspace, stream);
 }
 
 extern "C" libra_status libra_attn_bwd_dkdv(const void *plan, const void *plan_dev, const void *q,
@@ -688,12 +670,12 @@ extern "C" libra_status libra_attn_bwd(const void *plan, const void *plan_dev, c
                                        size_t workspace_bytes, libra_cu_record *records, void *stream) {
   libra_plan_info h;
   libra_status st = check_header(plan, &h);
-  if (st == LIBRA_OK) st = check_prepare(h, q, k, o, dout, lse, workspace, workspace_bytes);
+  if (st == LIBRA_OK) st = check_prepare(h, o, dout, lse, workspace, workspace_bytes);
   if (st == LIBRA_OK)
     st = check_pass(h, plan_dev, {q, k, v, dout, dq, dk, dv}, lse, cu_dev, softmax_scale, workspace,
                     workspace_bytes, records);
   if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
-  if ((st = launch_prepare(h, q, k, o, dout, lse, workspace, stream)) != LIBRA_OK) return st;
+  if ((st = launch_prepare(h, o, dout, lse, workspace, stream)) != LIBRA_OK) return st;
   const BwdArgs a = make_args(h, q, k, v, dout, lse, cu_dev, workspace, softmax_scale);
   if ((st = launch_dkdv(h, a, plan_dev, dk, dv, records, stream)) != LIBRA_OK) return st;
   return launch_dq(h, a, plan_dev, dq, records ? records + h.num_cus : nullptr, stream);

@@ -3,25 +3,24 @@
 // One persistent workgroup per CU runs the queue of work items the host
 // planner assigned to it (Libra technical review, section 5.4: placement is
 // decided on the host, the device only executes it).  A work item is up to
-// 256 query columns (positions x heads) of one KV head; each of the four
-// waves owns 64 query positions of one query head.
+// 256 query columns (positions x heads) of one KV head; each of the eight
+// waves owns 32 query positions of one query head (two waves per SIMD).
 //
 // Per item the workgroup walks key blocks of 64 from the start of the sample
-// holding the item's first row to its last row.  K and V^T blocks are staged
-// in LDS once and read by every wave, so all query heads of a GQA group share
-// one copy.  Each wave computes S^T = K Q^T with bf16 MFMA (its query columns
-// land one per lane, so row statistics need no cross-lane reduction beyond
-// the two 32-lane halves), applies the block-diagonal causal mask only on
-// blocks that straddle a sample start or the diagonal, skips blocks that are
-// wholly masked for it, and keeps an fp32 online softmax:
-//   m' = max(m, max_k s * c),  P = 2^(s c - m'),  l = l 2^(m - m') + sum P,
-//   O^T = O^T 2^(m - m') + V^T P^T            with c = scale * log2(e).
+// holding the item's first row to its last row.  K and V blocks are copied
+// straight from HBM into LDS (double-buffered) and read by every wave, so all
+// query heads of a GQA group share one copy.  Each wave computes S^T = K Q^T
+// with bf16 MFMA (its query columns land one per lane, so row statistics need
+// no cross-lane reduction beyond the two 32-lane halves), applies the
+// block-diagonal causal mask only on blocks that straddle a sample start or
+// the diagonal, skips blocks that are wholly masked for it, and keeps an fp32
+// online softmax with c = scale * log2(e):
+//   m' = max(m, max_k s c),  P = 2^(s c - m'),  l = l 2^(m - m') + sum P,
+//   O^T = O^T 2^(m - m') + V^T P^T.
 // P is rounded to bf16 for the PV product and l sums the rounded values, so
 // the weights applied to V sum to exactly l.  The epilogue writes O = O^T / l
-// (bf16) and LSE = (m + log2 l) ln 2 (natural log, fp32).
-//
-// V is transposed once per call into the workspace (Vt [h_kv][d][Lp]) so both
-// MFMA operands read 16 contiguous bytes per lane from LDS.
+// (bf16) and LSE = (m + log2 l) ln 2 (natural log, fp32).  The V^T operands
+// are read from the row-major V block with transposing LDS reads.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -34,55 +33,17 @@
 
 namespace libra {
 
-constexpr int kThreads = 256;
 constexpr int kBN = 64;          // keys per block
-constexpr int kTileTok = 64;     // tokens per transpose tile
-
-inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-
-// src [L][H][D] (token-major) -> dst [H][D][Lp]; tokens L..Lp-1 are zero.
-template <int D>
-__global__ __launch_bounds__(kThreads) void transpose_heads_kernel(const uint16_t *__restrict__ src,
-                                                                   uint16_t *__restrict__ dst, int L,
-                                                                   int H, int Lp) {
-  constexpr int kStride = D + 2;   // odd word stride: column reads hit distinct banks
-  __shared__ uint16_t tile[kTileTok * kStride];
-  const int t0 = blockIdx.x * kTileTok;
-  const int h = blockIdx.y;
-  const int tid = threadIdx.x;
-  constexpr int kChunks = D / 8;
-  for (int c = tid; c < kTileTok * kChunks; c += kThreads) {
-    const int r = c / kChunks, cc = c % kChunks;
-    const int tok = t0 + r;
-    u32x4 val = zero_u32x4();
-    if (tok < L) val = *reinterpret_cast<const u32x4 *>(src + ((int64_t)tok * H + h) * D + cc * 8);
-    uint32_t *row = reinterpret_cast<uint32_t *>(tile + r * kStride + cc * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) row[i] = val[i];
-  }
-  __syncthreads();
-  for (int c = tid; c < D * (kTileTok / 8); c += kThreads) {
-    const int d = c / (kTileTok / 8), j = c % (kTileTok / 8);
-    u32x4 out;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = tile[(8 * j + 2 * i) * kStride + d];
-      const uint32_t hi = tile[(8 * j + 2 * i + 1) * kStride + d];
-      out[i] = lo | (hi << 16);
-    }
-    *reinterpret_cast<u32x4 *>(dst + ((int64_t)h * D + d) * Lp + t0 + 8 * j) = out;
-  }
-}
 
 struct FwdArgs {
   const libra_item *items;
   const int32_t *cu_off;
-  const uint16_t *q, *k, *vt;
+  const uint16_t *q, *k, *v;
   const int32_t *cu;
   uint16_t *o;
   float *lse;
   libra_cu_record *records;
-  int n_samples, L, Lp, h_q, h_kv;
+  int n_samples, L, h_q, h_kv;
   float scale_log2;
 };
 
@@ -109,13 +70,11 @@ void attn_fwd_kernel(FwdArgs a) {
   constexpr int NS = D / 16;                    // reduction slabs of d
   constexpr int ND = D / 32;                    // 32-row tiles of d in O^T
   constexpr int CH = D / 8;                     // 16-byte chunks per K row
-  constexpr int KJ = kBN * CH / 64 / NW;        // LDS-DMA instructions per wave, K block
-  constexpr int VJ = D * (kBN / 8) / 64 / NW;   // LDS-DMA instructions per wave, V^T block
-  static_assert(KJ >= 1 && VJ >= 1 && KJ * NW * 64 == kBN * CH && VJ * NW * 64 == D * kBN / 8,
-                "the waves split each block copy evenly");
-  // Two buffers of K [kBN][D] and V^T [D][kBN], rows unpadded; 16-byte chunk c
-  // of row r sits at position c ^ (r mod chunks-per-row) so operand reads hit
-  // distinct banks.
+  constexpr int KJ = kBN * CH / 64 / NW;        // LDS-DMA instructions per wave, K or V block
+  static_assert(KJ >= 1 && KJ * NW * 64 == kBN * CH, "the waves split each block copy evenly");
+  // Two buffers of K and V [kBN][D], rows unpadded; 16-byte chunk c of row r
+  // sits at position c ^ (r mod chunks-per-row) so operand reads hit distinct
+  // banks.  The V^T operands of O^T = V^T P^T come from transposing reads.
   // Distinct arrays per buffer let the compiler see that a copy in flight into
   // one buffer cannot alias reads of the other, so it adds no waits for it.
   __shared__ __attribute__((aligned(16))) uint16_t k_lds0[kBN * D];
@@ -133,6 +92,12 @@ void attn_fwd_kernel(FwdArgs a) {
   const uint32_t vl0 = lds_addr(v_lds0), vl1 = lds_addr(v_lds1);
   const float NEG_INF = -__builtin_inff();
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  int tro[ND][2];                               // transposing-read offsets of V^T operands
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) {
+    tro[dt][0] = tr_lane_off<D>(lane, dt * 32, 0);
+    tro[dt][1] = tr_lane_off<D>(lane, dt * 32, 1);
+  }
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -172,7 +137,7 @@ void attn_fwd_kernel(FwdArgs a) {
       l_run[qt] = 0.0f;
     }
 
-    // Queue the K and V^T blocks at key k0 into LDS buffer BUF (no registers).
+    // Queue the K and V blocks at key k0 into LDS buffer BUF (no registers).
     auto issue = [&](int k0, auto bufc) {
       const uint32_t kdst = decltype(bufc)::value == 0 ? kl0 : kl1;
       const uint32_t vdst = decltype(bufc)::value == 0 ? vl0 : vl1;
@@ -181,13 +146,9 @@ void attn_fwd_kernel(FwdArgs a) {
         const int slot = (wave * KJ + j) * 64 + lane;
         const int r = slot / CH, c = (slot % CH) ^ (r & (CH - 1));
         const int key = min(k0 + r, a.L - 1);     // rows past L are masked; keep the address valid
-        lds_dma16(a.k + ((int64_t)key * a.h_kv + kvh) * D + c * 8, kdst + (wave * KJ + j) * 1024);
-      }
-#pragma unroll
-      for (int j = 0; j < VJ; ++j) {
-        const int slot = (wave * VJ + j) * 64 + lane;
-        const int d = slot / (kBN / 8), c = (slot % (kBN / 8)) ^ (d & 7);
-        lds_dma16(a.vt + ((int64_t)kvh * D + d) * a.Lp + k0 + c * 8, vdst + (wave * VJ + j) * 1024);
+        const int64_t g = ((int64_t)key * a.h_kv + kvh) * D + c * 8;
+        lds_dma16(a.k + g, kdst + (wave * KJ + j) * 1024);
+        lds_dma16(a.v + g, vdst + (wave * KJ + j) * 1024);
       }
     };
 
@@ -293,9 +254,7 @@ void attn_fwd_kernel(FwdArgs a) {
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-              const int row = dt * 32 + col;
-              const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                  vb + row * kBN + (((kt * 4 + 2 * t + half) ^ (row & 7)) * 8)));
+              const bf16x8 va = lds_tr_operand(vb + (kt * 32 + 16 * t) * D, tro[dt][0], tro[dt][1]);
 #pragma unroll
               for (int qt = 0; qt < QT; ++qt)
                 oacc[qt][dt] = mfma32x32x16(va, as_bf16x8(pw[qt][kt][t]), oacc[qt][dt]);
@@ -344,24 +303,6 @@ void attn_fwd_kernel(FwdArgs a) {
   }
 }
 
-size_t transposed_bytes(int64_t heads, int64_t d, int64_t L) {
-  return (size_t)round_up(heads * d * round_up(L, kTileTok) * 2, 256);
-}
-
-libra_status launch_transpose(const void *src, void *dst, int L, int H, int D, void *stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int Lp = (int)round_up(L, kTileTok);
-  dim3 grid(Lp / kTileTok, H);
-  clear_hip_error();
-  if (D == 128)
-    hipLaunchKernelGGL(transpose_heads_kernel<128>, grid, dim3(kThreads), 0, s,
-                       static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst), L, H, Lp);
-  else
-    hipLaunchKernelGGL(transpose_heads_kernel<64>, grid, dim3(kThreads), 0, s,
-                       static_cast<const uint16_t *>(src), static_cast<uint16_t *>(dst), L, H, Lp);
-  return launch_status();
-}
-
 bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 namespace {
@@ -381,13 +322,6 @@ libra_status launch_status() {
 
 using namespace libra;
 
-extern "C" libra_status libra_attn_fwd_workspace(const void *plan, size_t *bytes) {
-  libra_plan_info h;
-  if (!bytes || plan_header(plan, &h) != LIBRA_OK) return LIBRA_EINVAL;
-  *bytes = transposed_bytes(h.params.h_kv, h.params.head_dim, h.params.total_tokens);
-  return LIBRA_OK;
-}
-
 namespace {
 
 libra_status check_header(const void *plan, libra_plan_info *h) {
@@ -396,32 +330,22 @@ libra_status check_header(const void *plan, libra_plan_info *h) {
   return LIBRA_OK;
 }
 
-libra_status check_prepare(const libra_plan_info &h, const void *v, const void *workspace,
-                           size_t workspace_bytes) {
-  const libra_plan_params &p = h.params;
-  if (p.total_tokens == 0) return LIBRA_OK;
-  if (!v || !workspace || misaligned(v, 16) || misaligned(workspace, 16)) return LIBRA_EINVAL;
-  if (workspace_bytes < transposed_bytes(p.h_kv, p.head_dim, p.total_tokens)) return LIBRA_ESIZE;
-  return LIBRA_OK;
-}
-
-libra_status check_main(const libra_plan_info &h, const void *plan_dev, const void *q, const void *k,
-                        const int32_t *cu_dev, const void *o, const float *lse, float scale,
-                        const void *workspace, size_t workspace_bytes, const void *records) {
+libra_status check_fwd(const libra_plan_info &h, const void *plan_dev, const void *q, const void *k,
+                       const void *v, const int32_t *cu_dev, const void *o, const float *lse, float scale,
+                       const void *records) {
   const libra_plan_params &p = h.params;
   if (!(scale > 0.0f) || !std::isfinite(scale)) return LIBRA_EINVAL;
   if (p.total_tokens == 0) return LIBRA_OK;
-  if (!plan_dev || !q || !k || !cu_dev || !o || !lse || !workspace) return LIBRA_EINVAL;
-  if (misaligned(plan_dev, 16) || misaligned(q, 16) || misaligned(k, 16) || misaligned(o, 16) ||
-      misaligned(lse, 4) || misaligned(cu_dev, 4) || misaligned(workspace, 16) || misaligned(records, 16))
+  if (!plan_dev || !q || !k || !v || !cu_dev || !o || !lse) return LIBRA_EINVAL;
+  if (misaligned(plan_dev, 16) || misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) ||
+      misaligned(o, 16) || misaligned(lse, 4) || misaligned(cu_dev, 4) || misaligned(records, 16))
     return LIBRA_EINVAL;
-  if (workspace_bytes < transposed_bytes(p.h_kv, p.head_dim, p.total_tokens)) return LIBRA_ESIZE;
   return LIBRA_OK;
 }
 
-libra_status launch_main(const libra_plan_info &h, const void *plan_dev, const void *q, const void *k,
-                         const int32_t *cu_dev, void *o, float *lse, float scale, const void *workspace,
-                         libra_cu_record *records, void *stream) {
+libra_status launch_fwd(const libra_plan_info &h, const void *plan_dev, const void *q, const void *k,
+                        const void *v, const int32_t *cu_dev, void *o, float *lse, float scale,
+                        libra_cu_record *records, void *stream) {
   const libra_plan_params &p = h.params;
   FwdArgs a;
   const char *pd = static_cast<const char *>(plan_dev);
@@ -429,14 +353,13 @@ libra_status launch_main(const libra_plan_info &h, const void *plan_dev, const v
   a.cu_off = reinterpret_cast<const int32_t *>(pd + h.off_cu_off);
   a.q = static_cast<const uint16_t *>(q);
   a.k = static_cast<const uint16_t *>(k);
-  a.vt = static_cast<const uint16_t *>(workspace);
+  a.v = static_cast<const uint16_t *>(v);
   a.cu = cu_dev;
   a.o = static_cast<uint16_t *>(o);
   a.lse = lse;
   a.records = records;
   a.n_samples = p.num_samples;
   a.L = p.total_tokens;
-  a.Lp = (int)round_up(p.total_tokens, kTileTok);
   a.h_q = p.h_q;
   a.h_kv = p.h_kv;
   a.scale_log2 = scale * kLog2e;
@@ -451,41 +374,15 @@ libra_status launch_main(const libra_plan_info &h, const void *plan_dev, const v
 
 }  // namespace
 
-extern "C" libra_status libra_attn_fwd_prepare(const void *plan, const void *v, void *workspace,
-                                               size_t workspace_bytes, void *stream) {
-  libra_plan_info h;
-  libra_status st = check_header(plan, &h);
-  if (st == LIBRA_OK) st = check_prepare(h, v, workspace, workspace_bytes);
-  if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
-  return launch_transpose(v, workspace, h.params.total_tokens, h.params.h_kv, h.params.head_dim, stream);
-}
-
-extern "C" libra_status libra_attn_fwd_main(const void *plan, const void *plan_dev, const void *q,
-                                            const void *k, const int32_t *cu_dev, void *o, float *lse,
-                                            float softmax_scale, const void *workspace,
-                                            size_t workspace_bytes, libra_cu_record *records,
-                                            void *stream) {
-  libra_plan_info h;
-  libra_status st = check_header(plan, &h);
-  if (st == LIBRA_OK)
-    st = check_main(h, plan_dev, q, k, cu_dev, o, lse, softmax_scale, workspace, workspace_bytes, records);
-  if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
-  return launch_main(h, plan_dev, q, k, cu_dev, o, lse, softmax_scale, workspace, records, stream);
-}
-
 extern "C" libra_status libra_attn_fwd(const void *plan, const void *plan_dev, const void *q,
                                        const void *k, const void *v, const int32_t *cu_dev, void *o,
-                                       float *lse, float softmax_scale, void *workspace,
-                                       size_t workspace_bytes, libra_cu_record *records, void *stream) {
+                                       float *lse, float softmax_scale, libra_cu_record *records,
+                                       void *stream) {
   libra_plan_info h;
   libra_status st = check_header(plan, &h);
-  if (st == LIBRA_OK) st = check_prepare(h, v, workspace, workspace_bytes);
-  if (st == LIBRA_OK)
-    st = check_main(h, plan_dev, q, k, cu_dev, o, lse, softmax_scale, workspace, workspace_bytes, records);
+  if (st == LIBRA_OK) st = check_fwd(h, plan_dev, q, k, v, cu_dev, o, lse, softmax_scale, records);
   if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
-  st = launch_transpose(v, workspace, h.params.total_tokens, h.params.h_kv, h.params.head_dim, stream);
-  if (st != LIBRA_OK) return st;
-  return launch_main(h, plan_dev, q, k, cu_dev, o, lse, softmax_scale, workspace, records, stream);
+  return launch_fwd(h, plan_dev, q, k, v, cu_dev, o, lse, softmax_scale, records, stream);
 }
 
 extern "C" const char *libra_last_hip_error(void) {

@@ -143,6 +143,38 @@ __device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0
 // for the next block stay in flight across the barrier.
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j supplies the address of four consecutive 16-bit values M[j][0..3];
+// lane 4a + b receives M[a][b], M[a + 4][b], M[a + 8][b], M[a + 12][b].
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(const __attribute__((address_space(3))) void *)p);
+}
+
+// MFMA A operand of Mat^T from a row-major bf16 block Mat [rows][D] in LDS
+// whose 16-byte chunk c of row r sits at position c ^ (r mod D/8): lane
+// (col, half) receives Mat[k0 + 8 half + i][r0 + col], i = 0..7, for a
+// multiple of 32 r0 and a multiple of 16 k0.  Lane j of 16-lane group g
+// addresses row k0 + 8 (g >> 1) + 4 p + j / 4, columns r0 + 16 (g & 1) +
+// 4 (j % 4) + 0..3, for the two reads p = 0, 1; by the rule above the
+// group's lane i then holds rows k0 + 8 (g >> 1) + 4 p + 0..3 of column
+// r0 + 16 (g & 1) + i.  tr_lane_off gives the lane's element offset for
+// (r0, p) with k0 = 0; k0 adds k0 * D.
+template <int D>
+__device__ __forceinline__ int tr_lane_off(int lane, int r0, int p) {
+  constexpr int CH = D / 8;
+  const int g = lane >> 4, j = lane & 15;
+  const int d = r0 + 16 * (g & 1) + 4 * (j & 3);
+  const int q = 8 * (g >> 1) + 4 * p + (j >> 2);
+  return q * D + (((d >> 3) ^ (q & (CH - 1))) << 3) + (d & 7);
+}
+__device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t *blk, int off0, int off1) {
+  const s16x4 lo = lds_read_tr16(blk + off0), hi = lds_read_tr16(blk + off1);
+  const s16x4 v[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Row m of a 32-row C tile produced from A rows loaded in the order sigma:
 // sigma swaps bits 2 and 3, so C registers 8t..8t+7 of lane half h hold
 // A rows 16t + 8h + 0..7 (contiguous), ready to be a B operand.

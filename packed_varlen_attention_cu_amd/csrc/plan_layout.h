@@ -17,12 +17,6 @@ libra_status plan_header(const void *plan, libra_plan_info *out);
 
 namespace libra {
 
-// Bytes of a [heads][d][Lp] bf16 buffer, Lp = L rounded up to 64, padded to 256.
-size_t transposed_bytes(int64_t heads, int64_t d, int64_t L);
-
-// Enqueue src [L][H][D] -> dst [H][D][Lp] (tokens L..Lp-1 zero).
-libra_status launch_transpose(const void *src, void *dst, int L, int H, int D, void *stream);
-
 bool misaligned(const void *p, uintptr_t a);
 
 // Clear the calling thread's pending HIP error before a launch, so that the

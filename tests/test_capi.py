@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) >= 13
+    assert len(names) >= 11
     handle = ctypes.CDLL(lib.LIB_PATH)
     for n in names:
         assert hasattr(handle, n), n
@@ -173,7 +173,7 @@ def test_empty_pack_plans_and_runs_nothing():
                     tile_tokens=64, tile_heads=2)
     assert plan.info.n_tiles == 0 and plan.info.n_items == 0 and plan.info.n_kv_items == 0
     # L = 0: every entry point returns OK before touching any pointer or the device
-    lib.libra_attn_fwd(plan.host, None, None, None, None, None, None, None, 0.1, None, 0, None, None)
+    lib.libra_attn_fwd(plan.host, None, None, None, None, None, None, None, 0.1, None, None)
     lib.libra_attn_bwd(plan.host, None, None, None, None, None, None, None, None, None, None, None, 0.1,
                        None, 0, None, None)
 
@@ -186,25 +186,25 @@ def small_plan():
 
 
 def fwd_args(plan, **over):
-    ws = lib.libra_attn_fwd_workspace(plan.host)
     a = dict(plan_host=plan.host, plan_dev=FAKE, q=FAKE, k=FAKE, v=FAKE, cu=FAKE, o=FAKE, lse=FAKE,
-             scale=0.1, ws=FAKE, ws_bytes=ws, rec=None, stream=None)
+             scale=0.1, rec=None, stream=None)
     a.update(over)
     return a
 
 
 def call_fwd(a):
     return lib._lib.libra_attn_fwd(a["plan_host"].ctypes.data, a["plan_dev"], a["q"], a["k"], a["v"], a["cu"],
-                                   a["o"], a["lse"], a["scale"], a["ws"], a["ws_bytes"], a["rec"], a["stream"])
+                                   a["o"], a["lse"], a["scale"], a["rec"], a["stream"])
 
 
 @pytest.mark.parametrize("over,status", [
     ({"q": None}, lib.LIBRA_EINVAL), ({"k": None}, lib.LIBRA_EINVAL), ({"v": None}, lib.LIBRA_EINVAL),
     ({"o": None}, lib.LIBRA_EINVAL), ({"lse": None}, lib.LIBRA_EINVAL), ({"cu": None}, lib.LIBRA_EINVAL),
-    ({"plan_dev": None}, lib.LIBRA_EINVAL), ({"ws": None}, lib.LIBRA_EINVAL),
+    ({"plan_dev": None}, lib.LIBRA_EINVAL), ({"v": FAKE + 8}, lib.LIBRA_EINVAL),
     ({"q": FAKE + 8}, lib.LIBRA_EINVAL), ({"rec": FAKE + 4}, lib.LIBRA_EINVAL),
+    ({"lse": FAKE + 2}, lib.LIBRA_EINVAL),
     ({"scale": 0.0}, lib.LIBRA_EINVAL), ({"scale": float("nan")}, lib.LIBRA_EINVAL),
-    ({"scale": -1.0}, lib.LIBRA_EINVAL), ({"ws_bytes": 16}, lib.LIBRA_ESIZE),
+    ({"scale": -1.0}, lib.LIBRA_EINVAL),
 ])
 def test_fwd_validation(small_plan, over, status):
     assert call_fwd(fwd_args(small_plan, **over)) == status
@@ -218,18 +218,14 @@ def test_fwd_rejects_foreign_plan(small_plan):
 
 def test_phase_entry_points_validate(small_plan):
     h = small_plan.host.ctypes.data
-    fws = lib.libra_attn_fwd_workspace(small_plan.host)
     bws = lib.libra_attn_bwd_workspace(small_plan.host)
     L_ = lib._lib
-    assert L_.libra_attn_fwd_prepare(h, None, FAKE, fws, None) == lib.LIBRA_EINVAL
-    assert L_.libra_attn_fwd_prepare(h, FAKE, FAKE, fws - 1, None) == lib.LIBRA_ESIZE
-    assert L_.libra_attn_fwd_main(h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, 0, None, None) == lib.LIBRA_ESIZE
-    assert L_.libra_attn_fwd_main(h, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, fws, None, None) == lib.LIBRA_EINVAL
-    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, None, FAKE, FAKE, FAKE, bws, None) == lib.LIBRA_EINVAL
-    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE, None, FAKE, bws, None) == lib.LIBRA_EINVAL
-    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE, bws, None) == lib.LIBRA_EINVAL
-    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, bws, None) == lib.LIBRA_EINVAL
-    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, bws - 1, None) == lib.LIBRA_ESIZE
+    assert L_.libra_attn_bwd_prepare(h, None, FAKE, FAKE, FAKE, bws, None) == lib.LIBRA_EINVAL
+    assert L_.libra_attn_bwd_prepare(h, FAKE, None, FAKE, FAKE, bws, None) == lib.LIBRA_EINVAL
+    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, None, FAKE, bws, None) == lib.LIBRA_EINVAL
+    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE + 2, FAKE, bws, None) == lib.LIBRA_EINVAL
+    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE + 16, bws, None) == lib.LIBRA_EINVAL
+    assert L_.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE, bws - 1, None) == lib.LIBRA_ESIZE
     dkdv = [h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, bws, None, None]
     for i in (2, 3, 4, 5, 6, 7, 8, 9):           # q k v dout lse cu dk dv
         args = list(dkdv)
@@ -260,10 +256,8 @@ def test_bwd_validation(small_plan):
 
 
 def test_workspace_sizes(small_plan):
-    Lp = 128
-    assert lib.libra_attn_fwd_workspace(small_plan.host) == 2 * 128 * Lp * 2
-    # Q^T and dO^T (h_q), K^T (h_kv), D and LSE * log2(e) (fp32 [h_q][L] each)
-    assert lib.libra_attn_bwd_workspace(small_plan.host) == 2 * (4 * 128 * Lp * 2) + 2 * 128 * Lp * 2 + 2 * 2048
+    # D and LSE * log2(e): fp32 [h_q][L] each, 256-byte aligned (L = 128, h_q = 4)
+    assert lib.libra_attn_bwd_workspace(small_plan.host) == 2 * 2048
 
 
 def test_status_strings():

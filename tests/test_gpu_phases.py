@@ -1,4 +1,4 @@
-"""The phase entry points (prepare / main kernels) reproduce the one-call entry points bit for bit,
+"""The backward phase entry points reproduce the one-call entry point bit for bit,
 and the per-CU records account for every work item (needs an MI355X)."""
 import math
 
@@ -30,16 +30,13 @@ def test_phases_match_one_call_entry_points():
     plan_dev, cu_dev = plan.device(dev)
     sh = torch.cuda.current_stream(dev).cuda_stream
     ncu = plan.info.num_cus
-    fws = lib.libra_attn_fwd_workspace(plan.host)
     bws = lib.libra_attn_bwd_workspace(plan.host)
-    wf = torch.empty(fws, dtype=torch.uint8, device=dev)
     wb = torch.empty(bws, dtype=torch.uint8, device=dev)
     rec = torch.zeros(3 * ncu * 32, dtype=torch.uint8, device=dev)
     o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    lib.libra_attn_fwd_prepare(plan.host, v, wf, fws, sh)
-    lib.libra_attn_fwd_main(plan.host, plan_dev, q, k, cu_dev, o2, l2, scale, wf, fws, rec[:ncu * 32], sh)
-    lib.libra_attn_bwd_prepare(plan.host, q, k, o2, do, l2, wb, bws, sh)
+    lib.libra_attn_fwd(plan.host, plan_dev, q, k, v, cu_dev, o2, l2, scale, rec[:ncu * 32], sh)
+    lib.libra_attn_bwd_prepare(plan.host, o2, do, l2, wb, bws, sh)
     lib.libra_attn_bwd_dkdv(plan.host, plan_dev, q, k, v, do, l2, cu_dev, dk, dv, scale, wb, bws,
                             rec[ncu * 32:2 * ncu * 32], sh)
     lib.libra_attn_bwd_dq(plan.host, plan_dev, q, k, v, do, l2, cu_dev, dq, scale, wb, bws,
