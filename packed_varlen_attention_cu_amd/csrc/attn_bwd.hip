@@ -104,15 +104,14 @@ __device__ __forceinline__ void write_record(const BwdArgs &a, int w, int n, uin
 // reads) and the block's LSE * log2(e) and D values.  Two such buffers
 // alternate: after one barrier the copies for the next (head, query block)
 // step are queued into the other buffer, and the current one is computed
-// while they fly.  16-byte chunk c of row r sits at position c ^ (r mod
-// chunks-per-row), so the operand reads of a wave hit distinct banks.
+// while they fly.  Blocks use padded rows (PadRows).
 constexpr int kDkdvWaves = 8;
 
 template <int D>
 struct DkdvLds {
-  static constexpr int kRow = kQB * D;        // elements of a row-major block
-  static constexpr int kBuf = 2 * kRow + 2 * kQB * 2;   // Q, dO + LSE and D (fp32), in uint16 units
-  static constexpr int kP = 4 * 32 * kQB;     // bf16 P of the four key groups
+  static constexpr int kRow = kQB * PadRows<D>::kStride;   // elements of one padded block
+  static constexpr int kBuf = 2 * kRow + 2 * kQB * 2;      // Q, dO + LSE and D (fp32), in uint16 units
+  static constexpr int kP = 4 * 32 * kQB;                  // bf16 P of the four key groups
 };
 
 template <int D>
@@ -120,9 +119,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kDkdvWaves * 64, kDkdvWave
 void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NW = kDkdvWaves;
   constexpr int NS = D / 16, ND = D / 32;
-  constexpr int CH = D / 8;                        // 16-byte chunks per row-major row
-  constexpr int RJ = kQB * CH / 64 / NW;           // DMA instructions per wave, row-major block
-  static_assert(RJ * NW * 64 == kQB * CH, "copies split evenly");
   static_assert(2 * kQB <= NW * 16, "LSE and D copies: 16 values per wave");
   constexpr int ROW = DkdvLds<D>::kRow;
   __shared__ __attribute__((aligned(16))) uint16_t buf0[DkdvLds<D>::kBuf];
@@ -139,12 +135,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   const float c = a.scale_log2;
   const uint32_t bl0 = lds_addr(buf0), bl1 = lds_addr(buf1);
   u32x4 *p_mine = reinterpret_cast<u32x4 *>(p_lds + kg * 32 * kQB) + lane;   // [4 slabs][64 lanes]
-  int tro[ND][2];                                  // transposing-read offsets of dO^T / Q^T operands
-#pragma unroll
-  for (int dt = 0; dt < ND; ++dt) {
-    tro[dt][0] = tr_lane_off<D>(lane, dt * 32, 0);
-    tro[dt][1] = tr_lane_off<D>(lane, dt * 32, 1);
-  }
+  const int dlo = direct_lane_off<D>(lane);        // Q / dO operand reads
+  const int tlo = tr_lane_off<D>(lane);            // Q^T / dO^T operand reads
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -175,15 +167,9 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
     auto issue = [&](int i, uint32_t dst) {
       const int h = item.head0 + i / nqb;
       const int q0 = qstart + (i % nqb) * kQB;
-#pragma unroll
-      for (int j = 0; j < RJ; ++j) {
-        const int slot = (wave * RJ + j) * 64 + lane;
-        const int r = slot / CH, cc = (slot % CH) ^ (r & (CH - 1));
-        const int64_t g = ((int64_t)min(q0 + r, a.L - 1) * a.h_q + h) * D + cc * 8;   // rows past L are masked
-        const uint32_t off = (wave * RJ + j) * 1024;
-        lds_dma16(a.q + g, dst + off);
-        lds_dma16(a.dout + g, dst + 2 * ROW + off);     // byte offsets: a block is 2 * ROW bytes
-      }
+      auto row = [&](int r) { return ((int64_t)min(q0 + r, a.L - 1) * a.h_q + h) * D; };   // rows past L are masked
+      dma_rows<D, kQB, NW>(dst, wave, lane, [&](int r) { return a.q + row(r); });
+      dma_rows<D, kQB, NW>(dst + 2 * ROW, wave, lane, [&](int r) { return a.dout + row(r); });   // byte offsets
       // LSE * log2(e) then D of the block's queries: lanes 0..15 of each wave copy 16 values.
       if (lane < 16) {
         const int e = wave * 16 + lane;             // 0 .. 2 kQB - 1
@@ -208,19 +194,28 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
       const float *dd_l = lse_l + kQB;
 
       // First product: S (P wave, A = Q) or dP (dS wave, A = dO); C layout, lane = key.
+      // The two query tiles are independent accumulation chains; their A
+      // operands are read one slab ahead of use.
       f32x16 sacc[2];
       if (act) {
-        const uint16_t *a_l = pwave ? q_l : do_l;
+        const uint16_t *a_l = (pwave ? q_l : do_l) + dlo;
+        auto rd = [&](int qt, int s) {
+          return as_bf16x8(*reinterpret_cast<const u32x4 *>(a_l + direct_off<D>(qt, s)));
+        };
+        sacc[0] = zero16();
+        sacc[1] = zero16();
+        bf16x8 c0 = rd(0, 0), c1 = rd(1, 0);
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          sacc[qt] = zero16();
-          const int row = qt * 32 + sigma_row(col);
-#pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                a_l + row * D + (((2 * s + half) ^ (row & (CH - 1))) * 8)));
-            sacc[qt] = mfma32x32x16(av, bop[s], sacc[qt]);
+        for (int s = 0; s < NS; ++s) {
+          bf16x8 n0 = c0, n1 = c1;
+          if (s + 1 < NS) {
+            n0 = rd(0, s + 1);
+            n1 = rd(1, s + 1);
           }
+          sacc[0] = mfma32x32x16(c0, bop[s], sacc[0]);
+          sacc[1] = mfma32x32x16(c1, bop[s], sacc[1]);
+          c0 = n0;
+          c1 = n1;
         }
       }
       u32x4 pw[2][2];   // [query tile][16-query slab]: bf16 P (P wave) or dS (dS wave)
@@ -278,17 +273,18 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
       // Second product: dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave); the
       // transposed A operands are read from the row-major dO / Q blocks.
       if (act) {
-        const uint16_t *t_l = pwave ? do_l : q_l;
+        const uint16_t *t_l = (pwave ? do_l : q_l) + tlo;
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
+        for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt)
+          for (int t = 0; t < 2; ++t) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const uint16_t *slab = t_l + (qt * 32 + 16 * t) * D;
-              const bf16x8 av = lds_tr_operand(slab, tro[dt][0], tro[dt][1]);
+            for (int dt = 0; dt < ND; ++dt) {   // ND independent accumulators in a row
+              const bf16x8 av = lds_tr_operand(t_l + tr_off<D>(qt * 32 + 16 * t, dt * 32, 0),
+                                               t_l + tr_off<D>(qt * 32 + 16 * t, dt * 32, 1));
               acc[dt] = mfma32x32x16(av, as_bf16x8(pw[qt][t]), acc[dt]);
             }
+          }
       }
     };
 
@@ -331,10 +327,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kDqWaves * 64, kDqWaves * 
 void attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = kDqWaves;
   constexpr int NS = D / 16, ND = D / 32;
-  constexpr int CH = D / 8;
-  constexpr int RJ = kKB * CH / 64 / NW;           // DMA instructions per wave, K or V block
-  static_assert(RJ * NW * 64 == kKB * CH, "copies split evenly");
-  constexpr int BLK = kKB * D;                     // elements of one block
+  constexpr int BLK = kKB * PadRows<D>::kStride;   // elements of one padded block
   __shared__ __attribute__((aligned(16))) uint16_t buf0[2 * BLK];
   __shared__ __attribute__((aligned(16))) uint16_t buf1[2 * BLK];
 
@@ -345,12 +338,8 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const int beg = a.cu_off[w], end = a.cu_off[w + 1];
   const float c = a.scale_log2;
   const uint32_t bl0 = lds_addr(buf0), bl1 = lds_addr(buf1);
-  int tro[ND][2];                                  // transposing-read offsets of K^T operands
-#pragma unroll
-  for (int dt = 0; dt < ND; ++dt) {
-    tro[dt][0] = tr_lane_off<D>(lane, dt * 32, 0);
-    tro[dt][1] = tr_lane_off<D>(lane, dt * 32, 1);
-  }
+  const int dlo = direct_lane_off<D>(lane);        // K / V operand reads
+  const int tlo = tr_lane_off<D>(lane);            // K^T operand reads
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -381,15 +370,9 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     for (int dt = 0; dt < ND; ++dt) dqacc[dt] = zero16();
 
     auto issue = [&](int k0, uint32_t dst) {
-#pragma unroll
-      for (int j = 0; j < RJ; ++j) {
-        const int slot = (wave * RJ + j) * 64 + lane;
-        const int rr = slot / CH, cc = (slot % CH) ^ (rr & (CH - 1));
-        const int64_t g = ((int64_t)min(k0 + rr, a.L - 1) * a.h_kv + kvh) * D + cc * 8;   // rows past L are masked
-        const uint32_t off = (wave * RJ + j) * 1024;
-        lds_dma16(a.k + g, dst + off);
-        lds_dma16(a.v + g, dst + 2 * BLK + off);     // byte offsets: a block is 2 * BLK bytes
-      }
+      auto row = [&](int rr) { return ((int64_t)min(k0 + rr, a.L - 1) * a.h_kv + kvh) * D; };   // rows past L are masked
+      dma_rows<D, kKB, NW>(dst, wave, lane, [&](int rr) { return a.k + row(rr); });
+      dma_rows<D, kKB, NW>(dst + 2 * BLK, wave, lane, [&](int rr) { return a.v + row(rr); });   // byte offsets
     };
 
     auto block = [&](int b, auto bufc) {
@@ -409,10 +392,9 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int kt = 0; kt < kKB / 32; ++kt) {
           f32x16 sacc = zero16(), pacc = zero16();   // S^T and dP^T (lane = query)
-          const int row = kt * 32 + sigma_row(col);
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
-            const int off = row * D + (((2 * s + half) ^ (row & (CH - 1))) * 8);
+            const int off = dlo + direct_off<D>(kt, s);
             const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(k_l + off));
             const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(v_l + off));
             sacc = mfma32x32x16(ka, qop[s], sacc);
@@ -443,8 +425,8 @@ void attn_bwd_dq_kernel(BwdArgs a) {
           for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {   // K^T operand read transposed from the row-major K block
-              const uint16_t *slab = k_l + (kt * 32 + 16 * t) * D;
-              const bf16x8 ka = lds_tr_operand(slab, tro[dt][0], tro[dt][1]);
+              const bf16x8 ka = lds_tr_operand(k_l + tlo + tr_off<D>(kt * 32 + 16 * t, dt * 32, 0),
+                                               k_l + tlo + tr_off<D>(kt * 32 + 16 * t, dt * 32, 1));
               dqacc[dt] = mfma32x32x16(ka, as_bf16x8(dsw[t]), dqacc[dt]);
             }
         }

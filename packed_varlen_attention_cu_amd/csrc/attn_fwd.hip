@@ -69,18 +69,13 @@ void attn_fwd_kernel(FwdArgs a) {
   constexpr int QW = 32 * QT;                   // query positions per wave
   constexpr int NS = D / 16;                    // reduction slabs of d
   constexpr int ND = D / 32;                    // 32-row tiles of d in O^T
-  constexpr int CH = D / 8;                     // 16-byte chunks per K row
-  constexpr int KJ = kBN * CH / 64 / NW;        // LDS-DMA instructions per wave, K or V block
-  static_assert(KJ >= 1 && KJ * NW * 64 == kBN * CH, "the waves split each block copy evenly");
-  // Two buffers of K and V [kBN][D], rows unpadded; 16-byte chunk c of row r
-  // sits at position c ^ (r mod chunks-per-row) so operand reads hit distinct
-  // banks.  The V^T operands of O^T = V^T P^T come from transposing reads.
-  // Distinct arrays per buffer let the compiler see that a copy in flight into
-  // one buffer cannot alias reads of the other, so it adds no waits for it.
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds1[kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[D * kBN];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[D * kBN];
+  constexpr int RS = PadRows<D>::kStride;
+  // Two buffers of K and V [kBN][D] in padded rows.  The V^T operands of
+  // O^T = V^T P^T come from transposing reads of the V block.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[kBN * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds1[kBN * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[kBN * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[kBN * RS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int half = lane >> 5, col = lane & 31;
@@ -92,12 +87,8 @@ void attn_fwd_kernel(FwdArgs a) {
   const uint32_t vl0 = lds_addr(v_lds0), vl1 = lds_addr(v_lds1);
   const float NEG_INF = -__builtin_inff();
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  int tro[ND][2];                               // transposing-read offsets of V^T operands
-#pragma unroll
-  for (int dt = 0; dt < ND; ++dt) {
-    tro[dt][0] = tr_lane_off<D>(lane, dt * 32, 0);
-    tro[dt][1] = tr_lane_off<D>(lane, dt * 32, 1);
-  }
+  const int dlo = direct_lane_off<D>(lane);     // K operand reads
+  const int tlo = tr_lane_off<D>(lane);         // V^T operand reads
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -137,19 +128,14 @@ void attn_fwd_kernel(FwdArgs a) {
       l_run[qt] = 0.0f;
     }
 
-    // Queue the K and V blocks at key k0 into LDS buffer BUF (no registers).
+    // Queue the K and V blocks at key k0 into LDS buffer BUF (no registers);
+    // rows past L are masked, so their addresses are clamped to row L - 1.
     auto issue = [&](int k0, auto bufc) {
       const uint32_t kdst = decltype(bufc)::value == 0 ? kl0 : kl1;
       const uint32_t vdst = decltype(bufc)::value == 0 ? vl0 : vl1;
-#pragma unroll
-      for (int j = 0; j < KJ; ++j) {
-        const int slot = (wave * KJ + j) * 64 + lane;
-        const int r = slot / CH, c = (slot % CH) ^ (r & (CH - 1));
-        const int key = min(k0 + r, a.L - 1);     // rows past L are masked; keep the address valid
-        const int64_t g = ((int64_t)key * a.h_kv + kvh) * D + c * 8;
-        lds_dma16(a.k + g, kdst + (wave * KJ + j) * 1024);
-        lds_dma16(a.v + g, vdst + (wave * KJ + j) * 1024);
-      }
+      auto row = [&](int r) { return ((int64_t)min(k0 + r, a.L - 1) * a.h_kv + kvh) * D; };
+      dma_rows<D, kBN, NW>(kdst, wave, lane, [&](int r) { return a.k + row(r); });
+      dma_rows<D, kBN, NW>(vdst, wave, lane, [&](int r) { return a.v + row(r); });
     };
 
     // One key block.  After this wave's copies of block b have landed and its
@@ -182,9 +168,7 @@ void attn_fwd_kernel(FwdArgs a) {
           for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = zero16();
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
-            const int row = kt * 32 + sigma_row(col);
-            const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                kb + row * D + (((2 * s + half) ^ (row & (CH - 1))) * 8)));
+            const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(kb + dlo + direct_off<D>(kt, s)));
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = mfma32x32x16(ka, qop[qt][s], sacc[kt][qt]);
           }
@@ -254,7 +238,8 @@ void attn_fwd_kernel(FwdArgs a) {
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-              const bf16x8 va = lds_tr_operand(vb + (kt * 32 + 16 * t) * D, tro[dt][0], tro[dt][1]);
+              const bf16x8 va = lds_tr_operand(vb + tlo + tr_off<D>(kt * 32 + 16 * t, dt * 32, 0),
+                                               vb + tlo + tr_off<D>(kt * 32 + 16 * t, dt * 32, 1));
 #pragma unroll
               for (int qt = 0; qt < QT; ++qt)
                 oacc[qt][dt] = mfma32x32x16(va, as_bf16x8(pw[qt][kt][t]), oacc[qt][dt]);

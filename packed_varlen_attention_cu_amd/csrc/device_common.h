@@ -143,6 +143,13 @@ __device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0
 // for the next block stay in flight across the barrier.
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Row m of a 32-row C tile produced from A rows loaded in the order sigma:
+// sigma swaps bits 2 and 3, so C registers 8t..8t+7 of lane half h hold
+// A rows 16t + 8h + 0..7 (contiguous), ready to be a B operand.
+__device__ __forceinline__ int sigma_row(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane j supplies the address of four consecutive 16-bit values M[j][0..3];
 // lane 4a + b receives M[a][b], M[a + 4][b], M[a + 8][b], M[a + 12][b].
@@ -152,34 +159,69 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
       (__attribute__((address_space(3))) s16x4 *)(const __attribute__((address_space(3))) void *)p);
 }
 
-// MFMA A operand of Mat^T from a row-major bf16 block Mat [rows][D] in LDS
-// whose 16-byte chunk c of row r sits at position c ^ (r mod D/8): lane
-// (col, half) receives Mat[k0 + 8 half + i][r0 + col], i = 0..7, for a
-// multiple of 32 r0 and a multiple of 16 k0.  Lane j of 16-lane group g
-// addresses row k0 + 8 (g >> 1) + 4 p + j / 4, columns r0 + 16 (g & 1) +
-// 4 (j % 4) + 0..3, for the two reads p = 0, 1; by the rule above the
-// group's lane i then holds rows k0 + 8 (g >> 1) + 4 p + 0..3 of column
-// r0 + 16 (g & 1) + i.  tr_lane_off gives the lane's element offset for
-// (r0, p) with k0 = 0; k0 adds k0 * D.
+// Row-major bf16 blocks of D columns live in LDS with a padded row stride:
+// 152 elements (304 bytes) for D = 128, 72 (144 bytes) for D = 64.  With 64
+// four-byte banks, the stride moves consecutive rows by 12 (resp. 36) banks,
+// so 16 rows read at one column (the direct operand reads below) and the
+// 4 x 4 pieces of a transposing read both fall on distinct banks, and every
+// operand address is a per-lane base plus a compile-time offset.
 template <int D>
-__device__ __forceinline__ int tr_lane_off(int lane, int r0, int p) {
-  constexpr int CH = D / 8;
-  const int g = lane >> 4, j = lane & 15;
-  const int d = r0 + 16 * (g & 1) + 4 * (j & 3);
-  const int q = 8 * (g >> 1) + 4 * p + (j >> 2);
-  return q * D + (((d >> 3) ^ (q & (CH - 1))) << 3) + (d & 7);
+struct PadRows {
+  static constexpr int kStride = D == 128 ? 152 : 72;   // elements per row
+  static_assert(D == 128 || D == 64, "head_dim 64 or 128");
+  // LDS-DMA instructions (1 KB each) that fill nr rows.
+  static constexpr int copies(int nr) { return (nr * kStride * 2 + 1023) / 1024; }
+};
+
+// Copy rows 0..NR-1 of a block into LDS at byte address lds (padded rows).
+// row_src(r) is the global address of row r (16-byte aligned, D elements).
+// Instruction i of the copy is issued by wave i mod NW; lanes whose 16-byte
+// slot falls into a row's padding are switched off.
+template <int D, int NR, int NW, typename RowSrc>
+__device__ __forceinline__ void dma_rows(uint32_t lds, int wave, int lane, RowSrc row_src) {
+  constexpr int RS = PadRows<D>::kStride;
+  constexpr int NI = PadRows<D>::copies(NR);
+#pragma unroll
+  for (int j = 0; j < (NI + NW - 1) / NW; ++j) {
+    const int i = wave + j * NW;
+    if (i < NI) {
+      const int e = 512 * i + 8 * lane;      // element offset of this lane's slot
+      const int r = e / RS, c = e - r * RS;
+      if (c < D && r < NR) lds_dma16(row_src(r) + c, lds + 1024 * i);
+    }
+  }
 }
-__device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t *blk, int off0, int off1) {
-  const s16x4 lo = lds_read_tr16(blk + off0), hi = lds_read_tr16(blk + off1);
+
+// Direct A operand: lane (col, half) reads row sigma_row(col) + 32 t of the
+// block, reduction elements 16 s + 8 half .. + 7.  direct_lane_off is the
+// lane's part; slab (t, s) adds direct_off(t, s).
+template <int D>
+__device__ __forceinline__ int direct_lane_off(int lane) {
+  return sigma_row(lane & 31) * PadRows<D>::kStride + 8 * (lane >> 5);
+}
+template <int D>
+constexpr int direct_off(int t, int s) { return 32 * t * PadRows<D>::kStride + 16 * s; }
+
+// MFMA A operand of Mat^T from a row-major padded block Mat [rows][D] in LDS:
+// lane (col, half) receives Mat[k0 + 8 half + i][r0 + col], i = 0..7.  Lane j
+// of 16-lane group g addresses row k0 + 8 (g >> 1) + 4 p + j / 4, columns
+// r0 + 16 (g & 1) + 4 (j % 4) + 0..3, for the two reads p = 0, 1; by the rule
+// of the transposing read the group's lane i then holds rows
+// k0 + 8 (g >> 1) + 4 p + 0..3 of column r0 + 16 (g & 1) + i.  tr_lane_off is
+// the lane's part; (k0, r0, p) add tr_off(k0, r0, p).
+template <int D>
+__device__ __forceinline__ int tr_lane_off(int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  return (8 * (g >> 1) + (j >> 2)) * PadRows<D>::kStride + 16 * (g & 1) + 4 * (j & 3);
+}
+template <int D>
+constexpr int tr_off(int k0, int r0, int p) { return (k0 + 4 * p) * PadRows<D>::kStride + r0; }
+
+__device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t *lo_p, const uint16_t *hi_p) {
+  const s16x4 lo = lds_read_tr16(lo_p), hi = lds_read_tr16(hi_p);
   const s16x4 v[2] = {lo, hi};
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Row m of a 32-row C tile produced from A rows loaded in the order sigma:
-// sigma swaps bits 2 and 3, so C registers 8t..8t+7 of lane half h hold
-// A rows 16t + 8h + 0..7 (contiguous), ready to be a B operand.
-__device__ __forceinline__ int sigma_row(int m) {
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
 
 }  // namespace libra
