@@ -86,31 +86,57 @@ struct Queue {
 };
 
 // Algorithm 2 with a zero communication term (or round-robin), emitted as CSR.
-Queue place(std::vector<libra_item> units, int workers, float tau, int mode) {
-  (void)tau;  // the soft target cannot change the choice when dcomm == 0
+// Units are taken heaviest first (ties: lower enumeration index) and each goes
+// to the worker of least (load, worker id), kept in a binary min-heap.
+struct Load {
+  int64_t load;
+  int32_t worker;
+};
+inline bool lighter(const Load &x, const Load &y) {
+  return x.load != y.load ? x.load < y.load : x.worker < y.worker;
+}
+
+Queue place(const std::vector<libra_item> &units, int workers, int mode) {
   Queue q;
   const size_t n = units.size();
   std::vector<int32_t> worker(n);
   std::vector<int32_t> order(n);
-  for (size_t i = 0; i < n; ++i) order[i] = (int32_t)i;
   std::vector<int64_t> load(workers, 0);
   if (mode == LIBRA_ASSIGN_PLACER) {
-    std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
-      return units[a].cost != units[b].cost ? units[a].cost > units[b].cost : a < b;
+    struct Key {
+      int64_t cost;
+      int32_t idx;
+    };
+    std::vector<Key> keys(n);
+    for (size_t i = 0; i < n; ++i) keys[i] = {units[i].cost, (int32_t)i};
+    std::sort(keys.begin(), keys.end(), [](const Key &x, const Key &y) {
+      return x.cost != y.cost ? x.cost > y.cost : x.idx < y.idx;
     });
-    using Entry = std::pair<int64_t, int32_t>;  // (load, worker)
-    std::priority_queue<Entry, std::vector<Entry>, std::greater<Entry>> heap;
-    for (int32_t r = 0; r < workers; ++r) heap.push({0, r});
-    for (int32_t t : order) {
-      Entry e = heap.top();
-      heap.pop();
-      worker[t] = e.second;
-      e.first += units[t].cost;
-      load[e.second] = e.first;
-      heap.push(e);
+    std::vector<Load> heap(workers);
+    for (int32_t r = 0; r < workers; ++r) heap[r] = {0, r};   // ordered, hence a valid heap
+    for (size_t k = 0; k < n; ++k) {
+      const int32_t t = keys[k].idx;
+      order[k] = t;
+      Load top = heap[0];
+      worker[t] = top.worker;
+      top.load += keys[k].cost;
+      load[top.worker] = top.load;
+      size_t i = 0;                                            // sift the grown root down
+      for (;;) {
+        const size_t l = 2 * i + 1, r = l + 1;
+        size_t m = i;
+        const Load *best = &top;
+        if (l < heap.size() && lighter(heap[l], *best)) { m = l; best = &heap[l]; }
+        if (r < heap.size() && lighter(heap[r], *best)) { m = r; best = &heap[r]; }
+        if (m == i) break;
+        heap[i] = heap[m];
+        i = m;
+      }
+      heap[i] = top;
     }
   } else {
     for (size_t t = 0; t < n; ++t) {
+      order[t] = (int32_t)t;
       worker[t] = (int32_t)(t % workers);
       load[worker[t]] += units[t].cost;
     }
@@ -129,6 +155,29 @@ Queue place(std::vector<libra_item> units, int workers, float tau, int mode) {
 }
 
 size_t align64(size_t x) { return (x + 63) & ~size_t(63); }
+
+// Byte offsets of the plan sections (written into hdr when it is not null)
+// and the total size: header, tiles, items, cu_off, kv items, kv cu_off.
+size_t section_offsets(size_t n_tiles, size_t n_items, size_t n_kv, int workers, libra_plan_info *hdr) {
+  libra_plan_info tmp{};
+  libra_plan_info &h = hdr ? *hdr : tmp;
+  size_t off = align64(sizeof(libra_plan_info));
+  h.off_tiles = off;
+  off = align64(off + n_tiles * sizeof(libra_tile));
+  h.off_items = off;
+  off = align64(off + n_items * sizeof(libra_item));
+  h.off_cu_off = off;
+  off = align64(off + (workers + 1) * sizeof(int32_t));
+  h.off_kv_items = off;
+  off = align64(off + n_kv * sizeof(libra_item));
+  h.off_kv_cu_off = off;
+  off = align64(off + (workers + 1) * sizeof(int32_t));
+  return off;
+}
+
+size_t plan_bytes(int64_t n_tiles, int64_t n_items, int64_t n_kv, int workers) {
+  return section_offsets((size_t)n_tiles, (size_t)n_items, (size_t)n_kv, workers, nullptr);
+}
 
 uint64_t fnv1a_words(const void *buf, size_t bytes) {
   const uint64_t *w = static_cast<const uint64_t *>(buf);
@@ -175,6 +224,25 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
   const int g = p.h_q / p.h_kv;
   const int S = p.h_q / p.tile_heads;
   const int64_t nblocks = (L + p.tile_tokens - 1) / p.tile_tokens;
+
+  // Size query: the section lengths follow from the counts alone.
+  if (!buf) {
+    int64_t n_items = 0;
+    for (int64_t b = 0; b < nblocks; ++b) {
+      const int64_t rows_in = std::min<int64_t>(L, (b + 1) * p.tile_tokens) - b * p.tile_tokens;
+      for (int s = 0; s < S; ++s) {
+        const int h_lo = s * p.tile_heads, h_hi = h_lo + p.tile_heads;
+        for (int kv = h_lo / g; kv <= (h_hi - 1) / g; ++kv) {
+          const int hn = std::min(h_hi, (kv + 1) * g) - std::max(h_lo, kv * g);
+          const int nh = head_group(hn), rows = kItemColumns / nh;
+          n_items += (int64_t)(hn / nh) * ((rows_in + rows - 1) / rows);
+        }
+      }
+    }
+    const int64_t n_kv = (L + kKvChunk - 1) / kKvChunk * p.h_kv;
+    *bytes = plan_bytes(nblocks * S, n_items, n_kv, workers);
+    return LIBRA_OK;
+  }
 
   // Tiles (eq. 6-8) and forward items.
   std::vector<libra_tile> tiles;
@@ -256,8 +324,8 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
     }
   }
 
-  Queue fq = place(items, workers, p.tau, p.assign);
-  Queue kq = place(kv_items, workers, p.tau, p.assign);
+  Queue fq = place(items, workers, p.assign);
+  Queue kq = place(kv_items, workers, p.assign);
 
   libra_plan_info hdr{};
   hdr.magic = LIBRA_PLAN_MAGIC;
@@ -272,23 +340,9 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
   hdr.load_sum = fq.load_sum;
   hdr.kv_load_max = kq.load_max;
   hdr.kv_load_sum = kq.load_sum;
-  size_t off = align64(sizeof(libra_plan_info));
-  hdr.off_tiles = off;
-  off = align64(off + tiles.size() * sizeof(libra_tile));
-  hdr.off_items = off;
-  off = align64(off + fq.items.size() * sizeof(libra_item));
-  hdr.off_cu_off = off;
-  off = align64(off + fq.cu_off.size() * sizeof(int32_t));
-  hdr.off_kv_items = off;
-  off = align64(off + kq.items.size() * sizeof(libra_item));
-  hdr.off_kv_cu_off = off;
-  off = align64(off + kq.cu_off.size() * sizeof(int32_t));
+  const size_t off = section_offsets(tiles.size(), fq.items.size(), kq.items.size(), workers, &hdr);
   hdr.bytes = off;
 
-  if (!buf) {
-    *bytes = off;
-    return LIBRA_OK;
-  }
   if (*bytes < off || (reinterpret_cast<uintptr_t>(buf) & 7)) {
     *bytes = off;
     return (reinterpret_cast<uintptr_t>(buf) & 7) ? LIBRA_EINVAL : LIBRA_ESIZE;
