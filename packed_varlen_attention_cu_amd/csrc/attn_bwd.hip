@@ -127,7 +127,6 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int half = lane >> 5, col = lane & 31;
-  const bool pwave = wave < 4;                     // wave-uniform role
   const int kg = wave & 3;                         // key group
   const int w = blockIdx.x;
   const uint64_t t_start = wall_clock64();
@@ -137,179 +136,203 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   u32x4 *p_mine = reinterpret_cast<u32x4 *>(p_lds + kg * 32 * kQB) + lane;   // [4 slabs][64 lanes]
   const int dlo = direct_lane_off<D>(lane);        // Q / dO operand reads
   const int tlo = tr_lane_off<D>(lane);            // Q^T / dO^T operand reads
+  const int64_t q_stride = (int64_t)a.h_q * D;
+  RowCopy<D, kQB, NW> qcopy;
+  qcopy.init(wave, lane, q_stride);
 
-  for (int it = beg; it < end; ++it) {
-    const libra_item item = a.items[it];
-    const int row0 = item.row0, nrows = item.nrows, kvh = item.kv_head;
-    const int kloc = kg * 32 + col;
-    const bool kok = kloc < nrows;
-    const int key = row0 + kloc;
-    const int kend = kok ? segment_end(a.cu, a.n_samples, key) : 0;   // queries [key, kend)
+  // The two roles are separate instantiations, so each allocates registers
+  // for its own path only; both pass the same barriers.
+  auto run = [&](auto role) {
+    constexpr bool pwave = decltype(role)::value;
+    for (int it = beg; it < end; ++it) {
+      const libra_item item = a.items[it];
+      const int row0 = item.row0, nrows = item.nrows, kvh = item.kv_head;
+      const int kloc = kg * 32 + col;
+      const bool kok = kloc < nrows;
+      const int key = row0 + kloc;
+      const int kend = kok ? segment_end(a.cu, a.n_samples, key) : 0;   // queries [key, kend)
 
-    // B operand of this wave's first product: K (P wave) or V (dS wave).
-    bf16x8 bop[NS];
-    {
-      const uint16_t *src = (pwave ? a.k : a.v) + ((int64_t)key * a.h_kv + kvh) * D + 8 * half;
+      // B operand of this wave's first product: K (P wave) or V (dS wave).
+      bf16x8 bop[NS];
+      {
+        const uint16_t *src = (pwave ? a.k : a.v) + ((int64_t)key * a.h_kv + kvh) * D + 8 * half;
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-        bop[s] = as_bf16x8(kok ? *reinterpret_cast<const u32x4 *>(src + 16 * s) : zero_u32x4());
-    }
-    const int qstart = row0 & ~(kQB - 1);
-    const int qend = segment_end(a.cu, a.n_samples, row0 + nrows - 1);
-    const int nqb = (qend - qstart + kQB - 1) / kQB;
-    const int nsteps = nqb * item.nheads;
-
-    f32x16 acc[ND];   // dV^T (P wave) or dK^T (dS wave), one key column per lane
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) acc[dt] = zero16();
-
-    // Queue the copies of step i (head head0 + i / nqb, query block i % nqb).
-    auto issue = [&](int i, uint32_t dst) {
-      const int h = item.head0 + i / nqb;
-      const int q0 = qstart + (i % nqb) * kQB;
-      auto row = [&](int r) { return ((int64_t)min(q0 + r, a.L - 1) * a.h_q + h) * D; };   // rows past L are masked
-      dma_rows<D, kQB, NW>(dst, wave, lane, [&](int r) { return a.q + row(r); });
-      dma_rows<D, kQB, NW>(dst + 2 * ROW, wave, lane, [&](int r) { return a.dout + row(r); });   // byte offsets
-      // LSE * log2(e) then D of the block's queries: lanes 0..15 of each wave copy 16 values.
-      if (lane < 16) {
-        const int e = wave * 16 + lane;             // 0 .. 2 kQB - 1
-        const int qq = min(q0 + (e & (kQB - 1)), a.L - 1);
-        const float *src = (e < kQB ? a.lse2 : a.dvec) + (int64_t)h * a.L + qq;
-        lds_dma4(src, dst + 4 * ROW + wave * 64);
+        for (int s = 0; s < NS; ++s)
+          bop[s] = as_bf16x8(kok ? *reinterpret_cast<const u32x4 *>(src + 16 * s) : zero_u32x4());
       }
-    };
+      const int qstart = row0 & ~(kQB - 1);
+      const int qend = segment_end(a.cu, a.n_samples, row0 + nrows - 1);
+      const int nqb = (qend - qstart + kQB - 1) / kQB;
+      const int nsteps = nqb * item.nheads;
 
-    auto step = [&](int i, auto bufc) {
-      constexpr int BUF = decltype(bufc)::value;
-      const uint16_t *bq = BUF == 0 ? buf0 : buf1;
-      wait_vmem_lds();              // own copies of step i landed, own LDS accesses of step i - 1 done
-      block_barrier();
-      if (i + 1 < nsteps) issue(i + 1, BUF == 0 ? bl1 : bl0);
-      const int q0 = qstart + (i % nqb) * kQB;
-      const bool touch = kok && (q0 + kQB - 1 >= key) && (q0 < kend);
-      const bool full = !kok || ((key <= q0) && (q0 + kQB - 1 < kend));
-      const bool act = wave_any(touch);     // identical for the two waves of a key group
-      const uint16_t *q_l = bq, *do_l = bq + ROW;
-      const float *lse_l = reinterpret_cast<const float *>(bq + 2 * ROW);
-      const float *dd_l = lse_l + kQB;
+      f32x16 acc[ND];   // dV^T (P wave) or dK^T (dS wave), one key column per lane
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) acc[dt] = zero16();
 
-      // First product: S (P wave, A = Q) or dP (dS wave, A = dO); C layout, lane = key.
-      // The two query tiles are independent accumulation chains; their A
-      // operands are read one slab ahead of use.
-      f32x16 sacc[2];
-      if (act) {
-        const uint16_t *a_l = (pwave ? q_l : do_l) + dlo;
-        auto rd = [&](int qt, int s) {
-          return as_bf16x8(*reinterpret_cast<const u32x4 *>(a_l + direct_off<D>(qt, s)));
-        };
-        sacc[0] = zero16();
-        sacc[1] = zero16();
-        bf16x8 c0 = rd(0, 0), c1 = rd(1, 0);
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          bf16x8 n0 = c0, n1 = c1;
-          if (s + 1 < NS) {
-            n0 = rd(0, s + 1);
-            n1 = rd(1, s + 1);
-          }
-          sacc[0] = mfma32x32x16(c0, bop[s], sacc[0]);
-          sacc[1] = mfma32x32x16(c1, bop[s], sacc[1]);
-          c0 = n0;
-          c1 = n1;
+      // Queue the copies of the step at (head h, query block q0); rows past L
+      // are masked, so their addresses are clamped to row L - 1.
+      auto issue = [&](int h, int q0, uint32_t dst) {
+        qcopy.issue(dst, wave, a.q + h * D, q_stride, q0, a.L);
+        qcopy.issue(dst + 2 * ROW, wave, a.dout + h * D, q_stride, q0, a.L);   // byte offsets
+        // LSE * log2(e) then D of the block's queries: lanes 0..15 of each wave copy 16 values.
+        if (lane < 16) {
+          const int e = wave * 16 + lane;             // 0 .. 2 kQB - 1
+          const int qq = min(q0 + (e & (kQB - 1)), a.L - 1);
+          const float *src = (e < kQB ? a.lse2 : a.dvec) + (int64_t)h * a.L + qq;
+          lds_dma4(src, dst + 4 * ROW + wave * 64);
         }
-      }
-      u32x4 pw[2][2];   // [query tile][16-query slab]: bf16 P (P wave) or dS (dS wave)
-      if (pwave) {
-        if (act) {
-          if (wave_any(!full)) {      // rare: blocks on a sample start or the diagonal
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int qq = q0 + qt * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
-                if (!(kok && key <= qq && qq < kend)) sacc[qt][r] = -__builtin_inff();
-              }
-          }
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const int ql = qt * 32 + 16 * t + 8 * half;   // first of 8 consecutive queries
-              const float4 l0 = *reinterpret_cast<const float4 *>(lse_l + ql);
-              const float4 l1 = *reinterpret_cast<const float4 *>(lse_l + ql + 4);
-              const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float p0 = exp2_fast(fmaf(sacc[qt][8 * t + 2 * e], c, -lv[2 * e]));   // masked: 0
-                const float p1 = exp2_fast(fmaf(sacc[qt][8 * t + 2 * e + 1], c, -lv[2 * e + 1]));
-                pw[qt][t][e] = pack_bf16x2(p0, p1);
-              }
-              p_mine[(qt * 2 + t) * 64] = pw[qt][t];
-            }
+      };
+
+      // Steps run over (head, query block) in order; (nh, nq0) is the next one.
+      int nh = item.head0, nq0 = qstart;
+      auto advance = [&]() {
+        nq0 += kQB;
+        if (nq0 >= qstart + nqb * kQB) {
+          nq0 = qstart;
+          ++nh;
         }
-        wait_lds();
-        block_barrier();              // P of every key group is in LDS
-      } else {
+      };
+      auto step = [&](int i, auto bufc) {
+        constexpr int BUF = decltype(bufc)::value;
+        const uint16_t *bq = BUF == 0 ? buf0 : buf1;
+        const int q0 = nq0;
+        advance();
+        wait_vmem_lds();              // own copies of step i landed, own LDS accesses of step i - 1 done
         block_barrier();
-        if (act) {
+        if (i + 1 < nsteps) issue(nh, nq0, BUF == 0 ? bl1 : bl0);
+        const bool touch = kok && (q0 + kQB - 1 >= key) && (q0 < kend);
+        const bool full = !kok || ((key <= q0) && (q0 + kQB - 1 < kend));
+        const bool act = wave_any(touch);     // identical for the two waves of a key group
+        const bool masked = wave_any(!full);
+        const uint16_t *q_l = bq, *do_l = bq + ROW;
+        const float *lse_l = reinterpret_cast<const float *>(bq + 2 * ROW);
+        const float *dd_l = lse_l + kQB;
+
+        // First product of query tile qt: S (P wave, A = Q) or dP (dS wave, A = dO).
+        auto first = [&](int qt) {
+          const uint16_t *a_l = (pwave ? q_l : do_l) + dlo;
+          f32x16 out = zero16();
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt)
+          for (int s = 0; s < NS; ++s)
+            out = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4 *>(a_l + direct_off<D>(qt, s))),
+                               bop[s], out);
+          return out;
+        };
+        // Second product of query tile qt: acc += (dO or Q)^T x w, transposed reads.
+        auto second = [&](int qt, const u32x4 (&wv)[2]) {
+          const uint16_t *t_l = (pwave ? do_l : q_l) + tlo;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const int ql = qt * 32 + 16 * t + 8 * half;
-              const float4 d0 = *reinterpret_cast<const float4 *>(dd_l + ql);
-              const float4 d1 = *reinterpret_cast<const float4 *>(dd_l + ql + 4);
-              const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-              const u32x4 pv = p_mine[(qt * 2 + t) * 64];
+          for (int t = 0; t < 2; ++t)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float ds0 = bf16_lo(pv[e]) * (sacc[qt][8 * t + 2 * e] - dv8[2 * e]);
-                const float ds1 = bf16_hi(pv[e]) * (sacc[qt][8 * t + 2 * e + 1] - dv8[2 * e + 1]);
-                pw[qt][t][e] = pack_bf16x2(ds0, ds1);
-              }
-            }
-        }
-      }
-      // Second product: dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave); the
-      // transposed A operands are read from the row-major dO / Q blocks.
-      if (act) {
-        const uint16_t *t_l = (pwave ? do_l : q_l) + tlo;
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int dt = 0; dt < ND; ++dt) {   // ND independent accumulators in a row
+            for (int dt = 0; dt < ND; ++dt) {
               const bf16x8 av = lds_tr_operand(t_l + tr_off<D>(qt * 32 + 16 * t, dt * 32, 0),
                                                t_l + tr_off<D>(qt * 32 + 16 * t, dt * 32, 1));
-              acc[dt] = mfma32x32x16(av, as_bf16x8(pw[qt][t]), acc[dt]);
+              acc[dt] = mfma32x32x16(av, as_bf16x8(wv[t]), acc[dt]);
+            }
+        };
+        // P of query tile qt, published through LDS for the dS wave.
+        auto p_tile = [&](int qt, u32x4 (&pw)[2]) {
+          f32x16 sacc = first(qt);
+          if (masked) {             // rare: blocks on a sample start or the diagonal
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int qq = q0 + qt * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
+              if (!(kok && key <= qq && qq < kend)) sacc[r] = -__builtin_inff();
             }
           }
-      }
-    };
-
-    wait_vmem_lds();
-    block_barrier();                // the previous item's reads of buffer 0 and of P are done
-    if (nsteps > 0) issue(0, bl0);
-    for (int i = 0; i < nsteps; i += 2) {
-      step(i, std::integral_constant<int, 0>{});
-      if (i + 1 < nsteps) step(i + 1, std::integral_constant<int, 1>{});
-    }
-
-    if (kok) {
-      uint16_t *dst = (pwave ? a.dv : a.dk) + ((int64_t)key * a.h_kv + kvh) * D;
-      const float sc = pwave ? 1.0f : a.scale;
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt)
+          for (int t = 0; t < 2; ++t) {
+            const int ql = qt * 32 + 16 * t + 8 * half;   // first of 8 consecutive queries
+            const float4 l0 = *reinterpret_cast<const float4 *>(lse_l + ql);
+            const float4 l1 = *reinterpret_cast<const float4 *>(lse_l + ql + 4);
+            const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(acc[dt][4 * cc] * sc, acc[dt][4 * cc + 1] * sc);
-          pk[1] = pack_bf16x2(acc[dt][4 * cc + 2] * sc, acc[dt][4 * cc + 3] * sc);
-          *reinterpret_cast<u32x2 *>(dst + dt * 32 + 8 * cc + 4 * half) = pk;
+            for (int e = 0; e < 4; ++e) {
+              const float p0 = exp2_fast(fmaf(sacc[8 * t + 2 * e], c, -lv[2 * e]));   // masked: 0
+              const float p1 = exp2_fast(fmaf(sacc[8 * t + 2 * e + 1], c, -lv[2 * e + 1]));
+              pw[t][e] = pack_bf16x2(p0, p1);
+            }
+            p_mine[(qt * 2 + t) * 64] = pw[t];
+          }
+        };
+        // dS of query tile qt from this wave's dP and the P wave's P.
+        auto ds_tile = [&](int qt, const f32x16 &pacc, u32x4 (&dsw)[2]) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int ql = qt * 32 + 16 * t + 8 * half;
+            const float4 d0 = *reinterpret_cast<const float4 *>(dd_l + ql);
+            const float4 d1 = *reinterpret_cast<const float4 *>(dd_l + ql + 4);
+            const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+            const u32x4 pv = p_mine[(qt * 2 + t) * 64];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float ds0 = bf16_lo(pv[e]) * (pacc[8 * t + 2 * e] - dv8[2 * e]);
+              const float ds1 = bf16_hi(pv[e]) * (pacc[8 * t + 2 * e + 1] - dv8[2 * e + 1]);
+              dsw[t][e] = pack_bf16x2(ds0, ds1);
+            }
+          }
+        };
+
+        // The two query tiles are staggered across two mid-step barriers so
+        // that the two waves of a SIMD alternate matrix and element-wise work:
+        //   P wave:  S0 P0 | dV0 S1 P1 | dV1
+        //   dS wave: dP0   | dS0 dK0 dP1 | dS1 dK1
+        if constexpr (pwave) {
+          u32x4 pw0[2], pw1[2];
+          if (act) p_tile(0, pw0);
+          wait_lds();
+          block_barrier();            // P of query tile 0 is in LDS
+          if (act) {
+            second(0, pw0);
+            p_tile(1, pw1);
+          }
+          wait_lds();
+          block_barrier();            // P of query tile 1 is in LDS
+          if (act) second(1, pw1);
+        } else {
+          f32x16 pacc0, pacc1;
+          if (act) pacc0 = first(0);
+          block_barrier();
+          if (act) {
+            u32x4 dsw[2];
+            ds_tile(0, pacc0, dsw);
+            second(0, dsw);
+            pacc1 = first(1);
+          }
+          block_barrier();
+          if (act) {
+            u32x4 dsw[2];
+            ds_tile(1, pacc1, dsw);
+            second(1, dsw);
+          }
         }
+      };
+
+      wait_vmem_lds();
+      block_barrier();              // the previous item's reads of buffer 0 and of P are done
+      if (nsteps > 0) issue(nh, nq0, bl0);
+      for (int i = 0; i < nsteps; i += 2) {
+        step(i, std::integral_constant<int, 0>{});
+        if (i + 1 < nsteps) step(i + 1, std::integral_constant<int, 1>{});
+      }
+
+      if (kok) {
+        uint16_t *dst = (pwave ? a.dv : a.dk) + ((int64_t)key * a.h_kv + kvh) * D;
+        const float sc = pwave ? 1.0f : a.scale;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            u32x2 pk;
+            pk[0] = pack_bf16x2(acc[dt][4 * cc] * sc, acc[dt][4 * cc + 1] * sc);
+            pk[1] = pack_bf16x2(acc[dt][4 * cc + 2] * sc, acc[dt][4 * cc + 3] * sc);
+            *reinterpret_cast<u32x2 *>(dst + dt * 32 + 8 * cc + 4 * half) = pk;
+          }
+      }
     }
-  }
+  };
+  if (wave < 4) run(std::true_type{});
+  else run(std::false_type{});
   __syncthreads();
   if (a.records != nullptr && tid == 0) write_record(a, w, end - beg, t_start);
 }
@@ -340,6 +363,9 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const uint32_t bl0 = lds_addr(buf0), bl1 = lds_addr(buf1);
   const int dlo = direct_lane_off<D>(lane);        // K / V operand reads
   const int tlo = tr_lane_off<D>(lane);            // K^T operand reads
+  const int64_t kv_stride = (int64_t)a.h_kv * D;
+  RowCopy<D, kKB, NW> kvcopy;
+  kvcopy.init(wave, lane, kv_stride);
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -369,10 +395,9 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) dqacc[dt] = zero16();
 
-    auto issue = [&](int k0, uint32_t dst) {
-      auto row = [&](int rr) { return ((int64_t)min(k0 + rr, a.L - 1) * a.h_kv + kvh) * D; };   // rows past L are masked
-      dma_rows<D, kKB, NW>(dst, wave, lane, [&](int rr) { return a.k + row(rr); });
-      dma_rows<D, kKB, NW>(dst + 2 * BLK, wave, lane, [&](int rr) { return a.v + row(rr); });   // byte offsets
+    auto issue = [&](int k0, uint32_t dst) {   // rows past L are masked; clamped to row L - 1
+      kvcopy.issue(dst, wave, a.k + kvh * D, kv_stride, k0, a.L);
+      kvcopy.issue(dst + 2 * BLK, wave, a.v + kvh * D, kv_stride, k0, a.L);   // byte offsets
     };
 
     auto block = [&](int b, auto bufc) {

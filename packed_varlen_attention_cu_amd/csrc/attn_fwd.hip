@@ -89,6 +89,9 @@ void attn_fwd_kernel(FwdArgs a) {
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
   const int dlo = direct_lane_off<D>(lane);     // K operand reads
   const int tlo = tr_lane_off<D>(lane);         // V^T operand reads
+  const int64_t kv_stride = (int64_t)a.h_kv * D;
+  RowCopy<D, kBN, NW> kvcopy;
+  kvcopy.init(wave, lane, kv_stride);
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -133,9 +136,8 @@ void attn_fwd_kernel(FwdArgs a) {
     auto issue = [&](int k0, auto bufc) {
       const uint32_t kdst = decltype(bufc)::value == 0 ? kl0 : kl1;
       const uint32_t vdst = decltype(bufc)::value == 0 ? vl0 : vl1;
-      auto row = [&](int r) { return ((int64_t)min(k0 + r, a.L - 1) * a.h_kv + kvh) * D; };
-      dma_rows<D, kBN, NW>(kdst, wave, lane, [&](int r) { return a.k + row(r); });
-      dma_rows<D, kBN, NW>(vdst, wave, lane, [&](int r) { return a.v + row(r); });
+      kvcopy.issue(kdst, wave, a.k + kvh * D, kv_stride, k0, a.L);
+      kvcopy.issue(vdst, wave, a.v + kvh * D, kv_stride, k0, a.L);
     };
 
     // One key block.  After this wave's copies of block b have landed and its

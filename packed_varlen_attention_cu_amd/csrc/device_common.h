@@ -173,24 +173,47 @@ struct PadRows {
   static constexpr int copies(int nr) { return (nr * kStride * 2 + 1023) / 1024; }
 };
 
-// Copy rows 0..NR-1 of a block into LDS at byte address lds (padded rows).
-// row_src(r) is the global address of row r (16-byte aligned, D elements).
-// Instruction i of the copy is issued by wave i mod NW; lanes whose 16-byte
-// slot falls into a row's padding are switched off.
-template <int D, int NR, int NW, typename RowSrc>
-__device__ __forceinline__ void dma_rows(uint32_t lds, int wave, int lane, RowSrc row_src) {
-  constexpr int RS = PadRows<D>::kStride;
-  constexpr int NI = PadRows<D>::copies(NR);
+// Copy of a block of NR rows (D elements each, row r at src + r * stride)
+// into LDS in padded rows.  The block takes exactly NI one-kilobyte LDS-DMA
+// instructions (no lane falls past the last row); instruction i is issued by
+// wave i mod NW.  A lane whose 16-byte slot is a row's padding copies that
+// row's first chunk into the padding, which is never read, so no lane is
+// switched off.  The lane's offsets are fixed per kernel and computed once.
+template <int D, int NR, int NW>
+struct RowCopy {
+  static constexpr int RS = PadRows<D>::kStride;
+  static constexpr int NI = PadRows<D>::copies(NR);
+  static constexpr int NJ = (NI + NW - 1) / NW;
+  static_assert(NI * 1024 == NR * RS * 2, "the block fills whole copy instructions");
+  int row[NJ], col[NJ];
+  int64_t off[NJ];                           // row * stride + col
+
+  __device__ __forceinline__ void init(int wave, int lane, int64_t stride) {
 #pragma unroll
-  for (int j = 0; j < (NI + NW - 1) / NW; ++j) {
-    const int i = wave + j * NW;
-    if (i < NI) {
-      const int e = 512 * i + 8 * lane;      // element offset of this lane's slot
-      const int r = e / RS, c = e - r * RS;
-      if (c < D && r < NR) lds_dma16(row_src(r) + c, lds + 1024 * i);
+    for (int j = 0; j < NJ; ++j) {
+      const int e = 512 * (wave + j * NW) + 8 * lane;   // element offset of the lane's slot
+      row[j] = e / RS;
+      const int c = e - row[j] * RS;
+      col[j] = c < D ? c : 0;
+      off[j] = (int64_t)row[j] * stride + col[j];
     }
   }
-}
+  // Rows r0 .. r0 + NR - 1 of the tensor at base (whose row r starts at
+  // base + r * stride): rows at or past `rows` are replaced by row rows - 1.
+  __device__ __forceinline__ void issue(uint32_t lds, int wave, const uint16_t *base, int64_t stride, int r0,
+                                        int rows) const {
+    const uint16_t *b = base + (int64_t)r0 * stride;
+    const bool tail = r0 + NR > rows;        // wave-uniform; only the pack's last block
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int i = wave + j * NW;
+      if (i < NI) {
+        const uint16_t *src = tail ? base + (int64_t)min(r0 + row[j], rows - 1) * stride + col[j] : b + off[j];
+        lds_dma16(src, lds + 1024 * i);
+      }
+    }
+  }
+};
 
 // Direct A operand: lane (col, half) reads row sigma_row(col) + 32 t of the
 // block, reduction elements 16 s + 8 half .. + 7.  direct_lane_off is the
