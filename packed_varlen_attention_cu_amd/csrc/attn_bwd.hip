@@ -35,6 +35,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kQB = 64;      // query rows per block in the dK/dV pass
+constexpr int kStages = 3;   // LDS buffers: copies run kStages - 1 blocks ahead
 constexpr int kKB = 64;      // key rows per block in the dQ pass
 
 inline int64_t round_up64(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -121,8 +122,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NS = D / 16, ND = D / 32;
   static_assert(2 * kQB <= NW * 16, "LSE and D copies: 16 values per wave");
   constexpr int ROW = DkdvLds<D>::kRow;
-  __shared__ __attribute__((aligned(16))) uint16_t buf0[DkdvLds<D>::kBuf];
-  __shared__ __attribute__((aligned(16))) uint16_t buf1[DkdvLds<D>::kBuf];
+  // kStages buffers of a step's Q, dO, LSE and D; step i uses buffer i mod kStages.
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kStages * DkdvLds<D>::kBuf];
   __shared__ __attribute__((aligned(16))) uint16_t p_lds[DkdvLds<D>::kP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -132,13 +133,14 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   const uint64_t t_start = wall_clock64();
   const int beg = a.cu_off[w], end = a.cu_off[w + 1];
   const float c = a.scale_log2;
-  const uint32_t bl0 = lds_addr(buf0), bl1 = lds_addr(buf1);
+  const uint32_t q_base = lds_addr(q_lds);
   u32x4 *p_mine = reinterpret_cast<u32x4 *>(p_lds + kg * 32 * kQB) + lane;   // [4 slabs][64 lanes]
   const int dlo = direct_lane_off<D>(lane);        // Q / dO operand reads
   const int tlo = tr_lane_off<D>(lane);            // Q^T / dO^T operand reads
   const int64_t q_stride = (int64_t)a.h_q * D;
   RowCopy<D, kQB, NW> qcopy;
   qcopy.init(wave, lane, q_stride);
+  const int copies = 2 * RowCopy<D, kQB, NW>::count(wave) + 1;   // this wave's copies per step
 
   // The two roles are separate instantiations, so each allocates registers
   // for its own path only; both pass the same barriers.
@@ -171,7 +173,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 
       // Queue the copies of the step at (head h, query block q0); rows past L
       // are masked, so their addresses are clamped to row L - 1.
-      auto issue = [&](int h, int q0, uint32_t dst) {
+      auto issue = [&](int h, int q0, int buf) {
+        const uint32_t dst = q_base + buf * 2 * DkdvLds<D>::kBuf;   // bytes
         qcopy.issue(dst, wave, a.q + h * D, q_stride, q0, a.L);
         qcopy.issue(dst + 2 * ROW, wave, a.dout + h * D, q_stride, q0, a.L);   // byte offsets
         // LSE * log2(e) then D of the block's queries: lanes 0..15 of each wave copy 16 values.
@@ -183,23 +186,27 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
         }
       };
 
-      // Steps run over (head, query block) in order; (nh, nq0) is the next one.
-      int nh = item.head0, nq0 = qstart;
-      auto advance = [&]() {
-        nq0 += kQB;
-        if (nq0 >= qstart + nqb * kQB) {
-          nq0 = qstart;
-          ++nh;
+      // Steps run over (head, query block) in order: (ch, cq0) is the step to
+      // compute next, (nh, nq0) the next one to copy.
+      int ch = item.head0, cq0 = qstart, nh = item.head0, nq0 = qstart;
+      auto advance = [&](int &hh, int &qq) {
+        qq += kQB;
+        if (qq >= qstart + nqb * kQB) {
+          qq = qstart;
+          ++hh;
         }
       };
-      auto step = [&](int i, auto bufc) {
-        constexpr int BUF = decltype(bufc)::value;
-        const uint16_t *bq = BUF == 0 ? buf0 : buf1;
-        const int q0 = nq0;
-        advance();
-        wait_vmem_lds();              // own copies of step i landed, own LDS accesses of step i - 1 done
+      auto step = [&](int i, int buf) {
+        const uint16_t *bq = q_lds + buf * DkdvLds<D>::kBuf;
+        const int q0 = cq0;
+        advance(ch, cq0);
+        wait_vmem_upto(i + 1 < nsteps ? copies : 0);   // step i landed; step i + 1 may fly
+        wait_lds();                   // own LDS accesses of step i - 1 done
         block_barrier();
-        if (i + 1 < nsteps) issue(nh, nq0, BUF == 0 ? bl1 : bl0);
+        if (i + kStages - 1 < nsteps) {
+          issue(nh, nq0, buf == 0 ? kStages - 1 : buf - 1);
+          advance(nh, nq0);
+        }
         const bool touch = kok && (q0 + kQB - 1 >= key) && (q0 < kend);
         const bool full = !kok || ((key <= q0) && (q0 + kQB - 1 < kend));
         const bool act = wave_any(touch);     // identical for the two waves of a key group
@@ -309,12 +316,14 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
       };
 
       wait_vmem_lds();
-      block_barrier();              // the previous item's reads of buffer 0 and of P are done
-      if (nsteps > 0) issue(nh, nq0, bl0);
-      for (int i = 0; i < nsteps; i += 2) {
-        step(i, std::integral_constant<int, 0>{});
-        if (i + 1 < nsteps) step(i + 1, std::integral_constant<int, 1>{});
-      }
+      block_barrier();              // the previous item's reads of every buffer and of P are done
+#pragma unroll
+      for (int i = 0; i < kStages - 1; ++i)
+        if (i < nsteps) {
+          issue(nh, nq0, i);
+          advance(nh, nq0);
+        }
+      for (int i = 0, buf = 0; i < nsteps; ++i, buf = buf == kStages - 1 ? 0 : buf + 1) step(i, buf);
 
       if (kok) {
         uint16_t *dst = (pwave ? a.dv : a.dk) + ((int64_t)key * a.h_kv + kvh) * D;
@@ -351,8 +360,8 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = kDqWaves;
   constexpr int NS = D / 16, ND = D / 32;
   constexpr int BLK = kKB * PadRows<D>::kStride;   // elements of one padded block
-  __shared__ __attribute__((aligned(16))) uint16_t buf0[2 * BLK];
-  __shared__ __attribute__((aligned(16))) uint16_t buf1[2 * BLK];
+  // kStages buffers of a K and a V block; block b uses buffer b mod kStages.
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[kStages * 2 * BLK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int half = lane >> 5, col = lane & 31;
@@ -360,12 +369,13 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const uint64_t t_start = wall_clock64();
   const int beg = a.cu_off[w], end = a.cu_off[w + 1];
   const float c = a.scale_log2;
-  const uint32_t bl0 = lds_addr(buf0), bl1 = lds_addr(buf1);
+  const uint32_t kv_base = lds_addr(kv_lds);
   const int dlo = direct_lane_off<D>(lane);        // K / V operand reads
   const int tlo = tr_lane_off<D>(lane);            // K^T operand reads
   const int64_t kv_stride = (int64_t)a.h_kv * D;
   RowCopy<D, kKB, NW> kvcopy;
   kvcopy.init(wave, lane, kv_stride);
+  const int copies = 2 * RowCopy<D, kKB, NW>::count(wave);   // this wave's copies per block
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -395,18 +405,19 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) dqacc[dt] = zero16();
 
-    auto issue = [&](int k0, uint32_t dst) {   // rows past L are masked; clamped to row L - 1
+    auto issue = [&](int k0, int buf) {   // rows past L are masked; clamped to row L - 1
+      const uint32_t dst = kv_base + buf * 4 * BLK;   // bytes
       kvcopy.issue(dst, wave, a.k + kvh * D, kv_stride, k0, a.L);
-      kvcopy.issue(dst + 2 * BLK, wave, a.v + kvh * D, kv_stride, k0, a.L);   // byte offsets
+      kvcopy.issue(dst + 2 * BLK, wave, a.v + kvh * D, kv_stride, k0, a.L);
     };
 
-    auto block = [&](int b, auto bufc) {
-      constexpr int BUF = decltype(bufc)::value;
-      const uint16_t *bk = BUF == 0 ? buf0 : buf1;
+    auto block = [&](int b, int buf) {
+      const uint16_t *bk = kv_lds + buf * 2 * BLK;
       const int k0 = kstart + b * kKB;
-      wait_vmem_lds();
+      wait_vmem_upto(b + 1 < nkb ? copies : 0);   // block b landed; block b + 1 may fly
+      wait_lds();
       block_barrier();
-      if (b + 1 < nkb) issue(k0 + kKB, BUF == 0 ? bl1 : bl0);
+      if (b + kStages - 1 < nkb) issue(k0 + (kStages - 1) * kKB, buf == 0 ? kStages - 1 : buf - 1);
       const bool touch = qok && (k0 <= qpos) && (k0 + kKB - 1 >= qss);
       const bool partial = qok && !((k0 >= qss) && (k0 + kKB - 1 <= qpos));
       if (wave_any(touch)) {
@@ -459,12 +470,11 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     };
 
     wait_vmem_lds();
-    block_barrier();
-    if (nkb > 0) issue(kstart, bl0);
-    for (int b = 0; b < nkb; b += 2) {
-      block(b, std::integral_constant<int, 0>{});
-      if (b + 1 < nkb) block(b + 1, std::integral_constant<int, 1>{});
-    }
+    block_barrier();                // the previous item's reads of every buffer are done
+#pragma unroll
+    for (int b = 0; b < kStages - 1; ++b)
+      if (b < nkb) issue(kstart + b * kKB, b);
+    for (int b = 0, buf = 0; b < nkb; ++b, buf = buf == kStages - 1 ? 0 : buf + 1) block(b, buf);
 
     if (qok) {
       uint16_t *op = a.dq + ((int64_t)qpos * a.h_q + head) * D;

@@ -34,6 +34,7 @@
 namespace libra {
 
 constexpr int kBN = 64;          // keys per block
+constexpr int kStages = 3;       // LDS buffers: copies run kStages - 1 blocks ahead
 
 struct FwdArgs {
   const libra_item *items;
@@ -70,12 +71,11 @@ void attn_fwd_kernel(FwdArgs a) {
   constexpr int NS = D / 16;                    // reduction slabs of d
   constexpr int ND = D / 32;                    // 32-row tiles of d in O^T
   constexpr int RS = PadRows<D>::kStride;
-  // Two buffers of K and V [kBN][D] in padded rows.  The V^T operands of
-  // O^T = V^T P^T come from transposing reads of the V block.
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[kBN * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds1[kBN * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[kBN * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[kBN * RS];
+  // kStages buffers, each a K and a V block [kBN][D] in padded rows; block b
+  // uses buffer b mod kStages and is copied kStages - 1 blocks ahead.  The V^T
+  // operands of O^T = V^T P^T come from transposing reads of the V block.
+  constexpr int BLK = kBN * RS;
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[kStages * 2 * BLK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int half = lane >> 5, col = lane & 31;
@@ -83,8 +83,7 @@ void attn_fwd_kernel(FwdArgs a) {
   const uint64_t t_start = wall_clock64();
   const int beg = a.cu_off[w], end = a.cu_off[w + 1];
   const float sl2 = a.scale_log2;
-  const uint32_t kl0 = lds_addr(k_lds0), kl1 = lds_addr(k_lds1);
-  const uint32_t vl0 = lds_addr(v_lds0), vl1 = lds_addr(v_lds1);
+  const uint32_t kv_base = lds_addr(kv_lds);
   const float NEG_INF = -__builtin_inff();
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
   const int dlo = direct_lane_off<D>(lane);     // K operand reads
@@ -92,6 +91,7 @@ void attn_fwd_kernel(FwdArgs a) {
   const int64_t kv_stride = (int64_t)a.h_kv * D;
   RowCopy<D, kBN, NW> kvcopy;
   kvcopy.init(wave, lane, kv_stride);
+  const int copies = 2 * RowCopy<D, kBN, NW>::count(wave);   // this wave's copies per block
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -131,27 +131,26 @@ void attn_fwd_kernel(FwdArgs a) {
       l_run[qt] = 0.0f;
     }
 
-    // Queue the K and V blocks at key k0 into LDS buffer BUF (no registers);
+    // Queue the K and V blocks at key k0 into LDS buffer buf (no registers);
     // rows past L are masked, so their addresses are clamped to row L - 1.
-    auto issue = [&](int k0, auto bufc) {
-      const uint32_t kdst = decltype(bufc)::value == 0 ? kl0 : kl1;
-      const uint32_t vdst = decltype(bufc)::value == 0 ? vl0 : vl1;
-      kvcopy.issue(kdst, wave, a.k + kvh * D, kv_stride, k0, a.L);
-      kvcopy.issue(vdst, wave, a.v + kvh * D, kv_stride, k0, a.L);
+    auto issue = [&](int k0, int buf) {
+      const uint32_t dst = kv_base + buf * 4 * BLK;   // bytes
+      kvcopy.issue(dst, wave, a.k + kvh * D, kv_stride, k0, a.L);
+      kvcopy.issue(dst + 2 * BLK, wave, a.v + kvh * D, kv_stride, k0, a.L);
     };
 
-    // One key block.  After this wave's copies of block b have landed and its
-    // reads of the other buffer (block b - 1) have completed, one barrier makes
-    // both true for every wave; then block b + 1 is queued into the other
-    // buffer and block b is computed while it flies.
-    auto block = [&](int b, auto bufc) {
-      constexpr int BUF = decltype(bufc)::value;
+    // One key block.  Once this wave's copies of block b have landed (those of
+    // block b + 1 may still fly) and its reads of block b - 1 have completed,
+    // one barrier makes both true for every wave; then block b + kStages - 1
+    // is queued into the buffer block b - 1 used, and block b is computed.
+    auto block = [&](int b, int buf) {
       const int k0 = kstart + b * kBN;
-      wait_vmem_lds();
+      wait_vmem_upto(b + 1 < nblk ? copies : 0);
+      wait_lds();
       block_barrier();
-      if (b + 1 < nblk) issue(k0 + kBN, std::integral_constant<int, BUF ^ 1>{});
-      const uint16_t *kb = BUF == 0 ? k_lds0 : k_lds1;
-      const uint16_t *vb = BUF == 0 ? v_lds0 : v_lds1;
+      if (b + kStages - 1 < nblk) issue(k0 + (kStages - 1) * kBN, buf == 0 ? kStages - 1 : buf - 1);
+      const uint16_t *kb = kv_lds + buf * 2 * BLK;
+      const uint16_t *vb = kb + BLK;
 
       bool touch = false, partial = false;
 #pragma unroll
@@ -250,12 +249,11 @@ void attn_fwd_kernel(FwdArgs a) {
     };
 
     wait_vmem_lds();
-    block_barrier();                // the previous item's reads of buffer 0 are done
-    if (nblk > 0) issue(kstart, std::integral_constant<int, 0>{});
-    for (int b = 0; b < nblk; b += 2) {
-      block(b, std::integral_constant<int, 0>{});
-      if (b + 1 < nblk) block(b + 1, std::integral_constant<int, 1>{});
-    }
+    block_barrier();                // the previous item's reads of every buffer are done
+#pragma unroll
+    for (int b = 0; b < kStages - 1; ++b)
+      if (b < nblk) issue(kstart + b * kBN, b);
+    for (int b = 0, buf = 0; b < nblk; ++b, buf = buf == kStages - 1 ? 0 : buf + 1) block(b, buf);
 
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {

@@ -130,6 +130,29 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Wait until at most n (0..15, wave-uniform) vector-memory operations of this
+// wave are outstanding.
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+  switch (n) {
+    case 0: wait_vmem<0>(); break;
+    case 1: wait_vmem<1>(); break;
+    case 2: wait_vmem<2>(); break;
+    case 3: wait_vmem<3>(); break;
+    case 4: wait_vmem<4>(); break;
+    case 5: wait_vmem<5>(); break;
+    case 6: wait_vmem<6>(); break;
+    case 7: wait_vmem<7>(); break;
+    case 8: wait_vmem<8>(); break;
+    case 9: wait_vmem<9>(); break;
+    case 10: wait_vmem<10>(); break;
+    case 11: wait_vmem<11>(); break;
+    case 12: wait_vmem<12>(); break;
+    case 13: wait_vmem<13>(); break;
+    case 14: wait_vmem<14>(); break;
+    default: wait_vmem<15>(); break;
+  }
+}
+
 // Wait until this wave's LDS reads and writes have completed.
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
@@ -187,6 +210,9 @@ struct RowCopy {
   static_assert(NI * 1024 == NR * RS * 2, "the block fills whole copy instructions");
   int row[NJ], col[NJ];
   int64_t off[NJ];                           // row * stride + col
+
+  // Copy instructions a wave issues per block.
+  static __device__ __forceinline__ int count(int wave) { return wave < NI ? (NI - 1 - wave) / NW + 1 : 0; }
 
   __device__ __forceinline__ void init(int wave, int lane, int64_t stride) {
 #pragma unroll
