@@ -109,6 +109,22 @@ __device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gsrc) : "memory", "m0");
 }
 
+// The same with a wave-uniform base address (SGPR pair) and a 32-bit
+// per-lane byte offset: lane i copies 16 bytes at sbase + voff.
+__device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, uint32_t lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+// A pointer every lane holds the same value of, moved into scalar registers.
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void *)(((uint64_t)hi << 32) | lo);
+}
+
 // The same for 4 bytes per lane: lane i writes lds_base + 4 * i.
 __device__ __forceinline__ void lds_dma4(const void *gsrc, uint32_t lds_base) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_base);
@@ -208,36 +224,68 @@ struct RowCopy {
   static constexpr int NI = PadRows<D>::copies(NR);
   static constexpr int NJ = (NI + NW - 1) / NW;
   static_assert(NI * 1024 == NR * RS * 2, "the block fills whole copy instructions");
-  int row[NJ], col[NJ];
-  int64_t off[NJ];                           // row * stride + col
+  uint32_t voff[NJ];                         // byte offset of the lane's source: row * stride + col
 
   // Copy instructions a wave issues per block.
   static __device__ __forceinline__ int count(int wave) { return wave < NI ? (NI - 1 - wave) / NW + 1 : 0; }
+  // Block row and column (element) the lane copies in the wave's j-th copy;
+  // lanes that land in a row's padding re-copy column 0.
+  static __device__ __forceinline__ void slot(int wave, int lane, int j, int &row, int &col) {
+    const int e = 512 * (wave + j * NW) + 8 * lane;   // element offset of the lane's slot
+    row = e / RS;
+    const int c = e - row * RS;
+    col = c < D ? c : 0;
+  }
 
   __device__ __forceinline__ void init(int wave, int lane, int64_t stride) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int e = 512 * (wave + j * NW) + 8 * lane;   // element offset of the lane's slot
-      row[j] = e / RS;
-      const int c = e - row[j] * RS;
-      col[j] = c < D ? c : 0;
-      off[j] = (int64_t)row[j] * stride + col[j];
+      int row, col;
+      slot(wave, lane, j, row, col);
+      voff[j] = (uint32_t)(2 * ((int64_t)row * stride + col));
     }
   }
   // Rows r0 .. r0 + NR - 1 of the tensor at base (whose row r starts at
-  // base + r * stride): rows at or past `rows` are replaced by row rows - 1.
-  __device__ __forceinline__ void issue(uint32_t lds, int wave, const uint16_t *base, int64_t stride, int r0,
-                                        int rows) const {
-    const uint16_t *b = base + (int64_t)r0 * stride;
-    const bool tail = r0 + NR > rows;        // wave-uniform; only the pack's last block
+  // base + r * stride), for blocks that end at or before row `rows`: one
+  // scalar base address per block, the lanes' offsets fixed for the kernel.
+  __device__ __forceinline__ void issue_full(uint32_t lds, int wave, const uint16_t *base, int64_t stride,
+                                             int r0) const {
+    const void *b = uniform_ptr(base + (int64_t)r0 * stride);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int i = wave + j * NW;
+      if (i < NI) lds_dma16_s(b, voff[j], lds + 1024 * i);
+    }
+  }
+  // The same for a block that runs past row `rows` (only the pack's last
+  // block): rows at or past `rows` are replaced by row rows - 1.  The lane's
+  // row and column are recovered from its offset here, behind an empty asm
+  // statement, so that none of this arithmetic is hoisted out of the loops
+  // that call it (it would hold registers for the whole kernel).
+  __device__ __forceinline__ void issue_tail(uint32_t lds, int wave, const uint16_t *base, int64_t stride, int r0,
+                                             int rows) const {
+    const void *b = uniform_ptr(base + (int64_t)r0 * stride);
+    const uint32_t st = (uint32_t)stride;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int i = wave + j * NW;
       if (i < NI) {
-        const uint16_t *src = tail ? base + (int64_t)min(r0 + row[j], rows - 1) * stride + col[j] : b + off[j];
-        lds_dma16(src, lds + 1024 * i);
+        uint32_t vo = voff[j];
+        asm volatile("" : "+v"(vo));
+        const uint32_t e = vo >> 1;              // row * stride + col
+        const uint32_t row = e / st, col = e - row * st;
+        const uint32_t rr = (uint32_t)min(r0 + (int)row, rows - 1) - (uint32_t)r0;
+        lds_dma16_s(b, 2 * (rr * st + col), lds + 1024 * i);
       }
     }
+  }
+  // Either of the two, chosen per block (wave-uniform).
+  __device__ __forceinline__ void issue(uint32_t lds, int wave, const uint16_t *base, int64_t stride, int r0,
+                                        int rows) const {
+    if (r0 + NR <= rows)
+      issue_full(lds, wave, base, stride, r0);
+    else
+      issue_tail(lds, wave, base, stride, r0, rows);
   }
 };
 
