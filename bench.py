@@ -79,15 +79,20 @@ def cpu_baseline(w, cu, tensors, scale, with_bwd=True, budget_s=15.0):
     cores = max(1, min(16, len(os.sched_getaffinity(0))))
     g = w.h_q // w.h_kv
     lens = np.diff(np.asarray(cu, dtype=np.int64))
-    rng = np.random.default_rng(0)
+    # Units of work, heaviest first: the last 64 query rows of every (sample,
+    # KV head) pair, then the last 256, 1024, ... rows (each unit recomputes
+    # its own rows from scratch), until the time budget is spent.
     units = []
-    for j in np.argsort(-lens):                          # longest samples first: their tails
-        if lens[j] > 512:
-            units.append((int(j), int(rng.integers(0, w.h_kv)), int(lens[j]) - 256))
-    for j in range(len(lens)):
-        if 0 < lens[j] <= 512:
-            units.append((j, int(rng.integers(0, w.h_kv)), 0))
-
+    order = np.argsort(-lens, kind="stable")
+    tail = 64
+    while tail < 4 * int(lens.max()):
+        for j in order:
+            n = int(lens[j])
+            if n > tail // 4 or tail == 64:
+                for kv in range(w.h_kv):
+                    if n > 0:
+                        units.append((int(j), kv, max(0, n - tail)))
+        tail *= 4
     def run(unit):
         j, kv, first = unit
         s, e = int(cu[j]), int(cu[j + 1])
@@ -128,8 +133,8 @@ def cpu_baseline(w, cu, tensors, scale, with_bwd=True, budget_s=15.0):
     flops = (3.5 if with_bwd else 1.0) * 4 * w.head_dim * pairs
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"fp64 numpy oracle {'fwd+bwd' if with_bwd else 'fwd'} on {done} (sample, KV head) units of the same pack "
-                      f"(tails of 256 query rows of the longest samples, whole short samples; "
-                      f"{pairs} causal pairs) in {elapsed:.1f} s"}
+                      f"(the last 64, then 256, 1024, ... query rows of each sample, heaviest first, until "
+                      f"{budget_s:.0f} s were spent; {pairs} causal pair-heads) in {elapsed:.1f} s"}
 
 
 def traffic_for(kernel, workload, launches_bytes_fn):
@@ -187,43 +192,133 @@ def summarize_pmc(fetch_dir, write_dir, workload, copy_bytes):
     print(json.dumps({"written": out}))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="train_256k")
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--assign", type=int, default=0, help="0: Algorithm 2 placement, 1: round-robin")
-    ap.add_argument("--fwd-only", action="store_true", help="time the forward only")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
-                    help="run one plain device copy of this size first (counter calibration)")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    args = ap.parse_args()
+def _dbs(d):
+    return sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
 
-    if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
-                      args.calibrate_copy * (1 << 20))
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU sharding of this "
-              "path is a design note, not part of this build.", file=sys.stderr)
-        sys.exit(2)
 
+def _short(name):
+    """Kernel name without namespaces and argument lists: attn_fwd_kernel<128, 1, 8>."""
+    base = name.replace("(anonymous namespace)::", "").split("(")[0].replace("libra::", "")
+    return base.replace("void ", "").strip()
+
+
+def summarize_trace(d):
+    """Markdown table of every kernel in a rocprofv3 --kernel-trace database."""
+    import sqlite3
+    rows = {}
+    for p in _dbs(d):
+        con = sqlite3.connect(p)
+        q = "select name, duration, lds_size, grid_x, workgroup_x from kernels"
+        for name, dur, lds, gx, wx in con.execute(q):
+            r = rows.setdefault(name, {"d": [], "meta": (lds, gx, wx)})
+            r["d"].append(dur)
+    total = sum(sum(r["d"]) for r in rows.values())
+    print("| kernel | calls | total ms | avg ms | min ms | max ms | % | LDS bytes | grid (threads) | workgroup |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for name, r in sorted(rows.items(), key=lambda kv: -sum(kv[1]["d"])):
+        d_ = np.array(r["d"], dtype=np.float64) / 1e6
+        lds, gx, wx = r["meta"]
+        print(f"| `{_short(name)}` | {len(d_)} | {d_.sum():.3f} | {d_.mean():.3f} | {d_.min():.3f} | "
+              f"{d_.max():.3f} | {100 * d_.sum() * 1e6 / total:.2f} | {lds} | {gx} | {wx} |")
+
+
+def summarize_counters(dirs, clock_ghz=2.4, num_cus=256):
+    """Markdown table of rocprofv3 --pmc counters per kernel (mean over its dispatches), with
+    MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (kernel cycles x CUs x 4 SIMDs), kernel cycles
+    = its duration in the same run x the shader clock, and the LDS bank-conflict share
+    SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE."""
+    import sqlite3
+    vals, durs = {}, {}
+    for d in dirs:
+        for p in _dbs(d):
+            con = sqlite3.connect(p)
+            for k, c, v in con.execute("select kernel_name, counter_name, value from counters_collection"):
+                if "libra::" in k:
+                    vals.setdefault(_short(k), {}).setdefault(c, []).append(v)
+            for name, dur in con.execute("select name, duration from kernels"):
+                if "libra::" in name:
+                    durs.setdefault(_short(name), []).append(dur)
+    counters = sorted({c for v in vals.values() for c in v})
+    kernels = sorted(vals)
+    print("| counter | " + " | ".join(f"`{k}`" for k in kernels) + " |")
+    print("|---|" + "---|" * len(kernels))
+    mean = {k: {c: float(np.mean(v)) for c, v in vals[k].items()} for k in kernels}
+    for c in counters:
+        print(f"| {c} | " + " | ".join(f"{mean[k][c]:.4g}" if c in mean[k] else "" for k in kernels) + " |")
+
+    def derived(k):
+        m, out = mean[k], {}
+        dur = float(np.median(durs[k])) * 1e-9 if k in durs else None
+        if dur and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            out["MFMA util"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (dur * clock_ghz * 1e9 * num_cus * 4)
+        if "SQ_LDS_BANK_CONFLICT" in m and m.get("SQ_LDS_IDX_ACTIVE"):
+            out["LDS bank-conflict share"] = m["SQ_LDS_BANK_CONFLICT"] / m["SQ_LDS_IDX_ACTIVE"]
+        if m.get("SQ_INSTS_MFMA"):
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VALU_TRANS_F32"):
+                if c in m:
+                    out[c.replace("SQ_INSTS_", "") + " per MFMA"] = m[c] / m["SQ_INSTS_MFMA"]
+        if m.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in m:
+            out["VALU co-issued share of MFMA-busy cycles"] = m["SQ_VALU_MFMA_COEXEC_CYCLES"] / m["SQ_VALU_MFMA_BUSY_CYCLES"]
+        if dur:
+            out["kernel ms (this run)"] = dur * 1e3
+        return out
+    der = {k: derived(k) for k in kernels}
+    names = sorted({n for v in der.values() for n in v})
+    if names:
+        print()
+        print("| derived | " + " | ".join(f"`{k}`" for k in kernels) + " |")
+        print("|---|" + "---|" * len(kernels))
+        for n in names:
+            print(f"| {n} | " + " | ".join(f"{der[k][n]:.3f}" if n in der[k] else "" for k in kernels) + " |")
+
+
+def sweep():
+    """Forward on every workload at seed 0, then the per-CU balance of the skewed and uniform
+    packs at seeds 0-2 under Algorithm 2 and under round-robin placement."""
+    import torch
+    import synth
+    print("| workload | L | h_q/h_kv | d | samples | max sample | fwd ms | TFLOP/s | % bf16 peak | "
+          "CU busy max/mean | planned load max/mean | plan ms |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|", flush=True)
+    for wl in ("tiny_2k", "gqa_32k", "skew_128k_a", "skew_128k_b", "share_1m", "train_256k"):
+        o = measure(wl, 0, 0, True, 5, 2, False, quiet=True)
+        c = o["config"]
+        print(f"| {wl} | {c['total_tokens']} | {c['h_q']}/{c['h_kv']} | {c['head_dim']} | {c['samples']} | "
+              f"{c['max_sample']} | {o['kernel_ms']['fwd']:.3f} | {o['fwd_tflops']:.1f} | "
+              f"{100 * o['fwd_frac_peak']:.1f} | {o['cu_busy_max_over_mean']['fwd']:.3f} | "
+              f"{o['plan_load_max_over_mean']:.4f} | {o['plan_ms']:.2f} |", flush=True)
+        torch.cuda.empty_cache()
+    print()
+    print("| workload | seed | sum of squared lengths | placement | fwd ms | TFLOP/s | CU busy max/mean | "
+          "planned load max/mean |")
+    print("|---|---|---|---|---|---|---|---|", flush=True)
+    for wl in ("skew_128k_a", "skew_128k_b", "share_1m"):
+        for seed in (0, 1, 2):
+            sq = int((synth.make_lengths(synth.WORKLOADS[wl], seed).astype(np.int64) ** 2).sum())
+            for assign in (0, 1):
+                o = measure(wl, seed, assign, True, 3, 1, False, quiet=True)
+                print(f"| {wl} | {seed} | {sq:.4g} | {'Algorithm 2' if assign == 0 else 'round-robin'} | "
+                      f"{o['kernel_ms']['fwd']:.3f} | {o['fwd_tflops']:.1f} | "
+                      f"{o['cu_busy_max_over_mean']['fwd']:.3f} | {o['plan_load_max_over_mean']:.4f} |", flush=True)
+                torch.cuda.empty_cache()
+
+
+def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, warmup=2, cpu=True,
+            calibrate_copy=0, quiet=False):
+    """Time `steps` steps of the hot path on cuda:0; returns the JSON record."""
     import torch
     import synth
     import packed_varlen_attention_cu_amd as lib
 
-    w = synth.WORKLOADS[args.workload]
-    do_bwd = not args.fwd_only
+    w = synth.WORKLOADS[workload]
+    do_bwd = not fwd_only
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    lengths = synth.make_lengths(w, args.seed)
+    lengths = synth.make_lengths(w, seed)
     cu = synth.cu_seqlens(lengths)
     names = ("q", "k", "v", "dout") if do_bwd else ("q", "k", "v")
     t_gen = time.perf_counter()
-    host = synth.make_tensors(w, args.seed, names=names)
+    host = synth.make_tensors(w, seed, names=names)
     t_gen = time.perf_counter() - t_gen
 
     def up(bits):
@@ -238,7 +333,7 @@ def main():
     dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if do_bwd else (None,) * 3
 
     plan_kw = dict(total_tokens=L, h_q=w.h_q, h_kv=w.h_kv, head_dim=d, tile_tokens=w.tile_tokens,
-                   tile_heads=w.tile_heads, assign=args.assign)
+                   tile_heads=w.tile_heads, assign=assign)
     plan0 = lib.Plan(cu, **plan_kw)
     ncu = plan0.info.num_cus
     ws_b = torch.empty(max(1, lib.libra_attn_bwd_workspace(plan0.host)), dtype=torch.uint8, device=dev)
@@ -247,8 +342,8 @@ def main():
     cu_dev = torch.from_numpy(cu.copy()).to(dev)
     plan_dev = torch.empty(plan0.host.nbytes, dtype=torch.uint8, device=dev)
 
-    if args.calibrate_copy:
-        n = args.calibrate_copy << 20
+    if calibrate_copy:
+        n = calibrate_copy << 20
         a_ = torch.empty(n, dtype=torch.uint8, device=dev)
         b_ = torch.empty(n, dtype=torch.uint8, device=dev)
         b_.copy_(a_)
@@ -284,14 +379,14 @@ def main():
             timed("bwd_dq", lambda: lib.libra_attn_bwd_dq(plan.host, plan_dev, q, k, v, dout, lse, cu_dev, dq,
                                                           scale, ws_b, wsb, rec_q, sh))
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step(False)
     torch.cuda.synchronize()
     plan_ms.clear()
 
     wall = 0.0
     busy = {"fwd": [], "bwd_dkdv": [], "bwd_dq": []}
-    for i in range(args.steps):
+    for i in range(steps):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         step(True)
@@ -306,10 +401,11 @@ def main():
                 continue
             ratio, _ = cu_busy_ratio(r.cpu().numpy(), ncu)
             busy[n].append(ratio)
-        print(f"step {i + 1}/{args.steps}: {(time.perf_counter() - t0) * 1e3:.2f} ms", file=sys.stderr,
-              flush=True)
+        if not quiet:
+            print(f"step {i + 1}/{steps}: {(time.perf_counter() - t0) * 1e3:.2f} ms", file=sys.stderr,
+                  flush=True)
 
-    ms_step = wall / args.steps * 1e3
+    ms_step = wall / steps * 1e3
     pairs = causal_pairs(cu) * w.h_q
     assert pairs == plan0.info.total_pairs, "planner pair count disagrees with the closed form"
     fwd_flops = 4.0 * d * pairs
@@ -319,25 +415,25 @@ def main():
     kernels = {n: avg[n] for n in KERNEL_FLOPS_PER_PAIR if n in avg}
     dom = max(kernels, key=kernels.get)
     achieved = KERNEL_FLOPS_PER_PAIR[dom] * d * pairs / (kernels[dom] * 1e-3) / 1e12
-    traffic = traffic_for(dom, args.workload, lambda t: t["hbm_bytes_per_launch"])
+    traffic = traffic_for(dom, workload, lambda t: t["hbm_bytes_per_launch"])
 
     out = {
         "metric": METRIC,
         "value": round(total_flops / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "total_tokens": L, "h_q": w.h_q, "h_kv": w.h_kv,
+        "config": {"workload": workload, "total_tokens": L, "h_q": w.h_q, "h_kv": w.h_kv,
                    "head_dim": d, "sh_tile": [w.tile_tokens, w.tile_heads], "samples": int(len(lengths)),
-                   "max_sample": int(lengths.max()), "seed": args.seed, "pass": "fwd+bwd" if do_bwd else "fwd",
-                   "placement": "algorithm2" if args.assign == 0 else "round_robin", "num_cus": ncu},
+                   "max_sample": int(lengths.max()), "seed": seed, "pass": "fwd+bwd" if do_bwd else "fwd",
+                   "placement": "algorithm2" if assign == 0 else "round_robin", "num_cus": ncu},
         "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
         "fwd_frac_peak": round(fwd_flops / (avg["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": {n: round(t, 4) for n, t in avg.items()},
@@ -353,8 +449,51 @@ def main():
         bwd_ms = avg["bwd_prepare"] + avg["bwd_dkdv"] + avg["bwd_dq"]
         out["bwd_tflops"] = round(2.5 * fwd_flops / (bwd_ms * 1e-3) / 1e12, 2)
         out["fwd_bwd_kernels_tflops"] = round(3.5 * fwd_flops / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 2)
-    if not args.no_cpu_baseline:
+    if cpu:
         out["cpu_baseline"] = cpu_baseline(w, cu, host, scale, with_bwd=do_bwd)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="train_256k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--assign", type=int, default=0, help="0: Algorithm 2 placement, 1: round-robin")
+    ap.add_argument("--fwd-only", action="store_true", help="time the forward only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
+                    help="run one plain device copy of this size first (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", metavar="DIR", help="markdown table of a rocprofv3 --kernel-trace run")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", help="markdown table of rocprofv3 --pmc runs")
+    ap.add_argument("--sweep", action="store_true",
+                    help="forward on every workload (and seeds 0-2 and both placements on the skewed and "
+                         "uniform packs); prints a markdown table")
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload,
+                      args.calibrate_copy * (1 << 20))
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU sharding of this "
+              "path is a design note, not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.sweep:
+        sweep()
+        return
+    out = measure(args.workload, args.seed, args.assign, args.fwd_only, args.steps, args.warmup,
+                  not args.no_cpu_baseline, args.calibrate_copy)
     print(json.dumps(out), flush=True)
 
 
