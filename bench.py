@@ -38,10 +38,16 @@ KERNEL_SYMBOL = {"fwd": "attn_fwd_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel",
 
 
 def source_hash() -> str:
+    """Hash of the device sources with comments and blank lines removed (code changes only)."""
+    import re
     h = hashlib.sha256()
     for name in DEVICE_SOURCES:
-        with open(os.path.join(ROOT, "packed_varlen_attention_cu_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "packed_varlen_attention_cu_amd", "csrc", name)) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for line in text.splitlines():
+            line = re.sub(r"//.*", "", line).strip()
+            if line:
+                h.update(line.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -102,10 +102,10 @@ __device__ __forceinline__ void write_record(const BwdArgs &a, int w, int n, uin
 //
 // Per query block of kQB rows and one head, LDS holds Q and dO (row-major:
 // A operands of S and dP directly, and of dK^T and dV^T through transposing
-// reads) and the block's LSE * log2(e) and D values.  Two such buffers
-// alternate: after one barrier the copies for the next (head, query block)
-// step are queued into the other buffer, and the current one is computed
-// while they fly.  Blocks use padded rows (PadRows).
+// reads) and the block's LSE * log2(e) and D values.  kStages such buffers
+// rotate: after one barrier the copies for the step kStages - 1 ahead are
+// queued into the buffer the previous step used, and the current one is
+// computed while they fly.  Blocks use padded rows (PadRows).
 constexpr int kDkdvWaves = 8;
 
 template <int D>
@@ -350,8 +350,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 // Eight waves of 32 query positions each cover the 256 query columns of a
 // forward work item (two waves per SIMD).  Per key block of kKB keys, LDS
 // holds K and V (row-major: A operands of S^T and dP^T, and through
-// transposing reads the K^T operand of dQ^T), double-buffered like the
-// forward; all query heads of the item's KV head read the same copy.
+// transposing reads the K^T operand of dQ^T), in a ring of kStages buffers
+// like the forward; all query heads of the item's KV head read the same copy.
 constexpr int kDqWaves = 8;
 
 template <int D>

@@ -8,8 +8,9 @@
 //
 // Per item the workgroup walks key blocks of 64 from the start of the sample
 // holding the item's first row to its last row.  K and V blocks are copied
-// straight from HBM into LDS (double-buffered) and read by every wave, so all
-// query heads of a GQA group share one copy.  Each wave computes S^T = K Q^T
+// straight from HBM into LDS (a ring of kStages buffers, copies running
+// kStages - 1 blocks ahead) and read by every wave, so all query heads of a
+// GQA group share one copy.  Each wave computes S^T = K Q^T
 // with bf16 MFMA (its query columns land one per lane, so row statistics need
 // no cross-lane reduction beyond the two 32-lane halves), applies the
 // block-diagonal causal mask only on blocks that straddle a sample start or

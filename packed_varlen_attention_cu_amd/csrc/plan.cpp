@@ -9,11 +9,12 @@
 // the least-loaded worker under a soft target C = (1 + tau) * mean.
 //
 // On one GPU the workers are the CUs, every tensor is already in HBM (the
-// communication term of eq. 9 is zero), and a tile is cut into work items a
-// single workgroup of four 64-query waves executes (see libra.h).  With a zero
-// communication term both branches of Algorithm 2 pick the worker of least
-// (load, id) -- whenever any worker fits under C the least loaded one does --
-// so the placement is a binary heap keyed by (load, worker id).
+// communication term of eq. 9 is zero), and a tile is cut into work items of
+// 256 query columns (positions x heads) that one workgroup executes (see
+// libra.h).  With a zero communication term both branches of Algorithm 2
+// pick the worker of least (load, id) -- whenever any worker fits under C the
+// least loaded one does -- so the placement is a binary heap keyed by
+// (load, worker id).
 //
 // Everything here is integer arithmetic and bitwise deterministic.
 #include <algorithm>
@@ -28,10 +29,8 @@
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kWaveQueries = 64;
-constexpr int kItemColumns = kWaves * kWaveQueries;  // query positions x heads
-constexpr int kKvChunk = 128;                        // keys per dK/dV item
+constexpr int kItemColumns = 256;   // query positions x heads per forward / dQ item
+constexpr int kKvChunk = 128;       // keys per dK/dV item
 constexpr int kDefaultCus = 256;
 constexpr int kMaxCus = 1 << 16;
 
