@@ -279,8 +279,9 @@ def summarize_counters(dirs, clock_ghz=2.4, num_cus=256):
 
 
 def sweep():
-    """Forward on every workload at seed 0, then the per-CU balance of the skewed and uniform
-    packs at seeds 0-2 under Algorithm 2 and under round-robin placement."""
+    """Forward on every workload at seed 0; the skewed and the uniform 128K packs alone and pooled
+    into one launch; then the per-CU balance of the skewed and uniform packs at seeds 0-2 under
+    Algorithm 2 and under round-robin placement."""
     import torch
     import synth
     print("| workload | L | h_q/h_kv | d | samples | max sample | fwd ms | TFLOP/s | % bf16 peak | "
@@ -294,6 +295,19 @@ def sweep():
               f"{100 * o['fwd_frac_peak']:.1f} | {o['cu_busy_max_over_mean']['fwd']:.3f} | "
               f"{o['plan_load_max_over_mean']:.4f} | {o['plan_ms']:.2f} |", flush=True)
         torch.cuda.empty_cache()
+    print()
+    print("| launch | fwd ms | TFLOP/s | CU busy max/mean |")
+    print("|---|---|---|---|", flush=True)
+    total = 0.0
+    for wl in ("skew_128k_a", "skew_128k_b", "skew_128k_a+skew_128k_b"):
+        o = measure(wl, 0, 0, True, 5, 2, False, quiet=True)
+        if "+" not in wl:
+            total += o["kernel_ms"]["fwd"]
+        label = f"pool of two packs ({wl}), one launch" if "+" in wl else f"{wl} alone"
+        print(f"| {label} | {o['kernel_ms']['fwd']:.3f} | {o['fwd_tflops']:.1f} | "
+              f"{o['cu_busy_max_over_mean']['fwd']:.3f} |", flush=True)
+        torch.cuda.empty_cache()
+    print(f"| the two packs in two launches (sum) | {total:.3f} | | |", flush=True)
     print()
     print("| workload | seed | sum of squared lengths | placement | fwd ms | TFLOP/s | CU busy max/mean | "
           "planned load max/mean |")
@@ -309,6 +323,25 @@ def sweep():
                 torch.cuda.empty_cache()
 
 
+def pooled_inputs(workload, seed, names):
+    """Workload, sample lengths and bf16 tensors of one pack, or of a pool "a+b+...": the packs
+    concatenated into one (the block-diagonal mask keeps them apart), planned and launched once."""
+    import synth
+    parts = [synth.WORKLOADS[n] for n in workload.split("+")]
+    w0 = parts[0]
+    for p_ in parts[1:]:
+        if (p_.h_q, p_.h_kv, p_.head_dim, p_.tile_tokens, p_.tile_heads) != \
+                (w0.h_q, w0.h_kv, w0.head_dim, w0.tile_tokens, w0.tile_heads):
+            raise ValueError(f"pool members must share heads, head_dim and tiling: {workload}")
+    lengths = [synth.make_lengths(p_, seed) for p_ in parts]
+    tensors = [synth.make_tensors(p_, seed, names=names) for p_ in parts]
+    if len(parts) == 1:
+        return w0, lengths[0], tensors[0]
+    w = w0.with_tokens(sum(p_.total_tokens for p_ in parts), name=workload)
+    return (w, np.concatenate(lengths),
+            {n: np.concatenate([t[n] for t in tensors]) for n in names})
+
+
 def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, warmup=2, cpu=True,
             calibrate_copy=0, quiet=False):
     """Time `steps` steps of the hot path on cuda:0; returns the JSON record."""
@@ -316,16 +349,12 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
     import synth
     import packed_varlen_attention_cu_amd as lib
 
-    w = synth.WORKLOADS[workload]
     do_bwd = not fwd_only
+    names = ("q", "k", "v", "dout") if do_bwd else ("q", "k", "v")
+    w, lengths, host = pooled_inputs(workload, seed, names)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    lengths = synth.make_lengths(w, seed)
     cu = synth.cu_seqlens(lengths)
-    names = ("q", "k", "v", "dout") if do_bwd else ("q", "k", "v")
-    t_gen = time.perf_counter()
-    host = synth.make_tensors(w, seed, names=names)
-    t_gen = time.perf_counter() - t_gen
 
     def up(bits):
         return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)

@@ -56,6 +56,21 @@ def test_bwd_small_full(lib, name, L, first, kw):
         S.check_grad(S.from_dev_bf16(g), r, f"{name} {name_g}")
 
 
+@pytest.mark.parametrize("h_q,h_kv,d,tile_heads", [(12, 4, 128, 3), (6, 6, 64, 2), (16, 1, 128, 8),
+                                                    (32, 16, 64, 32)])
+def test_bwd_gqa_group_shapes(lib, h_q, h_kv, d, tile_heads):
+    """Group sizes 3, 1, 16 and 2: dK and dV sum over the group's query heads."""
+    import oracle.attention as A
+    w = synth.Workload(f"g{h_q}x{h_kv}", 1900, h_q, h_kv, d, 700, tile_heads, first_lengths=(700,))
+    cu = synth.cu_seqlens(synth.make_lengths(w, 4))
+    t = synth.make_tensors(w, 4, names=("q", "k", "v", "dout"))
+    S.say(f"[bwd] {w.name}: L={w.total_tokens} h={h_q}/{h_kv} d={d} samples={len(cu) - 1}")
+    dq, dk, dv = run_fwd_bwd(lib, w, cu, t)
+    ref = A.backward(*(A.widen_bf16(t[n]) for n in ("q", "k", "v", "dout")), cu, S.scale_of(w))
+    for name_g, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        S.check_grad(S.from_dev_bf16(g), r, f"{w.name} {name_g}")
+
+
 @pytest.mark.parametrize("lens", [[1] * 200, [0, 3, 0, 140, 1, 0, 70], [64], [65, 63, 2, 129]])
 def test_bwd_edge_packs(lib, lens):
     import oracle.attention as A

@@ -116,6 +116,37 @@ def test_fwd_plan_reuse_and_tilings_agree(lib):
         assert np.max(np.abs(o - outs[0])) <= 2 * S.O_MAX
 
 
+def test_fwd_pool_equals_separate_launches(lib):
+    """Two packs pooled into one plan and one launch (the rows of the second follow the first):
+    the pool matches the oracle, and each pack's rows match its own launch within tolerance,
+    since the block-diagonal mask keeps the packs apart."""
+    base = synth.WORKLOADS["skew_128k_a"]
+    wa = base.with_tokens(3000, first_lengths=(1500,))
+    wb = base.with_tokens(2001, first_lengths=())
+    la, lb = synth.make_lengths(wa, 2), synth.make_lengths(wb, 3)
+    ta, tb = synth.make_tensors(wa, 2), synth.make_tensors(wb, 3)
+    oa, lsa, _ = run_fwd(lib, wa, synth.cu_seqlens(la), ta)
+    ob, lsb, _ = run_fwd(lib, wb, synth.cu_seqlens(lb), tb)
+    wp = base.with_tokens(wa.total_tokens + wb.total_tokens, first_lengths=(), name="pool")
+    cup = synth.cu_seqlens(np.concatenate([la, lb]))
+    tp = {n: np.concatenate([ta[n], tb[n]]) for n in ("q", "k", "v")}
+    op, lsp = full_check(lib, wp, cup, tp, "pool of two packs")
+    op, lsp = S.from_dev_bf16(op), lsp.cpu().numpy()
+    sep = np.concatenate([S.from_dev_bf16(oa), S.from_dev_bf16(ob)])
+    assert np.max(np.abs(op - sep)) <= 2 * S.O_MAX
+    assert np.max(np.abs(lsp - np.concatenate([lsa.cpu().numpy(), lsb.cpu().numpy()], axis=1))) <= 2 * S.LSE_MAX
+
+
+@pytest.mark.parametrize("h_q,h_kv,d,tile_heads", [(12, 4, 128, 3), (6, 6, 64, 2), (16, 1, 128, 8),
+                                                    (32, 16, 64, 32)])
+def test_fwd_gqa_group_shapes(lib, h_q, h_kv, d, tile_heads):
+    """Group sizes 3, 1, 16 and 2, head counts that are not powers of two, both head sizes."""
+    w = synth.Workload(f"g{h_q}x{h_kv}", 2300, h_q, h_kv, d, 700, tile_heads, first_lengths=(900,))
+    cu = synth.cu_seqlens(synth.make_lengths(w, 4))
+    t = synth.make_tensors(w, 4)
+    full_check(lib, w, cu, t, w.name)
+
+
 FULL = [("gqa_32k", 96, 1), ("skew_128k_a", 64, 2), ("skew_128k_b", 64, 2), ("train_256k", 64, 4),
         ("share_1m", 12, 16)]
 
