@@ -323,6 +323,64 @@ def sweep():
                 torch.cuda.empty_cache()
 
 
+def vrsp_report(windows=20, seed=0):
+    """Variance-reduced sequence placement (host only): time per window, and the residual
+    inter-pool imbalance R - 1 (max / mean pool workload - 1) under the sampler's index order,
+    a seeded random grouping and VRSP, over windows of 128 synthetic packed sequences."""
+    import synth
+    import packed_varlen_attention_cu_amd as lib
+    import oracle.vrsp as V
+
+    def window(L, w_seed, D):
+        w = synth.WORKLOADS["train_256k"].with_tokens(L, first_lengths=())
+        return np.array([int((synth.make_lengths(w, w_seed * 1000 + i).astype(np.int64) ** 2).sum())
+                         for i in range(D)], dtype=np.int64)
+
+    print("| window D | pool size P | library, µs per window (median of 2000 calls, 1 thread) | "
+          "oracle (Python), µs per window | pages |")
+    print("|---|---|---|---|---|", flush=True)
+    for D, ref in ((128, "48 µs"), (256, "106 µs")):
+        F = window(262144, seed, D)
+        ts = []
+        for _ in range(2000):
+            t0 = time.perf_counter_ns()
+            lib.libra_vrsp(F, 8)
+            ts.append(time.perf_counter_ns() - t0)
+        to = []
+        Fl = F.tolist()
+        for _ in range(50):
+            t0 = time.perf_counter_ns()
+            V.vrsp(Fl, 8)
+            to.append(time.perf_counter_ns() - t0)
+        print(f"| {D} | 8 | {np.median(ts) / 1e3:.1f} | {np.median(to) / 1e3:.0f} | {ref} |", flush=True)
+    t_call = []
+    cu = np.array([0, 1], dtype=np.int32)
+    for _ in range(2000):
+        t0 = time.perf_counter_ns()
+        lib.libra_pack_workload(cu)
+        t_call.append(time.perf_counter_ns() - t0)
+    print(f"\nA trivial library call through the same binding takes {np.median(t_call) / 1e3:.1f} µs "
+          "(included above).\n")
+
+    print("| packs of | P | pools K | R - 1, index order | R - 1, random grouping | R - 1, VRSP | "
+          "lower bound (largest pack / mean pool - 1) |")
+    print("|---|---|---|---|---|---|---|", flush=True)
+    rng = np.random.default_rng(seed)
+    for L, label in ((262144, "256K tokens"), (1048576, "1M tokens")):
+        wins = [window(L, seed + 1 + r, 128) for r in range(windows)]
+        for P in (2, 4, 8, 16, 32, 64):
+            idx, rnd, vr, lb = [], [], [], []
+            for F in wins:
+                K = len(F) // P
+                lb.append(max(0.0, float(F.max()) / (float(F.sum()) / K) - 1.0))
+                idx.append(V.imbalance([int(F[k * P:(k + 1) * P].sum()) for k in range(K)]))
+                perm = rng.permutation(len(F))
+                rnd.append(V.imbalance([int(F[perm[k * P:(k + 1) * P]].sum()) for k in range(K)]))
+                vr.append(V.imbalance(lib.libra_vrsp(F, P)[2].tolist()))
+            print(f"| {label} | {P} | {len(wins[0]) // P} | {np.mean(idx):.4f} | {np.mean(rnd):.4f} | "
+                  f"{np.mean(vr):.5f} | {np.mean(lb):.5f} |", flush=True)
+
+
 def pooled_inputs(workload, seed, names):
     """Workload, sample lengths and bf16 tensors of one pack, or of a pool "a+b+...": the packs
     concatenated into one (the block-diagonal mask keeps them apart), planned and launched once."""
@@ -504,6 +562,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="DIR", help="markdown table of a rocprofv3 --kernel-trace run")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", help="markdown table of rocprofv3 --pmc runs")
+    ap.add_argument("--vrsp", action="store_true",
+                    help="host-only: variance-reduced sequence placement timing and pool balance")
     ap.add_argument("--sweep", action="store_true",
                     help="forward on every workload (and seeds 0-2 and both placements on the skewed and "
                          "uniform packs); prints a markdown table")
@@ -518,6 +578,9 @@ def main():
         return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters)
+        return
+    if args.vrsp:
+        vrsp_report()
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU sharding of this "

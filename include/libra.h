@@ -195,6 +195,41 @@ libra_status libra_attn_bwd_dq(const void *plan, const void *plan_dev,
                                float softmax_scale, const void *workspace,
                                size_t workspace_bytes, libra_cu_record *records, void *stream);
 
+/* ---- Sequence pools (host only) ----------------------------------------
+ *
+ * Variance-reduced sequence placement, VRSP (Libra technical review,
+ * section 4.2, Algorithm 1; Libra paper, section 4.2): the num_seqs packed
+ * sequences of one optimizer-step window are split into
+ * K = num_seqs / pool_size pools of exactly pool_size sequences each, so that
+ * the pools' summed workloads are as even as the heuristic makes them.
+ * Sequences are taken in order of decreasing workload (equal workloads by
+ * increasing index) and each goes to the least-loaded pool that still has
+ * room (equal loads by increasing pool index): the placement is a pure,
+ * deterministic function of its inputs.
+ */
+
+/* Workload proxy of one packed sequence (Libra technical review, section 3.1,
+ * eq. 1): *workload = sum over its samples of (sample length)^2.
+ * cu_seqlens: host, num_samples + 1 non-decreasing int32 offsets starting at
+ * 0 (empty samples allowed).  LIBRA_EINVAL on a NULL pointer, a negative
+ * num_samples or malformed offsets. */
+libra_status libra_pack_workload(const int32_t *cu_seqlens, int32_t num_samples, int64_t *workload);
+
+/* VRSP over one window.
+ *   workload   host, num_seqs values >= 0 (e.g. from libra_pack_workload);
+ *   pool_size  P > 0 dividing num_seqs;
+ *   pool_of    host out, num_seqs entries: the pool of sequence i;
+ *   order      host out, num_seqs entries: the reordered window S', the
+ *              pools in pool order (pool k fills order[k P .. k P + P - 1]),
+ *              each pool's sequences in the order they were assigned;
+ *   pool_load  host out, K entries, or NULL: each pool's summed workload.
+ * All buffers are the caller's; the call allocates nothing on the heap
+ * beyond temporaries and touches no device.  LIBRA_EINVAL on a NULL
+ * required pointer, num_seqs <= 0, pool_size <= 0, num_seqs not a multiple
+ * of pool_size or a negative workload; the outputs are then unspecified. */
+libra_status libra_vrsp(const int64_t *workload, int32_t num_seqs, int32_t pool_size, int32_t *pool_of,
+                        int32_t *order, int64_t *pool_load);
+
 /* Frequency of the clock in libra_cu_record, for the current device. */
 libra_status libra_device_clock_khz(int32_t *khz);
 

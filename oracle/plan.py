@@ -20,7 +20,7 @@ FLOPs are 4 * d per pair (two matrix products of 2 * d each).
 
 Work items (a reading: on one GPU the workers are CUs and a whole SH-Tile is
 too coarse for 256 of them).  Every tile is split into items that one
-workgroup of four 64-query waves runs:
+workgroup runs (256 query columns, positions x heads):
   * for each KV head kappa whose query heads meet the tile's shard, the heads
     H = shard ∩ group(kappa) are cut into groups of nh heads, nh = 4 if |H| is a
     multiple of 4, else 2 if even, else 1;

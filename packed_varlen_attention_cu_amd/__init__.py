@@ -93,9 +93,11 @@ def _load():
     lib.libra_status_str.restype = ctypes.c_char_p
     lib.libra_last_hip_error.argtypes = []
     lib.libra_last_hip_error.restype = ctypes.c_char_p
+    lib.libra_pack_workload.argtypes = [vp, ctypes.c_int32, vp]
+    lib.libra_vrsp.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
     for name in ("libra_plan", "libra_plan_check", "libra_attn_bwd_workspace", "libra_attn_fwd",
                  "libra_attn_bwd", "libra_device_clock_khz", "libra_attn_bwd_prepare", "libra_attn_bwd_dkdv",
-                 "libra_attn_bwd_dq"):
+                 "libra_attn_bwd_dq", "libra_pack_workload", "libra_vrsp"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -137,6 +139,27 @@ def libra_plan(cu_seqlens, params: PlanParams) -> np.ndarray:
     _check(_lib.libra_plan(cu.ctypes.data, ctypes.byref(params), buf.ctypes.data, ctypes.byref(cap)),
            "libra_plan")
     return buf
+
+
+def libra_pack_workload(cu_seqlens) -> int:
+    """Workload proxy of one packed sequence: sum of squared sample lengths."""
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    out = ctypes.c_int64(0)
+    _check(_lib.libra_pack_workload(cu.ctypes.data, len(cu) - 1, ctypes.byref(out)), "libra_pack_workload")
+    return out.value
+
+
+def libra_vrsp(workload, pool_size: int):
+    """Variance-reduced sequence placement of one window: (pool_of, order, pool_load)."""
+    f = np.ascontiguousarray(workload, dtype=np.int64)
+    n = len(f)
+    pool_of = np.empty(n, dtype=np.int32)
+    order = np.empty(n, dtype=np.int32)
+    pools = n // pool_size if pool_size > 0 else 0
+    pool_load = np.empty(max(pools, 1), dtype=np.int64)
+    _check(_lib.libra_vrsp(f.ctypes.data, n, pool_size, pool_of.ctypes.data, order.ctypes.data,
+                           pool_load.ctypes.data), "libra_vrsp")
+    return pool_of, order, pool_load[:pools]
 
 
 def libra_plan_check(buf: np.ndarray) -> PlanInfo:

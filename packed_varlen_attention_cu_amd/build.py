@@ -21,7 +21,7 @@ LIB = os.path.join(LIBDIR, "liblibra.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HOST_SOURCES = ["plan.cpp"]
+HOST_SOURCES = ["plan.cpp", "vrsp.cpp"]
 DEVICE_SOURCES = ["attn_fwd.hip", "attn_bwd.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall"]
