@@ -265,6 +265,9 @@ def summarize_counters(dirs, clock_ghz=2.4, num_cus=256):
                     out[c.replace("SQ_INSTS_", "") + " per MFMA"] = m[c] / m["SQ_INSTS_MFMA"]
         if m.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in m:
             out["VALU co-issued share of MFMA-busy cycles"] = m["SQ_VALU_MFMA_COEXEC_CYCLES"] / m["SQ_VALU_MFMA_BUSY_CYCLES"]
+        if dur and "GRBM_GUI_ACTIVE" in m:
+            # GRBM_GUI_ACTIVE sums the eight XCDs' busy clocks: their mean clock over the kernel
+            out["GPU clock GHz (GRBM_GUI_ACTIVE / 8 / duration)"] = m["GRBM_GUI_ACTIVE"] / 8 / dur / 1e9
         if dur:
             out["kernel ms (this run)"] = dur * 1e3
         return out
@@ -562,6 +565,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="DIR", help="markdown table of a rocprofv3 --kernel-trace run")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", help="markdown table of rocprofv3 --pmc runs")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="run the sustained bf16 MFMA probe (constant vs random operands, ~3 s each)")
     ap.add_argument("--vrsp", action="store_true",
                     help="host-only: variance-reduced sequence placement timing and pool balance")
     ap.add_argument("--sweep", action="store_true",
@@ -582,6 +587,12 @@ def main():
     if args.vrsp:
         vrsp_report()
         return
+    if args.mfma_ceiling:
+        import subprocess
+        probe = os.path.join(ROOT, "packed_varlen_attention_cu_amd", "_lib", "mfma_ceiling")
+        if not os.path.exists(probe):
+            sys.exit(f"{probe} is missing: build the package first")
+        sys.exit(subprocess.run([probe]).returncode)
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU sharding of this "
               "path is a design note, not part of this build.", file=sys.stderr)

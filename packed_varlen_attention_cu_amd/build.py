@@ -62,6 +62,12 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, out)
     shutil.rmtree(objdir, ignore_errors=True)
+    if os.path.abspath(out) == LIB:
+        # the sustained-MFMA probe that bench.py --mfma-ceiling runs (a measurement tool)
+        probe = os.path.join(libdir, "mfma_ceiling")
+        _run([HIPCC, "-O3", "-std=c++17", f"--offload-arch={ARCH}", os.path.join(CSRC, "mfma_ceiling.hip"),
+              "-o", probe + ".tmp"])
+        os.replace(probe + ".tmp", probe)
     return out
 
 
