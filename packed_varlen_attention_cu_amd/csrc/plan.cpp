@@ -107,10 +107,26 @@ Queue place(const std::vector<libra_item> &units, int workers, int mode) {
       int32_t idx;
     };
     std::vector<Key> keys(n);
-    for (size_t i = 0; i < n; ++i) keys[i] = {units[i].cost, (int32_t)i};
-    std::sort(keys.begin(), keys.end(), [](const Key &x, const Key &y) {
-      return x.cost != y.cost ? x.cost > y.cost : x.idx < y.idx;
-    });
+    int64_t cmax = 0;
+    for (size_t i = 0; i < n; ++i) {
+      keys[i] = {units[i].cost, (int32_t)i};
+      cmax = std::max(cmax, units[i].cost);
+    }
+    if (cmax < (int64_t(1) << 43) && n < (size_t(1) << 20)) {
+      // (cost descending, index ascending) as one ascending 64-bit key
+      std::vector<uint64_t> packed(n);
+      for (size_t i = 0; i < n; ++i)
+        packed[i] = (uint64_t)((int64_t(1) << 43) - 1 - keys[i].cost) << 20 | (uint64_t)i;
+      std::sort(packed.begin(), packed.end());
+      for (size_t k = 0; k < n; ++k) {
+        const int32_t i = (int32_t)(packed[k] & ((1u << 20) - 1));
+        keys[k] = {units[i].cost, i};
+      }
+    } else {
+      std::sort(keys.begin(), keys.end(), [](const Key &x, const Key &y) {
+        return x.cost != y.cost ? x.cost > y.cost : x.idx < y.idx;
+      });
+    }
     std::vector<Load> heap(workers);
     for (int32_t r = 0; r < workers; ++r) heap[r] = {0, r};   // ordered, hence a valid heap
     for (size_t k = 0; k < n; ++k) {
@@ -224,21 +240,21 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
   const int S = p.h_q / p.tile_heads;
   const int64_t nblocks = (L + p.tile_tokens - 1) / p.tile_tokens;
 
-  // Size query: the section lengths follow from the counts alone.
-  if (!buf) {
-    int64_t n_items = 0;
-    for (int64_t b = 0; b < nblocks; ++b) {
-      const int64_t rows_in = std::min<int64_t>(L, (b + 1) * p.tile_tokens) - b * p.tile_tokens;
-      for (int s = 0; s < S; ++s) {
-        const int h_lo = s * p.tile_heads, h_hi = h_lo + p.tile_heads;
-        for (int kv = h_lo / g; kv <= (h_hi - 1) / g; ++kv) {
-          const int hn = std::min(h_hi, (kv + 1) * g) - std::max(h_lo, kv * g);
-          const int nh = head_group(hn), rows = kItemColumns / nh;
-          n_items += (int64_t)(hn / nh) * ((rows_in + rows - 1) / rows);
-        }
+  // The section lengths follow from the counts alone.
+  int64_t n_items = 0;
+  for (int64_t b = 0; b < nblocks; ++b) {
+    const int64_t rows_in = std::min<int64_t>(L, (b + 1) * p.tile_tokens) - b * p.tile_tokens;
+    for (int s = 0; s < S; ++s) {
+      const int h_lo = s * p.tile_heads, h_hi = h_lo + p.tile_heads;
+      for (int kv = h_lo / g; kv <= (h_hi - 1) / g; ++kv) {
+        const int hn = std::min(h_hi, (kv + 1) * g) - std::max(h_lo, kv * g);
+        const int nh = head_group(hn), rows = kItemColumns / nh;
+        n_items += (int64_t)(hn / nh) * ((rows_in + rows - 1) / rows);
       }
     }
-    const int64_t n_kv = (L + kKvChunk - 1) / kKvChunk * p.h_kv;
+  }
+  const int64_t n_kv = (L + kKvChunk - 1) / kKvChunk * p.h_kv;
+  if (!buf) {   // size query
     *bytes = plan_bytes(nblocks * S, n_items, n_kv, workers);
     return LIBRA_OK;
   }
@@ -247,9 +263,17 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
   std::vector<libra_tile> tiles;
   std::vector<libra_item> items;
   tiles.reserve(nblocks * S);
+  items.reserve(n_items);
+  // Per-head pairs of the block's row chunks of each chunk length (1, 2 or 4
+  // heads per item give 256, 128 or 64 rows), computed once per block.
+  std::vector<int64_t> chunk_pairs[3];
+  auto chunks_of = [&](int rows) -> std::vector<int64_t> & {
+    return chunk_pairs[rows == kItemColumns ? 0 : rows == kItemColumns / 2 ? 1 : 2];
+  };
   int jb = 0;
   for (int64_t b = 0; b < nblocks; ++b) {
     const int64_t lo = b * p.tile_tokens, hi = std::min<int64_t>(L, lo + p.tile_tokens);
+    for (auto &v : chunk_pairs) v.clear();
     const int64_t per_head = query_pairs(cu, n, lo, hi, &jb);
     // K(t): the non-empty samples the block meets (all samples from jb end after lo).
     int first = -1, last = -1;
@@ -276,9 +300,15 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
         const int a = std::max(h_lo, kv * g), e = std::min(h_hi, (kv + 1) * g);
         const int nh = head_group(e - a);
         const int rows = kItemColumns / nh;
-        for (int gi = 0; gi < (e - a) / nh; ++gi) {
+        std::vector<int64_t> &cp = chunks_of(rows);
+        if (cp.empty()) {
           int ji = jb;
-          for (int64_t r0 = lo; r0 < hi; r0 += rows) {
+          for (int64_t r0 = lo; r0 < hi; r0 += rows)
+            cp.push_back(query_pairs(cu, n, r0, std::min<int64_t>(hi, r0 + rows), &ji));
+        }
+        for (int gi = 0; gi < (e - a) / nh; ++gi) {
+          size_t ci = 0;
+          for (int64_t r0 = lo; r0 < hi; r0 += rows, ++ci) {
             const int64_t r1 = std::min<int64_t>(hi, r0 + rows);
             libra_item it{};
             it.row0 = (int32_t)r0;
@@ -288,7 +318,7 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
             it.nheads = nh;
             it.tile_id = t.tile_id;
             it.id = (int32_t)items.size();
-            it.pairs = nh * query_pairs(cu, n, r0, r1, &ji);
+            it.pairs = nh * cp[ci];
             it.cost = it.pairs + p.item_overhead;
             items.push_back(it);
             ++made;
@@ -303,7 +333,7 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
   // Key-major dK/dV items: chunks of 128 keys, all g query heads of a KV head.
   std::vector<libra_item> kv_items;
   const int64_t nchunks = (L + kKvChunk - 1) / kKvChunk;
-  kv_items.reserve(nchunks * p.h_kv);
+  kv_items.reserve(n_kv);
   int jk = 0;
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t lo = c * kKvChunk, hi = std::min<int64_t>(L, lo + kKvChunk);
