@@ -20,9 +20,10 @@
  *       lse            : [h_q, L] fp32
  *     Device pointers must be 16-byte aligned.
  *   - The caller owns and allocates every buffer, host and device.  The
- *     library allocates nothing, keeps no global state, never synchronises,
- *     and only enqueues work on the stream it is given (a hipStream_t passed
- *     as void*; NULL is the default stream).
+ *     library allocates no device memory (the host-only planner and VRSP use
+ *     heap temporaries), keeps no state beyond the calling thread's last HIP
+ *     error, never synchronises, and only enqueues work on the stream it is
+ *     given (a hipStream_t passed as void*; NULL is the default stream).
  *   - Every argument is validated on the host before anything is enqueued;
  *     a failed check returns a negative libra_status and enqueues nothing.
  *     A launch error returns LIBRA_EHIP.  Faults inside kernels surface at

@@ -98,19 +98,13 @@ __device__ __forceinline__ uint32_t xcc_id_reg() {
   return __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 20);   // HW_REG_XCC_ID
 }
 
-// Direct global -> LDS copy of 16 bytes per lane: lane i of the wave writes
-// lds_base + 16 * i (lds_base is made wave-uniform); lanes switched off by
-// control flow write nothing.  The copy is issued from inline assembly so the
-// compiler does not track it: callers account for every copy themselves with
-// wait_vmem (the vector-memory counter retires in issue order) and a barrier
-// before another wave reads the data.
-__device__ __forceinline__ void lds_dma16(const void *gsrc, uint32_t lds_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gsrc) : "memory", "m0");
-}
-
-// The same with a wave-uniform base address (SGPR pair) and a 32-bit
-// per-lane byte offset: lane i copies 16 bytes at sbase + voff.
+// Direct global -> LDS copy of 16 bytes per lane: lane i of the wave copies
+// the 16 bytes at sbase + voff (sbase wave-uniform, in scalar registers; voff
+// the lane's 32-bit byte offset) to lds_base + 16 * i (lds_base is made
+// wave-uniform); lanes switched off by control flow copy nothing.  The copy
+// is issued from inline assembly so the compiler does not track it: callers
+// account for every copy themselves with wait_vmem (the vector-memory counter
+// retires in issue order) and a barrier before another wave reads the data.
 __device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, uint32_t lds_base) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_base);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
@@ -125,7 +119,8 @@ __device__ __forceinline__ const void *uniform_ptr(const void *p) {
   return (const void *)(((uint64_t)hi << 32) | lo);
 }
 
-// The same for 4 bytes per lane: lane i writes lds_base + 4 * i.
+// The same for 4 bytes per lane from a per-lane address: lane i copies the 4
+// bytes at gsrc to lds_base + 4 * i.
 __device__ __forceinline__ void lds_dma4(const void *gsrc, uint32_t lds_base) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_base);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gsrc) : "memory", "m0");
