@@ -93,7 +93,8 @@ typedef struct {
  *   [head0, head0 + nheads), all reading KV head kv_head; nheads is 1, 2 or 4
  *   and nrows * nheads <= 256.
  * dK/dV items (tile_id == -1): key rows [row0, row0 + nrows) of kv_head,
- *   gathering the gradient of all h_q / h_kv query heads of that KV head. */
+ *   nrows <= 192, gathering the gradient of all h_q / h_kv query heads of
+ *   that KV head. */
 typedef struct {
   int32_t row0, nrows;
   int32_t kv_head, head0, nheads;

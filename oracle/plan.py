@@ -30,9 +30,10 @@ pairs plus a fixed per-item overhead (a planner parameter).
 Items are numbered in (tile_id, kappa, head group, row chunk) order.
 
 Key-major items for the dK/dV pass: keys are cut at global positions into
-chunks of 128; item (chunk c, KV head kappa) has id c * h_kv + kappa and covers
-all g = h_q / h_kv query heads of kappa.  Its pairs count, for every key k in
-the chunk, the queries q >= k of k's sample: g * sum_k (end(k) - k).
+chunks of 192 (the dK/dV kernel's six key groups of 32); item (chunk c, KV
+head kappa) has id c * h_kv + kappa and covers all g = h_q / h_kv query heads
+of kappa.  Its pairs count, for every key k in the chunk, the queries q >= k
+of k's sample: g * sum_k (end(k) - k).
 
 Placement (Algorithm 2, section 5.4).  C = (1 + tau) * sum f / |W|.  Units go
 in order of decreasing f, then id.  Among workers whose load stays <= C the
@@ -47,7 +48,7 @@ from __future__ import annotations
 WAVES = 4
 WAVE_QUERIES = 64
 ITEM_COLUMNS = WAVES * WAVE_QUERIES      # query positions x heads per forward item
-KV_CHUNK = 128                           # keys per dK/dV item
+KV_CHUNK = 192                           # keys per dK/dV item
 
 
 def _ranges(cu):

@@ -92,13 +92,15 @@ __device__ __forceinline__ void write_record(const BwdArgs &a, int w, int n, uin
 }
 
 // ----------------------------------------------------------------- dK / dV pass
-// Eight waves, two per SIMD.  The 128 keys of an item are split into four
-// groups of 32; each group has a P wave (waves 0-3: S = Q K^T, P, dV^T +=
-// dO^T P) and a dS wave (waves 4-7: dP = dO V^T, dS = P * (dP - D),
-// dK^T += Q^T dS) on the same SIMD.  The P wave publishes its bf16 P through
-// LDS halfway through each step, so while one wave of a SIMD runs matrix
-// products the other runs its element-wise work.  Only the P wave applies the
-// block-diagonal mask: masked P is 0, hence masked dS is 0 too.
+// Twelve waves, three per SIMD.  The 192 keys of an item are split into six
+// groups of 32; each group has a P wave (waves 0-5: S = Q K^T, P, dV^T +=
+// dO^T P) and a dS wave (waves 6-11: dP = dO V^T, dS = P * (dP - D),
+// dK^T += Q^T dS).  The P wave publishes its bf16 P through LDS halfway
+// through each step, so the matrix products of some waves of a SIMD overlap
+// the element-wise work of others.  Only the P wave applies the
+// block-diagonal mask: masked P is 0, hence masked dS is 0 too.  Three waves
+// per SIMD leave each 168 registers, which the kernel fits in; the larger
+// item shares each Q and dO block among 192 keys instead of 128.
 //
 // Per query block of kQB rows and one head, LDS holds Q and dO (row-major:
 // A operands of S and dP directly, and of dK^T and dV^T through transposing
@@ -106,17 +108,20 @@ __device__ __forceinline__ void write_record(const BwdArgs &a, int w, int n, uin
 // rotate: after one barrier the copies for the step kStages - 1 ahead are
 // queued into the buffer the previous step used, and the current one is
 // computed while they fly.  Blocks use padded rows (PadRows).
-constexpr int kDkdvWaves = 8;
+constexpr int kDkdvGroups = kKvItemKeys / 32;   // key groups of 32
+constexpr int kDkdvWaves = 2 * kDkdvGroups;      // a P wave and a dS wave per group
+static_assert(kDkdvWaves % 4 == 0, "whole waves per SIMD");
 
 template <int D>
 struct DkdvLds {
   static constexpr int kRow = kQB * PadRows<D>::kStride;   // elements of one padded block
   static constexpr int kBuf = 2 * kRow + 2 * kQB * 2;      // Q, dO + LSE and D (fp32), in uint16 units
-  static constexpr int kP = 4 * 32 * kQB;                  // bf16 P of the four key groups
+  static constexpr int kP = kDkdvGroups * 32 * kQB;       // bf16 P of every key group
 };
 
 template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kDkdvWaves * 64, kDkdvWaves * 64), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kDkdvWaves * 64, kDkdvWaves * 64),
+                         amdgpu_waves_per_eu(kDkdvWaves / 4, kDkdvWaves / 4)))
 void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NW = kDkdvWaves;
   constexpr int NS = D / 16, ND = D / 32;
@@ -128,7 +133,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int half = lane >> 5, col = lane & 31;
-  const int kg = wave & 3;                         // key group
+  const int kg = wave % kDkdvGroups;               // key group
   const int w = blockIdx.x;
   const uint64_t t_start = wall_clock64();
   const int beg = a.cu_off[w], end = a.cu_off[w + 1];
@@ -140,7 +145,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int64_t q_stride = (int64_t)a.h_q * D;
   RowCopy<D, kQB, NW> qcopy;
   qcopy.init(wave, lane, q_stride);
-  const int copies = 2 * RowCopy<D, kQB, NW>::count(wave) + 1;   // this wave's copies per step
+  const bool rowvec = wave * 16 < 2 * kQB;         // the wave copies 16 LSE / D values
+  const int copies = 2 * RowCopy<D, kQB, NW>::count(wave) + (rowvec ? 1 : 0);   // this wave's copies per step
 
   // The two roles are separate instantiations, so each allocates registers
   // for its own path only; both pass the same barriers.
@@ -177,8 +183,9 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
         const uint32_t dst = q_base + buf * 2 * DkdvLds<D>::kBuf;   // bytes
         qcopy.issue(dst, wave, a.q + h * D, q_stride, q0, a.L);
         qcopy.issue(dst + 2 * ROW, wave, a.dout + h * D, q_stride, q0, a.L);   // byte offsets
-        // LSE * log2(e) then D of the block's queries: lanes 0..15 of each wave copy 16 values.
-        if (lane < 16) {
+        // LSE * log2(e) then D of the block's queries: lanes 0..15 of the first
+        // 2 kQB / 16 waves copy 16 values each.
+        if (rowvec && lane < 16) {
           const int e = wave * 16 + lane;             // 0 .. 2 kQB - 1
           const int qq = min(q0 + (e & (kQB - 1)), a.L - 1);
           const float *src = (e < kQB ? a.lse2 : a.dvec) + (int64_t)h * a.L + qq;
@@ -340,7 +347,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
       }
     }
   };
-  if (wave < 4) run(std::true_type{});
+  if (wave < kDkdvGroups) run(std::true_type{});
   else run(std::false_type{});
   __syncthreads();
   if (a.records != nullptr && tid == 0) write_record(a, w, end - beg, t_start);

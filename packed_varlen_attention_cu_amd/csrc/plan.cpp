@@ -30,7 +30,7 @@
 namespace {
 
 constexpr int kItemColumns = 256;   // query positions x heads per forward / dQ item
-constexpr int kKvChunk = 128;       // keys per dK/dV item
+constexpr int kKvChunk = libra::kKvItemKeys;   // keys per dK/dV item
 constexpr int kDefaultCus = 256;
 constexpr int kMaxCus = 1 << 16;
 
@@ -330,7 +330,7 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
     }
   }
 
-  // Key-major dK/dV items: chunks of 128 keys, all g query heads of a KV head.
+  // Key-major dK/dV items: chunks of kKvChunk keys, all g query heads of a KV head.
   std::vector<libra_item> kv_items;
   const int64_t nchunks = (L + kKvChunk - 1) / kKvChunk;
   kv_items.reserve(n_kv);

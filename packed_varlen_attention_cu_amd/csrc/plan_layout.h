@@ -7,6 +7,9 @@
 
 namespace libra {
 
+// Keys per dK/dV work item: the dK/dV kernel's six key groups of 32 keys.
+constexpr int kKvItemKeys = 192;
+
 // Checksum stored in libra_plan_info::checksum (computed with that field as 0).
 uint64_t plan_checksum(const void *plan, size_t bytes);
 
