@@ -33,7 +33,11 @@ Key-major items for the dK/dV pass: keys are cut at global positions into
 chunks of 192 (the dK/dV kernel's six key groups of 32); item (chunk c, KV
 head kappa) has id c * h_kv + kappa and covers all g = h_q / h_kv query heads
 of kappa.  Its pairs count, for every key k in the chunk, the queries q >= k
-of k's sample: g * sum_k (end(k) - k).
+of k's sample: g * sum_k (end(k) - k).  Its cost (a reading: the pages
+define no cost for backward work) is the work the dK/dV kernel executes for
+it, masked or not: g heads x the query blocks of 64 rows from the chunk's
+first key rounded down to a multiple of 64 up to the end of the sample of its
+last key x 64 rows x its keys.
 
 Placement (Algorithm 2, section 5.4).  C = (1 + tau) * sum f / |W|.  Units go
 in order of decreasing f, then id.  Among workers whose load stays <= C the
@@ -49,6 +53,7 @@ WAVES = 4
 WAVE_QUERIES = 64
 ITEM_COLUMNS = WAVES * WAVE_QUERIES      # query positions x heads per forward item
 KV_CHUNK = 192                           # keys per dK/dV item
+KV_QUERY_BLOCK = 64                      # query rows per step of the dK/dV kernel
 
 
 def _ranges(cu):
@@ -141,10 +146,14 @@ def kv_items(cu, total_tokens, h_q, h_kv, overhead=0) -> list:
         for s, e in ranges:
             a, b = max(lo, s), min(hi, e)
             per_head += sum(e - k for k in range(a, b))
+        last_end = next(e for s, e in ranges if s <= hi - 1 < e)   # the last key's sample
+        q_first = lo - lo % KV_QUERY_BLOCK
+        q_blocks = -(-(last_end - q_first) // KV_QUERY_BLOCK)
+        executed = g * q_blocks * KV_QUERY_BLOCK * (hi - lo)
         for kappa in range(h_kv):
             items.append(dict(id=len(items), tile_id=-1, row0=lo, nrows=hi - lo, kv_head=kappa,
                               head0=kappa * g, nheads=g, pairs=g * per_head,
-                              cost=g * per_head + overhead))
+                              cost=executed + overhead))
     return items
 
 

@@ -34,7 +34,7 @@ namespace libra {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kQB = 64;      // query rows per block in the dK/dV pass
+constexpr int kQB = kKvQueryBlock;   // query rows per block in the dK/dV pass
 constexpr int kStages = 3;   // LDS buffers: copies run kStages - 1 blocks ahead
 constexpr int kKB = 64;      // key rows per block in the dQ pass
 

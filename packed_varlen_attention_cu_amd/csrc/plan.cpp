@@ -59,6 +59,12 @@ int64_t key_pairs(const int32_t *cu, int n, int64_t lo, int64_t hi, int *j) {
   return pairs;
 }
 
+// End of the non-empty sample holding position pos; `j` walks forward over samples.
+int64_t sample_end(const int32_t *cu, int n, int64_t pos, int *j) {
+  while (*j < n && cu[*j + 1] <= pos) ++*j;
+  return cu[*j + 1];
+}
+
 int head_group(int n) { return n % 4 == 0 ? 4 : (n % 2 == 0 ? 2 : 1); }
 
 libra_status validate(const int32_t *cu, const libra_plan_params *p) {
@@ -330,14 +336,23 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
     }
   }
 
-  // Key-major dK/dV items: chunks of kKvChunk keys, all g query heads of a KV head.
+  // Key-major dK/dV items: chunks of kKvChunk keys, all g query heads of a KV
+  // head.  Their cost is the work the dK/dV kernel executes, not the causal
+  // pairs: every step runs a whole query block of kKvQueryBlock rows against
+  // all of the item's keys, masked or not, and a step's time hardly depends
+  // on how many of its pairs the mask keeps (per-CU busy time follows the
+  // step count, not the pair count).
   std::vector<libra_item> kv_items;
   const int64_t nchunks = (L + kKvChunk - 1) / kKvChunk;
   kv_items.reserve(n_kv);
-  int jk = 0;
+  int jk = 0, je = 0;
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t lo = c * kKvChunk, hi = std::min<int64_t>(L, lo + kKvChunk);
     const int64_t per_head = key_pairs(cu, n, lo, hi, &jk);
+    const int64_t qstart = lo / libra::kKvQueryBlock * libra::kKvQueryBlock;
+    const int64_t qblocks = (sample_end(cu, n, hi - 1, &je) - qstart + libra::kKvQueryBlock - 1) /
+                            libra::kKvQueryBlock;
+    const int64_t executed = g * qblocks * libra::kKvQueryBlock * (hi - lo);
     for (int kv = 0; kv < p.h_kv; ++kv) {
       libra_item it{};
       it.row0 = (int32_t)lo;
@@ -348,7 +363,7 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
       it.tile_id = -1;
       it.id = (int32_t)kv_items.size();
       it.pairs = g * per_head;
-      it.cost = it.pairs + p.item_overhead;
+      it.cost = executed + p.item_overhead;
       kv_items.push_back(it);
     }
   }

@@ -9,6 +9,10 @@ namespace libra {
 
 // Keys per dK/dV work item: the dK/dV kernel's six key groups of 32 keys.
 constexpr int kKvItemKeys = 192;
+// Query rows per step of the dK/dV kernel: a step runs one query block of
+// this many rows (from the item's first key rounded down to a multiple of
+// it, to the end of its last key's sample) against all of the item's keys.
+constexpr int kKvQueryBlock = 64;
 
 // Checksum stored in libra_plan_info::checksum (computed with that field as 0).
 uint64_t plan_checksum(const void *plan, size_t bytes);
