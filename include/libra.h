@@ -58,7 +58,7 @@ enum {
 };
 
 #define LIBRA_PLAN_MAGIC 0x4152424Cu   /* "LBRA" little-endian */
-#define LIBRA_PLAN_VERSION 1u
+#define LIBRA_PLAN_VERSION 2u
 
 /* Planner inputs.  SH-Tiles (Libra technical review, section 5.1, eq. 6)
  * are tile_tokens (B) tokens by tile_heads (W = h_q / H) query heads. */
@@ -89,9 +89,9 @@ typedef struct {
 } libra_tile;
 
 /* One unit of work for one persistent workgroup.
- * Forward / dQ items: query rows [row0, row0 + nrows) of heads
+ * Forward and dQ items: query rows [row0, row0 + nrows) of heads
  *   [head0, head0 + nheads), all reading KV head kv_head; nheads is 1, 2 or 4
- *   and nrows * nheads <= 256.
+ *   and nrows * nheads <= 384 (forward) or 256 (dQ).
  * dK/dV items (tile_id == -1): key rows [row0, row0 + nrows) of kv_head,
  *   nrows <= 192, gathering the gradient of all h_q / h_kv query heads of
  *   that KV head. */
@@ -106,19 +106,23 @@ typedef struct {
 } libra_item;
 
 /* Header at offset 0 of every plan buffer.  Sections follow at the given
- * byte offsets: tiles[n_tiles]; items[n_items] grouped by CU in placement
- * order with cu_off[num_cus + 1] (CSR); the same for the dK/dV queue. */
+ * byte offsets: tiles[n_tiles]; the forward queue, items[n_items] grouped by
+ * CU in placement order with cu_off[num_cus + 1] (CSR); the same for the dQ
+ * queue and for the dK/dV queue. */
 typedef struct {
   uint32_t magic, version;
   uint64_t bytes;
   libra_plan_params params;
   int32_t num_cus;                  /* resolved worker count */
-  int32_t n_tiles, n_items, n_kv_items;
+  int32_t n_tiles, n_items, n_dq_items, n_kv_items, reserved;
   int64_t total_pairs;              /* sum of tile pairs = h_q * sum_j l_j (l_j + 1) / 2 */
-  int64_t load_max, load_sum;       /* per-CU cost of the forward/dQ queue */
+  int64_t load_max, load_sum;       /* per-CU cost of the forward queue */
+  int64_t dq_load_max, dq_load_sum; /* per-CU cost of the dQ queue */
   int64_t kv_load_max, kv_load_sum; /* per-CU cost of the dK/dV queue */
-  uint64_t off_tiles, off_items, off_cu_off, off_kv_items, off_kv_cu_off;
-  uint64_t checksum;                /* FNV-1a over 64-bit words, this field as 0 */
+  uint64_t off_tiles, off_items, off_cu_off, off_dq_items, off_dq_cu_off, off_kv_items, off_kv_cu_off;
+  uint64_t checksum;                /* FNV-1a over 64-bit words in four interleaved streams
+                                       (word i feeds stream i mod 4), folded in order; this
+                                       field taken as 0 */
 } libra_plan_info;
 
 /* Per-workgroup record of a persistent kernel (optional output).  hw_id and

@@ -20,11 +20,13 @@ FLOPs are 4 * d per pair (two matrix products of 2 * d each).
 
 Work items (a reading: on one GPU the workers are CUs and a whole SH-Tile is
 too coarse for 256 of them).  Every tile is split into items that one
-workgroup runs (256 query columns, positions x heads):
+workgroup runs, of at most c query columns (positions x heads): c = 384 for
+the forward kernel, c = 256 for the dQ kernel, which cuts the same tiles into
+its own items and places them the same way:
   * for each KV head kappa whose query heads meet the tile's shard, the heads
     H = shard ∩ group(kappa) are cut into groups of nh heads, nh = 4 if |H| is a
     multiple of 4, else 2 if even, else 1;
-  * each head group takes the tile's rows in chunks of 256 / nh positions.
+  * each head group takes the tile's rows in chunks of c / nh positions.
 An item's pairs are eq. 8 restricted to its rows and heads; its cost is its
 pairs plus a fixed per-item overhead (a planner parameter).
 Items are numbered in (tile_id, kappa, head group, row chunk) order.
@@ -49,9 +51,8 @@ worker runs its units in the order they were placed.  The round-robin mode
 """
 from __future__ import annotations
 
-WAVES = 4
-WAVE_QUERIES = 64
-ITEM_COLUMNS = WAVES * WAVE_QUERIES      # query positions x heads per forward item
+ITEM_COLUMNS = 384                       # query positions x heads per forward item
+DQ_ITEM_COLUMNS = 256                    # query positions x heads per dQ item
 KV_CHUNK = 192                           # keys per dK/dV item
 KV_QUERY_BLOCK = 64                      # query rows per step of the dK/dV kernel
 
@@ -113,8 +114,8 @@ def _head_group_size(n: int) -> int:
     return 1
 
 
-def fwd_items(cu, total_tokens, h_q, h_kv, B, W, overhead=0) -> list:
-    """Forward / dQ work items in id order."""
+def fwd_items(cu, total_tokens, h_q, h_kv, B, W, overhead=0, columns=ITEM_COLUMNS) -> list:
+    """Forward work items in id order (dQ items: columns=DQ_ITEM_COLUMNS)."""
     g = h_q // h_kv
     ranges = _ranges(cu)
     items = []
@@ -123,7 +124,7 @@ def fwd_items(cu, total_tokens, h_q, h_kv, B, W, overhead=0) -> list:
         for kappa in range(h_lo // g, (h_hi - 1) // g + 1):
             heads = list(range(max(h_lo, kappa * g), min(h_hi, (kappa + 1) * g)))
             nh = _head_group_size(len(heads))
-            rows = ITEM_COLUMNS // nh
+            rows = columns // nh
             for gi in range(len(heads) // nh):
                 for r0 in range(t["tok_begin"], t["tok_end"], rows):
                     r1 = min(t["tok_end"], r0 + rows)

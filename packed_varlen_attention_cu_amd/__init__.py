@@ -43,11 +43,14 @@ class PlanParams(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32), ("bytes", ctypes.c_uint64),
                 ("params", PlanParams), ("num_cus", ctypes.c_int32), ("n_tiles", ctypes.c_int32),
-                ("n_items", ctypes.c_int32), ("n_kv_items", ctypes.c_int32),
+                ("n_items", ctypes.c_int32), ("n_dq_items", ctypes.c_int32), ("n_kv_items", ctypes.c_int32),
+                ("reserved", ctypes.c_int32),
                 ("total_pairs", ctypes.c_int64), ("load_max", ctypes.c_int64),
-                ("load_sum", ctypes.c_int64), ("kv_load_max", ctypes.c_int64),
+                ("load_sum", ctypes.c_int64), ("dq_load_max", ctypes.c_int64),
+                ("dq_load_sum", ctypes.c_int64), ("kv_load_max", ctypes.c_int64),
                 ("kv_load_sum", ctypes.c_int64), ("off_tiles", ctypes.c_uint64),
                 ("off_items", ctypes.c_uint64), ("off_cu_off", ctypes.c_uint64),
+                ("off_dq_items", ctypes.c_uint64), ("off_dq_cu_off", ctypes.c_uint64),
                 ("off_kv_items", ctypes.c_uint64), ("off_kv_cu_off", ctypes.c_uint64),
                 ("checksum", ctypes.c_uint64)]
 
@@ -62,7 +65,7 @@ ITEM_DTYPE = np.dtype([("row0", "<i4"), ("nrows", "<i4"), ("kv_head", "<i4"), ("
 RECORD_DTYPE = np.dtype([("hw_id", "<u4"), ("xcc_id", "<u4"), ("n_items", "<u4"), ("reserved", "<u4"),
                          ("t_start", "<u8"), ("t_end", "<u8")])
 
-assert ctypes.sizeof(PlanParams) == 48 and ctypes.sizeof(PlanInfo) == 168
+assert ctypes.sizeof(PlanParams) == 48 and ctypes.sizeof(PlanInfo) == 208
 assert TILE_DTYPE.itemsize == 48 and ITEM_DTYPE.itemsize == 48 and RECORD_DTYPE.itemsize == 32
 
 
@@ -133,7 +136,7 @@ def libra_plan(cu_seqlens, params: PlanParams) -> np.ndarray:
     cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
     need = ctypes.c_size_t(0)
     _check(_lib.libra_plan(cu.ctypes.data, ctypes.byref(params), None, ctypes.byref(need)), "libra_plan")
-    words = np.zeros((need.value + 7) // 8, dtype=np.uint64)
+    words = np.empty((need.value + 7) // 8, dtype=np.uint64)   # the library fills every byte
     buf = words.view(np.uint8)[:need.value]
     cap = ctypes.c_size_t(need.value)
     _check(_lib.libra_plan(cu.ctypes.data, ctypes.byref(params), buf.ctypes.data, ctypes.byref(cap)),
@@ -230,7 +233,8 @@ class Plan:
                                  int(item_overhead))
         self.cu_seqlens = cu
         self.host = libra_plan(cu, self.params)
-        self.info = libra_plan_check(self.host)
+        # the header of a buffer the library just built (libra_plan_check verifies foreign ones)
+        self.info = PlanInfo.from_buffer_copy(self.host[:ctypes.sizeof(PlanInfo)].tobytes())
         self._dev = {}
 
     def _section(self, off, count, dtype):
@@ -247,6 +251,14 @@ class Plan:
     @property
     def cu_off(self):
         return self._section(self.info.off_cu_off, self.info.num_cus + 1, np.dtype("<i4"))
+
+    @property
+    def dq_items(self):
+        return self._section(self.info.off_dq_items, self.info.n_dq_items, ITEM_DTYPE)
+
+    @property
+    def dq_cu_off(self):
+        return self._section(self.info.off_dq_cu_off, self.info.num_cus + 1, np.dtype("<i4"))
 
     @property
     def kv_items(self):

@@ -24,7 +24,7 @@ ARCH = "gfx950"
 HOST_SOURCES = ["plan.cpp", "vrsp.cpp"]
 DEVICE_SOURCES = ["attn_fwd.hip", "attn_bwd.hip"]
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-I", INCLUDE, "-I", CSRC, "-Wall"]
 # Packed fp32 VALU forms are kept out of the generated code on purpose.
 DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-munsafe-fp-atomics",
@@ -59,7 +59,7 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
                 print(r.stdout, r.stderr, file=sys.stderr)
     objs = [os.path.join(objdir, s + ".o") for s in HOST_SOURCES + DEVICE_SOURCES]
     tmp = out + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp])
     os.replace(tmp, out)
     shutil.rmtree(objdir, ignore_errors=True)
     if os.path.abspath(out) == LIB:

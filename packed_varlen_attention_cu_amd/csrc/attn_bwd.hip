@@ -9,12 +9,13 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Work is split into two deterministic persistent passes (no atomics):
-//   * key-major dK/dV: an item is 128 keys of one KV head; pairs of waves own
+//   * key-major dK/dV: an item is 192 keys of one KV head; pairs of waves own
 //     32 keys each and walk every query block of every query head of the group
 //     that can see them, accumulating dK^T and dV^T in registers (GQA heads
 //     are summed in place);
-//   * query-major dQ: the forward's items and CU assignment, each wave owning
-//     32 query positions of one head and walking its key blocks.
+//   * query-major dQ: items cut from the forward's SH-Tiles (256 query
+//     columns each, the forward's are 384) and placed like them, each wave
+//     owning 32 query positions of one head and walking its key blocks.
 // Operand blocks are copied straight from HBM into LDS; operands that need
 // the transposed layout (Q^T, dO^T, K^T) come from transposing LDS reads of
 // the row-major blocks.  A first phase computes D = rowsum(dO * O) (fp32)
@@ -354,12 +355,13 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------- dQ pass
-// Eight waves of 32 query positions each cover the 256 query columns of a
-// forward work item (two waves per SIMD).  Per key block of kKB keys, LDS
+// Eight waves of 32 query positions each cover the kDqItemColumns query
+// columns of a dQ work item (two waves per SIMD: the kernel needs more than
+// the 168 registers three would leave).  Per key block of kKB keys, LDS
 // holds K and V (row-major: A operands of S^T and dP^T, and through
 // transposing reads the K^T operand of dQ^T), in a ring of kStages buffers
 // like the forward; all query heads of the item's KV head read the same copy.
-constexpr int kDqWaves = 8;
+constexpr int kDqWaves = kDqItemColumns / 32;
 
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kDqWaves * 64, kDqWaves * 64), amdgpu_waves_per_eu(2, 2)))
@@ -621,8 +623,8 @@ libra_status launch_dkdv(const libra_plan_info &h, BwdArgs a, const void *plan_d
 libra_status launch_dq(const libra_plan_info &h, BwdArgs a, const void *plan_dev, void *dq,
                        libra_cu_record *records, void *stream) {
   const char *pd = static_cast<const char *>(plan_dev);
-  a.items = reinterpret_cast<const libra_item *>(pd + h.off_items);
-  a.cu_off = reinterpret_cast<const int32_t *>(pd + h.off_cu_off);
+  a.items = reinterpret_cast<const libra_item *>(pd + h.off_dq_items);
+  a.cu_off = reinterpret_cast<const int32_t *>(pd + h.off_dq_cu_off);
   a.dq = static_cast<uint16_t *>(dq);
   a.records = records;
   hipStream_t s = static_cast<hipStream_t>(stream);

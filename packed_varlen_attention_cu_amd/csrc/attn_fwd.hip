@@ -3,8 +3,8 @@
 // One persistent workgroup per CU runs the queue of work items the host
 // planner assigned to it (Libra technical review, section 5.4: placement is
 // decided on the host, the device only executes it).  A work item is up to
-// 256 query columns (positions x heads) of one KV head; each of the eight
-// waves owns 32 query positions of one query head (two waves per SIMD).
+// 384 query columns (positions x heads) of one KV head; each of the twelve
+// waves owns 32 query positions of one query head (three waves per SIMD).
 //
 // Per item the workgroup walks key blocks of 64 from the start of the sample
 // holding the item's first row to its last row.  K and V blocks are copied
@@ -49,16 +49,15 @@ struct FwdArgs {
   float scale_log2;
 };
 
-// Workgroup shape of the forward kernel: kFwdWaves waves, each owning
-// 32 * kFwdQT query positions of one head, so a workgroup covers the 256 query
-// columns of one work item.  Eight waves of 32 queries run two waves per SIMD,
-// so one wave's softmax (VALU) overlaps the other's matrix products (MFMA).
-#ifndef LIBRA_FWD_WAVES
-#define LIBRA_FWD_WAVES 8
-#endif
-constexpr int kFwdWaves = LIBRA_FWD_WAVES;
-constexpr int kFwdQT = 8 / kFwdWaves;             // 32-query tiles per wave
-static_assert(kFwdWaves * 32 * kFwdQT == 256, "a work item is 256 query columns");
+// Workgroup shape of the forward kernel: kFwdWaves waves, each owning 32
+// query positions of one head, so a workgroup covers the kFwdItemColumns query
+// columns of one work item.  Twelve waves run three per SIMD: the kernel fits
+// in the 168 registers that leaves, the softmax of some waves overlaps the
+// matrix products of others, and each K/V block copied into LDS serves 384
+// query columns.
+constexpr int kFwdQT = 1;                          // 32-query tiles per wave
+constexpr int kFwdWaves = kFwdItemColumns / 32;
+static_assert(kFwdWaves % 4 == 0, "whole waves per SIMD");
 
 // Exponent slack of the online softmax: the running maximum m (log2 units)
 // is only raised when a block's maximum exceeds it by more than this, so O is

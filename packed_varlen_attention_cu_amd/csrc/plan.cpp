@@ -22,6 +22,7 @@
 #include <cstring>
 #include <functional>
 #include <queue>
+#include <thread>
 #include <vector>
 
 #include "libra.h"
@@ -29,7 +30,8 @@
 
 namespace {
 
-constexpr int kItemColumns = 256;   // query positions x heads per forward / dQ item
+constexpr int kFwdItemColumns = libra::kFwdItemColumns;   // query columns per forward item
+constexpr int kDqItemColumns = libra::kDqItemColumns;     // query columns per dQ item
 constexpr int kKvChunk = libra::kKvItemKeys;   // keys per dK/dV item
 constexpr int kDefaultCus = 256;
 constexpr int kMaxCus = 1 << 16;
@@ -178,8 +180,10 @@ Queue place(const std::vector<libra_item> &units, int workers, int mode) {
 size_t align64(size_t x) { return (x + 63) & ~size_t(63); }
 
 // Byte offsets of the plan sections (written into hdr when it is not null)
-// and the total size: header, tiles, items, cu_off, kv items, kv cu_off.
-size_t section_offsets(size_t n_tiles, size_t n_items, size_t n_kv, int workers, libra_plan_info *hdr) {
+// and the total size: header, tiles, items, cu_off, dQ items, dQ cu_off,
+// kv items, kv cu_off.
+size_t section_offsets(size_t n_tiles, size_t n_items, size_t n_dq, size_t n_kv, int workers,
+                       libra_plan_info *hdr) {
   libra_plan_info tmp{};
   libra_plan_info &h = hdr ? *hdr : tmp;
   size_t off = align64(sizeof(libra_plan_info));
@@ -189,6 +193,10 @@ size_t section_offsets(size_t n_tiles, size_t n_items, size_t n_kv, int workers,
   off = align64(off + n_items * sizeof(libra_item));
   h.off_cu_off = off;
   off = align64(off + (workers + 1) * sizeof(int32_t));
+  h.off_dq_items = off;
+  off = align64(off + n_dq * sizeof(libra_item));
+  h.off_dq_cu_off = off;
+  off = align64(off + (workers + 1) * sizeof(int32_t));
   h.off_kv_items = off;
   off = align64(off + n_kv * sizeof(libra_item));
   h.off_kv_cu_off = off;
@@ -196,18 +204,33 @@ size_t section_offsets(size_t n_tiles, size_t n_items, size_t n_kv, int workers,
   return off;
 }
 
-size_t plan_bytes(int64_t n_tiles, int64_t n_items, int64_t n_kv, int workers) {
-  return section_offsets((size_t)n_tiles, (size_t)n_items, (size_t)n_kv, workers, nullptr);
+size_t plan_bytes(int64_t n_tiles, int64_t n_items, int64_t n_dq, int64_t n_kv, int workers) {
+  return section_offsets((size_t)n_tiles, (size_t)n_items, (size_t)n_dq, (size_t)n_kv, workers, nullptr);
 }
 
+// FNV-1a over 64-bit words, run as four interleaved streams (words i mod 4)
+// that are folded together at the end, so the multiplies overlap.
 uint64_t fnv1a_words(const void *buf, size_t bytes) {
   const uint64_t *w = static_cast<const uint64_t *>(buf);
-  uint64_t h = 0xcbf29ce484222325ull;
-  for (size_t i = 0; i < bytes / 8; ++i) {
-    h ^= w[i];
-    h *= 0x100000001b3ull;
+  const size_t n = bytes / 8;
+  uint64_t h[4] = {0xcbf29ce484222325ull, 0xcbf29ce484222325ull ^ 1, 0xcbf29ce484222325ull ^ 2,
+                   0xcbf29ce484222325ull ^ 3};
+  size_t i = 0;
+  for (; i + 4 <= n; i += 4)
+    for (int s = 0; s < 4; ++s) {
+      h[s] ^= w[i + s];
+      h[s] *= 0x100000001b3ull;
+    }
+  for (; i < n; ++i) {
+    h[0] ^= w[i];
+    h[0] *= 0x100000001b3ull;
   }
-  return h;
+  uint64_t r = h[0];
+  for (int s = 1; s < 4; ++s) {
+    r ^= h[s];
+    r *= 0x100000001b3ull;
+  }
+  return r;
 }
 
 }  // namespace
@@ -246,40 +269,85 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
   const int S = p.h_q / p.tile_heads;
   const int64_t nblocks = (L + p.tile_tokens - 1) / p.tile_tokens;
 
-  // The section lengths follow from the counts alone.
-  int64_t n_items = 0;
-  for (int64_t b = 0; b < nblocks; ++b) {
-    const int64_t rows_in = std::min<int64_t>(L, (b + 1) * p.tile_tokens) - b * p.tile_tokens;
-    for (int s = 0; s < S; ++s) {
-      const int h_lo = s * p.tile_heads, h_hi = h_lo + p.tile_heads;
-      for (int kv = h_lo / g; kv <= (h_hi - 1) / g; ++kv) {
-        const int hn = std::min(h_hi, (kv + 1) * g) - std::max(h_lo, kv * g);
-        const int nh = head_group(hn), rows = kItemColumns / nh;
-        n_items += (int64_t)(hn / nh) * ((rows_in + rows - 1) / rows);
+  // Work items a tile is cut into for a kernel whose workgroup covers
+  // `columns` query columns (positions x heads).
+  auto count_items = [&](int columns) {
+    int64_t count = 0;
+    for (int64_t b = 0; b < nblocks; ++b) {
+      const int64_t rows_in = std::min<int64_t>(L, (b + 1) * p.tile_tokens) - b * p.tile_tokens;
+      for (int s = 0; s < S; ++s) {
+        const int h_lo = s * p.tile_heads, h_hi = h_lo + p.tile_heads;
+        for (int kv = h_lo / g; kv <= (h_hi - 1) / g; ++kv) {
+          const int hn = std::min(h_hi, (kv + 1) * g) - std::max(h_lo, kv * g);
+          const int nh = head_group(hn), rows = columns / nh;
+          count += (int64_t)(hn / nh) * ((rows_in + rows - 1) / rows);
+        }
       }
     }
-  }
+    return count;
+  };
+  // The section lengths follow from the counts alone.
+  const int64_t n_items = count_items(kFwdItemColumns), n_dq = count_items(kDqItemColumns);
   const int64_t n_kv = (L + kKvChunk - 1) / kKvChunk * p.h_kv;
   if (!buf) {   // size query
-    *bytes = plan_bytes(nblocks * S, n_items, n_kv, workers);
+    *bytes = plan_bytes(nblocks * S, n_items, n_dq, n_kv, workers);
     return LIBRA_OK;
   }
 
-  // Tiles (eq. 6-8) and forward items.
+  // Tiles (eq. 6-8), forward items and dQ items.
   std::vector<libra_tile> tiles;
-  std::vector<libra_item> items;
+  std::vector<libra_item> items, dq_items;
   tiles.reserve(nblocks * S);
   items.reserve(n_items);
-  // Per-head pairs of the block's row chunks of each chunk length (1, 2 or 4
-  // heads per item give 256, 128 or 64 rows), computed once per block.
-  std::vector<int64_t> chunk_pairs[3];
-  auto chunks_of = [&](int rows) -> std::vector<int64_t> & {
-    return chunk_pairs[rows == kItemColumns ? 0 : rows == kItemColumns / 2 ? 1 : 2];
-  };
+  dq_items.reserve(n_dq);
+  // Per-head pairs of a block's row chunks of one length, computed once per
+  // block and chunk length.
+  std::vector<std::pair<int, std::vector<int64_t>>> chunk_pairs;
   int jb = 0;
+  // Cut tile t (rows [lo, hi) of block b, whose first sample is jb) into
+  // items of at most `columns` query columns, appended to `out`; returns how
+  // many.
+  auto cut = [&](const libra_tile &t, int64_t lo, int64_t hi, int columns, std::vector<libra_item> &out) {
+    const int h_lo = t.head_begin, h_hi = h_lo + t.head_count;
+    int32_t made = 0;
+    for (int kv = h_lo / g; kv <= (h_hi - 1) / g; ++kv) {
+      const int a = std::max(h_lo, kv * g), e = std::min(h_hi, (kv + 1) * g);
+      const int nh = head_group(e - a);
+      const int rows = columns / nh;
+      std::vector<int64_t> *cp = nullptr;
+      for (auto &c : chunk_pairs)
+        if (c.first == rows) cp = &c.second;
+      if (!cp) {
+        chunk_pairs.emplace_back(rows, std::vector<int64_t>());
+        cp = &chunk_pairs.back().second;
+        int ji = jb;
+        for (int64_t r0 = lo; r0 < hi; r0 += rows)
+          cp->push_back(query_pairs(cu, n, r0, std::min<int64_t>(hi, r0 + rows), &ji));
+      }
+      for (int gi = 0; gi < (e - a) / nh; ++gi) {
+        size_t ci = 0;
+        for (int64_t r0 = lo; r0 < hi; r0 += rows, ++ci) {
+          const int64_t r1 = std::min<int64_t>(hi, r0 + rows);
+          libra_item it{};
+          it.row0 = (int32_t)r0;
+          it.nrows = (int32_t)(r1 - r0);
+          it.kv_head = kv;
+          it.head0 = a + gi * nh;
+          it.nheads = nh;
+          it.tile_id = t.tile_id;
+          it.id = (int32_t)out.size();
+          it.pairs = nh * (*cp)[ci];
+          it.cost = it.pairs + p.item_overhead;
+          out.push_back(it);
+          ++made;
+        }
+      }
+    }
+    return made;
+  };
   for (int64_t b = 0; b < nblocks; ++b) {
     const int64_t lo = b * p.tile_tokens, hi = std::min<int64_t>(L, lo + p.tile_tokens);
-    for (auto &v : chunk_pairs) v.clear();
+    chunk_pairs.clear();
     const int64_t per_head = query_pairs(cu, n, lo, hi, &jb);
     // K(t): the non-empty samples the block meets (all samples from jb end after lo).
     int first = -1, last = -1;
@@ -300,38 +368,8 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
       t.sample_first = first;
       t.sample_last = last;
       t.pairs = per_head * p.tile_heads;
-      const int h_lo = t.head_begin, h_hi = h_lo + p.tile_heads;
-      int32_t made = 0;
-      for (int kv = h_lo / g; kv <= (h_hi - 1) / g; ++kv) {
-        const int a = std::max(h_lo, kv * g), e = std::min(h_hi, (kv + 1) * g);
-        const int nh = head_group(e - a);
-        const int rows = kItemColumns / nh;
-        std::vector<int64_t> &cp = chunks_of(rows);
-        if (cp.empty()) {
-          int ji = jb;
-          for (int64_t r0 = lo; r0 < hi; r0 += rows)
-            cp.push_back(query_pairs(cu, n, r0, std::min<int64_t>(hi, r0 + rows), &ji));
-        }
-        for (int gi = 0; gi < (e - a) / nh; ++gi) {
-          size_t ci = 0;
-          for (int64_t r0 = lo; r0 < hi; r0 += rows, ++ci) {
-            const int64_t r1 = std::min<int64_t>(hi, r0 + rows);
-            libra_item it{};
-            it.row0 = (int32_t)r0;
-            it.nrows = (int32_t)(r1 - r0);
-            it.kv_head = kv;
-            it.head0 = a + gi * nh;
-            it.nheads = nh;
-            it.tile_id = t.tile_id;
-            it.id = (int32_t)items.size();
-            it.pairs = nh * cp[ci];
-            it.cost = it.pairs + p.item_overhead;
-            items.push_back(it);
-            ++made;
-          }
-        }
-      }
-      t.n_items = made;
+      t.n_items = cut(t, lo, hi, kFwdItemColumns, items);
+      cut(t, lo, hi, kDqItemColumns, dq_items);
       tiles.push_back(t);
     }
   }
@@ -368,8 +406,13 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
     }
   }
 
-  Queue fq = place(items, workers, p.assign);
-  Queue kq = place(kv_items, workers, p.assign);
+  // The three queues are independent: place them on three host threads.
+  Queue fq, dq, kq;
+  std::thread t_dq([&] { dq = place(dq_items, workers, p.assign); });
+  std::thread t_kv([&] { kq = place(kv_items, workers, p.assign); });
+  fq = place(items, workers, p.assign);
+  t_dq.join();
+  t_kv.join();
 
   libra_plan_info hdr{};
   hdr.magic = LIBRA_PLAN_MAGIC;
@@ -378,13 +421,16 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
   hdr.num_cus = workers;
   hdr.n_tiles = (int32_t)tiles.size();
   hdr.n_items = (int32_t)items.size();
+  hdr.n_dq_items = (int32_t)dq_items.size();
   hdr.n_kv_items = (int32_t)kv_items.size();
   for (const auto &t : tiles) hdr.total_pairs += t.pairs;
   hdr.load_max = fq.load_max;
   hdr.load_sum = fq.load_sum;
+  hdr.dq_load_max = dq.load_max;
+  hdr.dq_load_sum = dq.load_sum;
   hdr.kv_load_max = kq.load_max;
   hdr.kv_load_sum = kq.load_sum;
-  const size_t off = section_offsets(tiles.size(), fq.items.size(), kq.items.size(), workers, &hdr);
+  const size_t off = section_offsets(tiles.size(), fq.items.size(), dq.items.size(), kq.items.size(), workers, &hdr);
   hdr.bytes = off;
 
   if (*bytes < off || (reinterpret_cast<uintptr_t>(buf) & 7)) {
@@ -396,6 +442,8 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
   std::memcpy(out + hdr.off_tiles, tiles.data(), tiles.size() * sizeof(libra_tile));
   std::memcpy(out + hdr.off_items, fq.items.data(), fq.items.size() * sizeof(libra_item));
   std::memcpy(out + hdr.off_cu_off, fq.cu_off.data(), fq.cu_off.size() * sizeof(int32_t));
+  std::memcpy(out + hdr.off_dq_items, dq.items.data(), dq.items.size() * sizeof(libra_item));
+  std::memcpy(out + hdr.off_dq_cu_off, dq.cu_off.data(), dq.cu_off.size() * sizeof(int32_t));
   std::memcpy(out + hdr.off_kv_items, kq.items.data(), kq.items.size() * sizeof(libra_item));
   std::memcpy(out + hdr.off_kv_cu_off, kq.cu_off.data(), kq.cu_off.size() * sizeof(int32_t));
   std::memcpy(out, &hdr, sizeof hdr);
@@ -414,6 +462,8 @@ extern "C" libra_status libra_plan_check(const void *plan, size_t bytes, libra_p
       hdr.off_tiles + (uint64_t)hdr.n_tiles * sizeof(libra_tile),
       hdr.off_items + (uint64_t)hdr.n_items * sizeof(libra_item),
       hdr.off_cu_off + (uint64_t)(hdr.num_cus + 1) * sizeof(int32_t),
+      hdr.off_dq_items + (uint64_t)hdr.n_dq_items * sizeof(libra_item),
+      hdr.off_dq_cu_off + (uint64_t)(hdr.num_cus + 1) * sizeof(int32_t),
       hdr.off_kv_items + (uint64_t)hdr.n_kv_items * sizeof(libra_item),
       hdr.off_kv_cu_off + (uint64_t)(hdr.num_cus + 1) * sizeof(int32_t)};
   for (uint64_t e : ends)

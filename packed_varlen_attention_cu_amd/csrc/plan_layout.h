@@ -7,6 +7,10 @@
 
 namespace libra {
 
+// Query columns (positions x heads) per forward work item and per dQ work
+// item: 32 per wave of the forward's twelve and of the dQ kernel's eight waves.
+constexpr int kFwdItemColumns = 384;
+constexpr int kDqItemColumns = 256;
 // Keys per dK/dV work item: the dK/dV kernel's six key groups of 32 keys.
 constexpr int kKvItemKeys = 192;
 // Query rows per step of the dK/dV kernel: a step runs one query block of

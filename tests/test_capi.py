@@ -82,6 +82,17 @@ def test_planner_matches_oracle(lens, h_q, h_kv, d, B, W, kw):
     assert info.load_max == max(load) and info.load_sum == sum(load)
     assert [int(t["n_items"]) for t in got] == [sum(1 for it in items if it["tile_id"] == t["tile_id"])
                                                for t in ref_tiles]
+    # dQ items (the same tiles, cut for the dQ kernel) and their placement
+    dq = P.fwd_items(cu, L, h_q, h_kv, B, W, overhead=ov, columns=P.DQ_ITEM_COLUMNS)
+    offsets, ids, load = P.queue([it["cost"] for it in dq], ncu, 0.03, mode)
+    assert list(plan.dq_cu_off) == offsets
+    got_dq = plan.dq_items
+    assert [int(x) for x in got_dq["id"]] == ids
+    for g_, i in zip(got_dq, ids):
+        r = dq[i]
+        for f in ("row0", "nrows", "kv_head", "head0", "nheads", "tile_id", "cost", "pairs"):
+            assert int(g_[f]) == r[f], f
+    assert info.dq_load_max == max(load) and info.dq_load_sum == sum(load)
     # key-major dK/dV items and their placement
     kv = P.kv_items(cu, L, h_q, h_kv, overhead=ov)
     offsets, ids, load = P.queue([it["cost"] for it in kv], ncu, 0.03, mode)
@@ -171,7 +182,8 @@ def test_plan_reports_size_when_buffer_too_small():
 def test_empty_pack_plans_and_runs_nothing():
     plan = lib.Plan(np.array([0], dtype=np.int32), total_tokens=0, h_q=4, h_kv=2, head_dim=128,
                     tile_tokens=64, tile_heads=2)
-    assert plan.info.n_tiles == 0 and plan.info.n_items == 0 and plan.info.n_kv_items == 0
+    assert plan.info.n_tiles == 0 and plan.info.n_items == 0 and plan.info.n_dq_items == 0
+    assert plan.info.n_kv_items == 0
     # L = 0: every entry point returns OK before touching any pointer or the device
     lib.libra_attn_fwd(plan.host, None, None, None, None, None, None, None, 0.1, None, None)
     lib.libra_attn_bwd(plan.host, None, None, None, None, None, None, None, None, None, None, None, 0.1,

@@ -48,5 +48,5 @@ def test_phases_match_one_call_entry_points():
     r = rec.cpu().numpy().view(lib.RECORD_DTYPE).reshape(3, ncu)
     assert int(r[0]["n_items"].sum()) == plan.info.n_items
     assert int(r[1]["n_items"].sum()) == plan.info.n_kv_items
-    assert int(r[2]["n_items"].sum()) == plan.info.n_items
+    assert int(r[2]["n_items"].sum()) == plan.info.n_dq_items
     assert (r["t_end"] >= r["t_start"]).all()
