@@ -326,6 +326,25 @@ def sweep():
                 torch.cuda.empty_cache()
 
 
+def granularity():
+    """Forward of train_256k at seed 0 for SH-Tiles of B tokens x W heads: the planner cuts
+    work items inside tiles, so B and W set where items are cut and how many query heads
+    share one K/V block copy (W < 4 leaves W heads per item)."""
+    import torch
+    print("| tile tokens B | tile heads W | tiles | forward items | heads per item | fwd ms | TFLOP/s | "
+          "CU busy max/mean | planned load max/mean | plan ms |")
+    print("|---|---|---|---|---|---|---|---|---|---|", flush=True)
+    for b_ in (512, 2048, 8192, 32768):
+        for w_ in (1, 2, 4, 8):
+            o = measure("train_256k", 0, 0, True, 5, 2, False, quiet=True, tiling=(b_, w_))
+            ps = o["plan_sizes"]
+            print(f"| {b_} | {w_} | {ps['tiles']} | {ps['fwd_items']} | {min(w_, 4)} | "
+                  f"{o['kernel_ms']['fwd']:.3f} | {o['fwd_tflops']:.1f} | "
+                  f"{o['cu_busy_max_over_mean']['fwd']:.3f} | {o['plan_load_max_over_mean']:.4f} | "
+                  f"{o['plan_ms']:.2f} |", flush=True)
+            torch.cuda.empty_cache()
+
+
 def vrsp_report(windows=20, seed=0):
     """Variance-reduced sequence placement (host only): time per window, and the residual
     inter-pool imbalance R - 1 (max / mean pool workload - 1) under the sampler's index order,
@@ -404,8 +423,9 @@ def pooled_inputs(workload, seed, names):
 
 
 def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, warmup=2, cpu=True,
-            calibrate_copy=0, quiet=False):
-    """Time `steps` steps of the hot path on cuda:0; returns the JSON record."""
+            calibrate_copy=0, quiet=False, tiling=None):
+    """Time `steps` steps of the hot path on cuda:0; returns the JSON record.  `tiling`
+    = (tile_tokens, tile_heads) replaces the workload's SH-Tile shape."""
     import torch
     import synth
     import packed_varlen_attention_cu_amd as lib
@@ -428,8 +448,9 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
     lse = torch.empty((w.h_q, L), dtype=torch.float32, device=dev)
     dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if do_bwd else (None,) * 3
 
-    plan_kw = dict(total_tokens=L, h_q=w.h_q, h_kv=w.h_kv, head_dim=d, tile_tokens=w.tile_tokens,
-                   tile_heads=w.tile_heads, assign=assign)
+    tile_tokens, tile_heads = tiling if tiling else (w.tile_tokens, w.tile_heads)
+    plan_kw = dict(total_tokens=L, h_q=w.h_q, h_kv=w.h_kv, head_dim=d, tile_tokens=tile_tokens,
+                   tile_heads=tile_heads, assign=assign)
     plan0 = lib.Plan(cu, **plan_kw)
     ncu = plan0.info.num_cus
     ws_b = torch.empty(max(1, lib.libra_attn_bwd_workspace(plan0.host)), dtype=torch.uint8, device=dev)
@@ -527,7 +548,7 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": workload, "total_tokens": L, "h_q": w.h_q, "h_kv": w.h_kv,
-                   "head_dim": d, "sh_tile": [w.tile_tokens, w.tile_heads], "samples": int(len(lengths)),
+                   "head_dim": d, "sh_tile": [tile_tokens, tile_heads], "samples": int(len(lengths)),
                    "max_sample": int(lengths.max()), "seed": seed, "pass": "fwd+bwd" if do_bwd else "fwd",
                    "placement": "algorithm2" if assign == 0 else "round_robin", "num_cus": ncu},
         "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
@@ -536,6 +557,8 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
         "plan_ms": round(float(np.mean(plan_ms)), 3),
         "cu_busy_max_over_mean": {n: round(float(np.mean(b)), 4) for n, b in busy.items() if b},
         "plan_load_max_over_mean": round(plan0.info.load_max / (plan0.info.load_sum / ncu), 5),
+        "plan_sizes": {"tiles": plan0.info.n_tiles, "fwd_items": plan0.info.n_items,
+                       "dq_items": plan0.info.n_dq_items, "kv_items": plan0.info.n_kv_items},
         "flops_fwd": fwd_flops,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -569,6 +592,10 @@ def main():
                     help="run the sustained bf16 MFMA probe (constant vs random operands, ~3 s each)")
     ap.add_argument("--vrsp", action="store_true",
                     help="host-only: variance-reduced sequence placement timing and pool balance")
+    ap.add_argument("--atomic-rate", action="store_true",
+                    help="run the fp32 atomic-add vs store throughput probe (dQ-shaped tiles)")
+    ap.add_argument("--granularity", action="store_true",
+                    help="forward of train_256k against the SH-Tile shape (tile tokens x tile heads)")
     ap.add_argument("--sweep", action="store_true",
                     help="forward on every workload (and seeds 0-2 and both placements on the skewed and "
                          "uniform packs); prints a markdown table")
@@ -587,19 +614,23 @@ def main():
     if args.vrsp:
         vrsp_report()
         return
-    if args.mfma_ceiling:
+    if args.mfma_ceiling or args.atomic_rate:
         import subprocess
-        probe = os.path.join(ROOT, "packed_varlen_attention_cu_amd", "_lib", "mfma_ceiling")
+        name, argv = ("mfma_ceiling", []) if args.mfma_ceiling else ("mem_probes", ["atomic"])
+        probe = os.path.join(ROOT, "packed_varlen_attention_cu_amd", "_lib", name)
         if not os.path.exists(probe):
             sys.exit(f"{probe} is missing: build the package first")
-        sys.exit(subprocess.run([probe]).returncode)
+        sys.exit(subprocess.run([probe, *argv]).returncode)
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU sharding of this "
-              "path is a design note, not part of this build.", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); sharding this path over "
+              "several GPUs is a design note and is not run here.", file=sys.stderr)
         sys.exit(2)
 
     if args.sweep:
         sweep()
+        return
+    if args.granularity:
+        granularity()
         return
     out = measure(args.workload, args.seed, args.assign, args.fwd_only, args.steps, args.warmup,
                   not args.no_cpu_baseline, args.calibrate_copy)

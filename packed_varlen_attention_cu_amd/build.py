@@ -23,6 +23,7 @@ ARCH = "gfx950"
 
 HOST_SOURCES = ["plan.cpp", "vrsp.cpp"]
 DEVICE_SOURCES = ["attn_fwd.hip", "attn_bwd.hip"]
+PROBES = ["mfma_ceiling", "mem_probes"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-I", INCLUDE, "-I", CSRC, "-Wall"]
 # Packed fp32 VALU forms are kept out of the generated code on purpose.
@@ -63,11 +64,13 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     os.replace(tmp, out)
     shutil.rmtree(objdir, ignore_errors=True)
     if os.path.abspath(out) == LIB:
-        # the sustained-MFMA probe that bench.py --mfma-ceiling runs (a measurement tool)
-        probe = os.path.join(libdir, "mfma_ceiling")
-        _run([HIPCC, "-O3", "-std=c++17", f"--offload-arch={ARCH}", os.path.join(CSRC, "mfma_ceiling.hip"),
-              "-o", probe + ".tmp"])
-        os.replace(probe + ".tmp", probe)
+        # measurement tools that bench.py runs: the sustained-MFMA probe
+        # (--mfma-ceiling) and the atomic / LDS-bank probes (--atomic-rate, --lds-banks)
+        for name in PROBES:
+            probe = os.path.join(libdir, name)
+            _run([HIPCC, "-O3", "-std=c++17", *DEVICE_FLAGS, os.path.join(CSRC, name + ".hip"),
+                  "-o", probe + ".tmp"])
+            os.replace(probe + ".tmp", probe)
     return out
 
 

@@ -70,12 +70,13 @@ void attn_fwd_kernel(FwdArgs a) {
   constexpr int QW = 32 * QT;                   // query positions per wave
   constexpr int NS = D / 16;                    // reduction slabs of d
   constexpr int ND = D / 32;                    // 32-row tiles of d in O^T
-  constexpr int RS = PadRows<D>::kStride;
+  constexpr int RS = PadRows<D>::kStride;      // K rows: direct operand reads
+  constexpr int RV = PadRows<D>::kTrStride;    // V rows: transposing reads only
   // kStages buffers, each a K and a V block [kBN][D] in padded rows; block b
   // uses buffer b mod kStages and is copied kStages - 1 blocks ahead.  The V^T
   // operands of O^T = V^T P^T come from transposing reads of the V block.
-  constexpr int BLK = kBN * RS;
-  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[kStages * 2 * BLK];
+  constexpr int KBLK = kBN * RS, BUF = KBLK + kBN * RV;
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[kStages * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int half = lane >> 5, col = lane & 31;
@@ -86,12 +87,15 @@ void attn_fwd_kernel(FwdArgs a) {
   const uint32_t kv_base = lds_addr(kv_lds);
   const float NEG_INF = -__builtin_inff();
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  const int dlo = direct_lane_off<D>(lane);     // K operand reads
-  const int tlo = tr_lane_off<D>(lane);         // V^T operand reads
+  const int dlo = direct_lane_off<RS>(lane);    // K operand reads
+  const int tlo = tr_lane_off<RV>(lane);        // V^T operand reads
   const int64_t kv_stride = (int64_t)a.h_kv * D;
-  RowCopy<D, kBN, NW> kvcopy;
-  kvcopy.init(wave, lane, kv_stride);
-  const int copies = 2 * RowCopy<D, kBN, NW>::count(wave);   // this wave's copies per block
+  RowCopy<D, kBN, NW, RS> kcopy;
+  RowCopy<D, kBN, NW, RV> vcopy;
+  kcopy.init(wave, lane, kv_stride);
+  vcopy.init(wave, lane, kv_stride);
+  // this wave's copies per block
+  const int copies = RowCopy<D, kBN, NW, RS>::count(wave) + RowCopy<D, kBN, NW, RV>::count(wave);
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -134,9 +138,9 @@ void attn_fwd_kernel(FwdArgs a) {
     // Queue the K and V blocks at key k0 into LDS buffer buf (no registers);
     // rows past L are masked, so their addresses are clamped to row L - 1.
     auto issue = [&](int k0, int buf) {
-      const uint32_t dst = kv_base + buf * 4 * BLK;   // bytes
-      kvcopy.issue(dst, wave, a.k + kvh * D, kv_stride, k0, a.L);
-      kvcopy.issue(dst + 2 * BLK, wave, a.v + kvh * D, kv_stride, k0, a.L);
+      const uint32_t dst = kv_base + buf * 2 * BUF;   // bytes
+      kcopy.issue(dst, wave, a.k + kvh * D, kv_stride, k0, a.L);
+      vcopy.issue(dst + 2 * KBLK, wave, a.v + kvh * D, kv_stride, k0, a.L);
     };
 
     // One key block.  Once this wave's copies of block b have landed (those of
@@ -149,8 +153,8 @@ void attn_fwd_kernel(FwdArgs a) {
       wait_lds();
       block_barrier();
       if (b + kStages - 1 < nblk) issue(k0 + (kStages - 1) * kBN, buf == 0 ? kStages - 1 : buf - 1);
-      const uint16_t *kb = kv_lds + buf * 2 * BLK;
-      const uint16_t *vb = kb + BLK;
+      const uint16_t *kb = kv_lds + buf * BUF;
+      const uint16_t *vb = kb + KBLK;
 
       bool touch = false, partial = false;
 #pragma unroll
@@ -169,7 +173,7 @@ void attn_fwd_kernel(FwdArgs a) {
           for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = zero16();
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
-            const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(kb + dlo + direct_off<D>(kt, s)));
+            const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(kb + dlo + direct_off<RS>(kt, s)));
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = mfma32x32x16(ka, qop[qt][s], sacc[kt][qt]);
           }
@@ -239,8 +243,8 @@ void attn_fwd_kernel(FwdArgs a) {
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-              const bf16x8 va = lds_tr_operand(vb + tlo + tr_off<D>(kt * 32 + 16 * t, dt * 32, 0),
-                                               vb + tlo + tr_off<D>(kt * 32 + 16 * t, dt * 32, 1));
+              const bf16x8 va = lds_tr_operand(vb + tlo + tr_off<RV>(kt * 32 + 16 * t, dt * 32, 0),
+                                               vb + tlo + tr_off<RV>(kt * 32 + 16 * t, dt * 32, 1));
 #pragma unroll
               for (int qt = 0; qt < QT; ++qt)
                 oacc[qt][dt] = mfma32x32x16(va, as_bf16x8(pw[qt][kt][t]), oacc[qt][dt]);

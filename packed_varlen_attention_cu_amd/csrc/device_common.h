@@ -193,18 +193,20 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
       (__attribute__((address_space(3))) s16x4 *)(const __attribute__((address_space(3))) void *)p);
 }
 
-// Row-major bf16 blocks of D columns live in LDS with a padded row stride:
-// 152 elements (304 bytes) for D = 128, 72 (144 bytes) for D = 64.  With 64
-// four-byte banks, the stride moves consecutive rows by 12 (resp. 36) banks,
-// so 16 rows read at one column (the direct operand reads below) and the
-// 4 x 4 pieces of a transposing read both fall on distinct banks, and every
-// operand address is a per-lane base plus a compile-time offset.
+// Row-major bf16 blocks of D columns live in LDS with a padded row stride.
+// The LDS has 64 four-byte banks.  A 16-byte read serves 16 lanes per cycle
+// (here 16 rows at one column), an 8-byte transposing read 32 lanes (here 4
+// rows x 64 bytes).  The first is conflict-free when the stride in 16-byte
+// units is odd, the second when the stride is an odd multiple of 64 bytes;
+// no stride is both, so blocks read only by transposing reads get their own:
+//   kStride   = 152 elements (D = 128) or 72 (D = 64): direct reads;
+//   kTrStride = 160 elements (D = 128) or 96 (D = 64): transposing reads.
+// Every operand address stays a per-lane base plus a compile-time offset.
 template <int D>
 struct PadRows {
-  static constexpr int kStride = D == 128 ? 152 : 72;   // elements per row
   static_assert(D == 128 || D == 64, "head_dim 64 or 128");
-  // LDS-DMA instructions (1 KB each) that fill nr rows.
-  static constexpr int copies(int nr) { return (nr * kStride * 2 + 1023) / 1024; }
+  static constexpr int kStride = D == 128 ? 152 : 72;     // elements per row
+  static constexpr int kTrStride = D == 128 ? 160 : 96;
 };
 
 // Copy of a block of NR rows (D elements each, row r at src + r * stride)
@@ -213,10 +215,9 @@ struct PadRows {
 // wave i mod NW.  A lane whose 16-byte slot is a row's padding copies that
 // row's first chunk into the padding, which is never read, so no lane is
 // switched off.  The lane's offsets are fixed per kernel and computed once.
-template <int D, int NR, int NW>
+template <int D, int NR, int NW, int RS = PadRows<D>::kStride>
 struct RowCopy {
-  static constexpr int RS = PadRows<D>::kStride;
-  static constexpr int NI = PadRows<D>::copies(NR);
+  static constexpr int NI = (NR * RS * 2 + 1023) / 1024;
   static constexpr int NJ = (NI + NW - 1) / NW;
   static_assert(NI * 1024 == NR * RS * 2, "the block fills whole copy instructions");
   uint32_t voff[NJ];                         // byte offset of the lane's source: row * stride + col
@@ -287,12 +288,12 @@ struct RowCopy {
 // Direct A operand: lane (col, half) reads row sigma_row(col) + 32 t of the
 // block, reduction elements 16 s + 8 half .. + 7.  direct_lane_off is the
 // lane's part; slab (t, s) adds direct_off(t, s).
-template <int D>
+template <int RS>
 __device__ __forceinline__ int direct_lane_off(int lane) {
-  return sigma_row(lane & 31) * PadRows<D>::kStride + 8 * (lane >> 5);
+  return sigma_row(lane & 31) * RS + 8 * (lane >> 5);
 }
-template <int D>
-constexpr int direct_off(int t, int s) { return 32 * t * PadRows<D>::kStride + 16 * s; }
+template <int RS>
+constexpr int direct_off(int t, int s) { return 32 * t * RS + 16 * s; }
 
 // MFMA A operand of Mat^T from a row-major padded block Mat [rows][D] in LDS:
 // lane (col, half) receives Mat[k0 + 8 half + i][r0 + col], i = 0..7.  Lane j
@@ -301,13 +302,13 @@ constexpr int direct_off(int t, int s) { return 32 * t * PadRows<D>::kStride + 1
 // of the transposing read the group's lane i then holds rows
 // k0 + 8 (g >> 1) + 4 p + 0..3 of column r0 + 16 (g & 1) + i.  tr_lane_off is
 // the lane's part; (k0, r0, p) add tr_off(k0, r0, p).
-template <int D>
+template <int RS>
 __device__ __forceinline__ int tr_lane_off(int lane) {
   const int g = lane >> 4, j = lane & 15;
-  return (8 * (g >> 1) + (j >> 2)) * PadRows<D>::kStride + 16 * (g & 1) + 4 * (j & 3);
+  return (8 * (g >> 1) + (j >> 2)) * RS + 16 * (g & 1) + 4 * (j & 3);
 }
-template <int D>
-constexpr int tr_off(int k0, int r0, int p) { return (k0 + 4 * p) * PadRows<D>::kStride + r0; }
+template <int RS>
+constexpr int tr_off(int k0, int r0, int p) { return (k0 + 4 * p) * RS + r0; }
 
 __device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t *lo_p, const uint16_t *hi_p) {
   const s16x4 lo = lds_read_tr16(lo_p), hi = lds_read_tr16(hi_p);
