@@ -1,10 +1,11 @@
 """Benchmark of the packed varlen causal attention hot path on one MI355X.
 
 One step = plan the pack on the host (SH-Tiles, eq. 8 pair counts, Algorithm 2
-placement onto the CUs), upload the plan, run the forward (V transpose +
-persistent kernel) and the backward (transposes + rowsum, dK/dV kernel, dQ
-kernel), with per-CU busy records.  Inputs (q, k, v, dout) are resident in
-HBM before timing starts.  Throughput counts only unmasked causal pairs:
+placement onto the CUs), upload the plan, run the persistent forward kernel and
+the backward (row dot D, dK/dV kernel, dQ kernel), with per-CU busy records.
+The host builds each step's plan one step ahead, on a worker thread, while the
+GPU runs the previous step.  Inputs (q, k, v, dout) are resident in HBM before
+timing starts.  Throughput counts only unmasked causal pairs:
 FLOPs_fwd = 4 d h_q sum_j l_j (l_j + 1) / 2, FLOPs_bwd = 2.5 FLOPs_fwd.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -19,6 +20,7 @@ import math
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -454,8 +456,7 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
     plan0 = lib.Plan(cu, **plan_kw)
     ncu = plan0.info.num_cus
     ws_b = torch.empty(max(1, lib.libra_attn_bwd_workspace(plan0.host)), dtype=torch.uint8, device=dev)
-    rec = torch.zeros(3 * ncu * lib.RECORD_DTYPE.itemsize, dtype=torch.uint8, device=dev)
-    rec_f, rec_kv, rec_q = rec[:ncu * 32], rec[ncu * 32:2 * ncu * 32], rec[2 * ncu * 32:]
+    rec = torch.zeros(3 * ncu * lib.RECORD_DTYPE.itemsize, dtype=torch.uint8, device=dev)   # warm-up steps
     cu_dev = torch.from_numpy(cu.copy()).to(dev)
     plan_dev = torch.empty(plan0.host.nbytes, dtype=torch.uint8, device=dev)
 
@@ -469,59 +470,80 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
 
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
-    ev = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for n in ("fwd", "bwd_prepare", "bwd_dkdv", "bwd_dq")}
-    times = {n: [] for n in ev}
+    names_ = ("fwd", "bwd_prepare", "bwd_dkdv", "bwd_dq")
+    ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names_}
+          for _ in range(steps)]
+    recs = [torch.zeros(3 * ncu * lib.RECORD_DTYPE.itemsize, dtype=torch.uint8, device=dev) for _ in range(steps)]
+    times = {n: [] for n in names_}
     plan_ms = []
 
-    def step(record):
+    # The host planner runs one step ahead on a worker thread (the planner call
+    # releases the GIL): the plan of step i + 1 is built while the GPU runs
+    # step i, so planning stays off the GPU's critical path, as the method
+    # intends.  Every step still builds its own plan inside the timed region.
+    def make_plan():
         t0 = time.perf_counter()
         plan = lib.Plan(cu, **plan_kw)                                  # host planner (a1-a3)
         plan_ms.append((time.perf_counter() - t0) * 1e3)
-        plan_dev.copy_(torch.from_numpy(plan.host))                      # plan upload
+        return plan
+
+    planner = ThreadPoolExecutor(1)
+
+    def step(plan, i, record):
+        # plan upload; the copy waits for the previous step's kernels, which read plan_dev
+        plan_dev.copy_(torch.from_numpy(plan.host))
         wsb = ws_b.numel()
+        r = recs[i] if record else rec
+        r_f, r_kv, r_q = r[:ncu * 32], r[ncu * 32:2 * ncu * 32], r[2 * ncu * 32:]
 
         def timed(name, fn):
             if record:
-                ev[name][0].record(stream)
+                ev[i][name][0].record(stream)
             fn()
             if record:
-                ev[name][1].record(stream)
+                ev[i][name][1].record(stream)
 
-        timed("fwd", lambda: lib.libra_attn_fwd(plan.host, plan_dev, q, k, v, cu_dev, o, lse, scale, rec_f, sh))
+        timed("fwd", lambda: lib.libra_attn_fwd(plan.host, plan_dev, q, k, v, cu_dev, o, lse, scale, r_f, sh))
         if do_bwd:
             timed("bwd_prepare", lambda: lib.libra_attn_bwd_prepare(plan.host, o, dout, lse, ws_b, wsb, sh))
             timed("bwd_dkdv", lambda: lib.libra_attn_bwd_dkdv(plan.host, plan_dev, q, k, v, dout, lse, cu_dev,
-                                                              dk, dv, scale, ws_b, wsb, rec_kv, sh))
+                                                              dk, dv, scale, ws_b, wsb, r_kv, sh))
             timed("bwd_dq", lambda: lib.libra_attn_bwd_dq(plan.host, plan_dev, q, k, v, dout, lse, cu_dev, dq,
-                                                          scale, ws_b, wsb, rec_q, sh))
+                                                          scale, ws_b, wsb, r_q, sh))
 
+    nxt = planner.submit(make_plan)
     for _ in range(warmup):
-        step(False)
+        plan = nxt.result()
+        nxt = planner.submit(make_plan)
+        step(plan, 0, False)
     torch.cuda.synchronize()
     plan_ms.clear()
 
-    wall = 0.0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        plan = nxt.result()
+        nxt = planner.submit(make_plan)                                 # the next step's plan
+        step(plan, i, True)
+        if not quiet:
+            print(f"step {i + 1}/{steps} enqueued", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nxt.result()
+    planner.shutdown()
+
     busy = {"fwd": [], "bwd_dkdv": [], "bwd_dq": []}
     for i in range(steps):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        step(True)
-        torch.cuda.synchronize()
-        wall += time.perf_counter() - t0
-        for n, (a_, b_) in ev.items():
+        for n, (a_, b_) in ev[i].items():
             if n.startswith("bwd") and not do_bwd:
                 continue
             times[n].append(a_.elapsed_time(b_))
-        for n, r in (("fwd", rec_f), ("bwd_dkdv", rec_kv), ("bwd_dq", rec_q)):
+        r = recs[i]
+        for n, rr in (("fwd", r[:ncu * 32]), ("bwd_dkdv", r[ncu * 32:2 * ncu * 32]), ("bwd_dq", r[2 * ncu * 32:])):
             if n.startswith("bwd") and not do_bwd:
                 continue
-            ratio, _ = cu_busy_ratio(r.cpu().numpy(), ncu)
+            ratio, _ = cu_busy_ratio(rr.cpu().numpy(), ncu)
             busy[n].append(ratio)
-        if not quiet:
-            print(f"step {i + 1}/{steps}: {(time.perf_counter() - t0) * 1e3:.2f} ms", file=sys.stderr,
-                  flush=True)
-
     ms_step = wall / steps * 1e3
     pairs = causal_pairs(cu) * w.h_q
     assert pairs == plan0.info.total_pairs, "planner pair count disagrees with the closed form"
