@@ -71,6 +71,28 @@ def test_bwd_gqa_group_shapes(lib, h_q, h_kv, d, tile_heads):
         S.check_grad(S.from_dev_bf16(g), r, f"{w.name} {name_g}")
 
 
+@pytest.mark.parametrize("kind", ["x4", "rising", "falling"])
+def test_bwd_extreme_logits(lib, kind):
+    """The backward's recomputed P = exp(S scale - LSE) with logits far outside N(0, 1), from the
+    forward's LSE of the same extreme inputs.  When keys share a large common component
+    (rising, falling), dQ = scale sum_k dS_k K_k cancels heavily, and the bf16 rounding of dS
+    and of the O that D is computed from (the standard rounding points of this backward)
+    exceed the fixed 5e-2 bound.  Those cases are held to the pages' own criterion instead:
+    within 2x the error of a plain bf16 evaluation (Libra paper section 6.7)."""
+    import oracle.attention as A
+    lens = [600, 1, 300, 199]
+    w = synth.Workload(f"logits-{kind}", sum(lens), 8, 2, 128, 512, 4, fixed_lengths=tuple(lens), fill=False)
+    cu = synth.cu_seqlens(lens)
+    t = S.extreme_logit_inputs(w, cu, kind, 7, names=("q", "k", "v", "dout"))
+    S.say(f"[bwd] extreme logits {kind}")
+    dq, dk, dv = run_fwd_bwd(lib, w, cu, t)
+    args = [A.widen_bf16(t[n]) for n in ("q", "k", "v", "dout")]
+    ref = A.backward(*args, cu, S.scale_of(w))
+    yard = A.backward_bf16_reference(*args, cu, S.scale_of(w))[1:]
+    for name_g, g, r, y in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, yard):
+        S.check_grad(S.from_dev_bf16(g), r, f"{kind} {name_g}", g_bf16=y)
+
+
 @pytest.mark.parametrize("lens", [[1] * 200, [0, 3, 0, 140, 1, 0, 70], [64], [65, 63, 2, 129]])
 def test_bwd_edge_packs(lib, lens):
     import oracle.attention as A

@@ -137,6 +137,19 @@ def test_fwd_pool_equals_separate_launches(lib):
     assert np.max(np.abs(lsp - np.concatenate([lsa.cpu().numpy(), lsb.cpu().numpy()], axis=1))) <= 2 * S.LSE_MAX
 
 
+@pytest.mark.parametrize("kind", ["x4", "x8", "rising", "falling"])
+def test_fwd_extreme_logits(lib, kind):
+    """Logits far outside the N(0, 1) range: large jumps of the running maximum (x4, x8), a
+    rescale at every key block (rising), weights that underflow behind an early maximum
+    (falling).  Both head sizes."""
+    lens = [700, 1, 500, 64, 235]
+    for d in (128, 64):
+        w = synth.Workload(f"logits-{kind}", sum(lens), 8, 2, d, 512, 4, fixed_lengths=tuple(lens), fill=False)
+        cu = synth.cu_seqlens(lens)
+        t = S.extreme_logit_inputs(w, cu, kind, 6)
+        full_check(lib, w, cu, t, f"{kind} d={d}")
+
+
 @pytest.mark.parametrize("h_q,h_kv,d,tile_heads", [(12, 4, 128, 3), (6, 6, 64, 2), (16, 1, 128, 8),
                                                     (32, 16, 64, 32)])
 def test_fwd_gqa_group_shapes(lib, h_q, h_kv, d, tile_heads):
