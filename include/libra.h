@@ -58,7 +58,7 @@ enum {
 };
 
 #define LIBRA_PLAN_MAGIC 0x4152424Cu   /* "LBRA" little-endian */
-#define LIBRA_PLAN_VERSION 2u
+#define LIBRA_PLAN_VERSION 3u
 
 /* Planner inputs.  SH-Tiles (Libra technical review, section 5.1, eq. 6)
  * are tile_tokens (B) tokens by tile_heads (W = h_q / H) query heads. */
@@ -94,13 +94,19 @@ typedef struct {
  *   and nrows * nheads <= 384 (forward) or 256 (dQ).
  * dK/dV items (tile_id == -1): key rows [row0, row0 + nrows) of kv_head,
  *   nrows <= 192, gathering the gradient of all h_q / h_kv query heads of
- *   that KV head. */
+ *   that KV head.  They walk the query blocks of their keys' sample down from
+ *   its last block, or up from their own first block when flags has
+ *   LIBRA_ITEM_WALK_UP.  The planner places them in pairs (chunk i and chunk
+ *   n - 1 - i of the chunks ending in one sample, one KV head) that run back
+ *   to back, the first walking down, the second up: pairs then cost the same
+ *   and pairs started together read the same query block at every step. */
+#define LIBRA_ITEM_WALK_UP 1
 typedef struct {
   int32_t row0, nrows;
   int32_t kv_head, head0, nheads;
   int32_t tile_id;
   int32_t id;                       /* position in the planner's enumeration */
-  int32_t reserved;
+  int32_t flags;                    /* LIBRA_ITEM_WALK_UP (dK/dV items); 0 otherwise */
   int64_t cost;                     /* placement key: pairs + item_overhead */
   int64_t pairs;                    /* unmasked (query, key, head) triples */
 } libra_item;

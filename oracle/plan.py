@@ -41,6 +41,22 @@ it, masked or not: g heads x the query blocks of 64 rows from the chunk's
 first key rounded down to a multiple of 64 up to the end of the sample of its
 last key x 64 rows x its keys.
 
+Zigzag units of dK/dV items (a reading for one GPU: the pages place tiles,
+not items, and say nothing of walk order).  For each KV head, the chunks
+whose last key lies in the same sample form a group c_0 .. c_{n-1}; chunk c_i
+is paired with chunk c_{n-1-i} (the middle chunk of an odd group stands
+alone).  A pair is placed as one unit of cost f(c_i) + f(c_{n-1-i}), and its
+worker runs c_i first, walking the query blocks down from the sample's last
+block, then c_{n-1-i}, walking them up from its own first block (flag
+KV_WALK_UP).  Pairs of a group then cost the same, and pairs that start
+together read the same query block at every step, which is what lets the
+workers of one L2 share the streamed Q and dO rows.  Units are numbered by
+their first chunk's item id.  Pairs are coarser units than single chunks: they
+are kept only if their largest worker load is within 0.5 % of the largest
+load single chunks give; otherwise the single chunks are placed, all walking
+down (a pack dominated by one sample and one KV head, such as the 1M-token
+share, would otherwise lose its balance).
+
 Placement (Algorithm 2, section 5.4).  C = (1 + tau) * sum f / |W|.  Units go
 in order of decreasing f, then id.  Among workers whose load stays <= C the
 placer takes the minimum of (dcomm, load, worker id); if there is none it
@@ -55,6 +71,7 @@ ITEM_COLUMNS = 384                       # query positions x heads per forward i
 DQ_ITEM_COLUMNS = 256                    # query positions x heads per dQ item
 KV_CHUNK = 192                           # keys per dK/dV item
 KV_QUERY_BLOCK = 64                      # query rows per step of the dK/dV kernel
+KV_WALK_UP = 1                           # dK/dV item flag: walk the query blocks upward
 
 
 def _ranges(cu):
@@ -197,3 +214,50 @@ def queue(costs, n_workers, tau=0.03, mode="lpt"):
         offsets.append(len(ids))
     load = [sum(costs[t] for t in per[r]) for r in range(n_workers)]
     return offsets, ids, load
+
+
+def kv_units(cu, kv) -> list:
+    """Zigzag units of the dK/dV items ``kv`` (in id order): [(first id, second id or None)],
+    numbered by the first chunk's id."""
+    ranges = _ranges(cu)
+
+    def last_sample(it):
+        r = it["row0"] + it["nrows"] - 1
+        return next(j for j, (s, e) in enumerate(ranges) if s <= r < e)
+
+    groups = {}
+    for it in kv:
+        groups.setdefault((last_sample(it), it["kv_head"]), []).append(it)
+    partner = {}
+    for its in groups.values():
+        its = sorted(its, key=lambda it: it["row0"])
+        n = len(its)
+        for i in range((n + 1) // 2):
+            a, b = its[i], its[n - 1 - i]
+            partner[a["id"]] = None if a is b else b["id"]
+    return [(a, partner[a]) for a in sorted(partner)]
+
+
+def kv_queue(cu, kv, n_workers, tau=0.03, mode="lpt"):
+    """Per-worker dK/dV queues as CSR: (offsets, item ids, item flags, per-worker load).  Units
+    are placed like any other units; each expands into its first chunk (walking down), then its
+    second (walking up).  If the pairs' largest load exceeds that of single chunks by more than
+    0.5 %, the single chunks are placed instead, all walking down."""
+    units = kv_units(cu, kv)
+    costs = [kv[a]["cost"] + (kv[b]["cost"] if b is not None else 0) for a, b in units]
+    u_off, u_ids, load = queue(costs, n_workers, tau, mode)
+    s_off, s_ids, s_load = queue([it["cost"] for it in kv], n_workers, tau, mode)
+    if max(load) * 1000 > max(s_load) * 1005:          # pairs too coarse: single chunks, walking down
+        return s_off, s_ids, [0] * len(s_ids), s_load
+    offsets, ids, flags = [0], [], []
+    for r in range(n_workers):
+        for u in u_ids[u_off[r]:u_off[r + 1]]:
+            a, b = units[u]
+            ids.append(a)
+            flags.append(0)
+            if b is not None:
+                ids.append(b)
+                flags.append(KV_WALK_UP)
+        offsets.append(len(ids))
+    return offsets, ids, flags, load
+

@@ -60,7 +60,7 @@ TILE_DTYPE = np.dtype([("tile_id", "<i4"), ("block", "<i4"), ("shard", "<i4"), (
                        ("sample_first", "<i4"), ("sample_last", "<i4"), ("n_items", "<i4"),
                        ("pairs", "<i8")])
 ITEM_DTYPE = np.dtype([("row0", "<i4"), ("nrows", "<i4"), ("kv_head", "<i4"), ("head0", "<i4"),
-                       ("nheads", "<i4"), ("tile_id", "<i4"), ("id", "<i4"), ("reserved", "<i4"),
+                       ("nheads", "<i4"), ("tile_id", "<i4"), ("id", "<i4"), ("flags", "<i4"),
                        ("cost", "<i8"), ("pairs", "<i8")])
 RECORD_DTYPE = np.dtype([("hw_id", "<u4"), ("xcc_id", "<u4"), ("n_items", "<u4"), ("reserved", "<u4"),
                          ("t_start", "<u8"), ("t_end", "<u8")])

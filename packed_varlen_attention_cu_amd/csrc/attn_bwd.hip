@@ -194,18 +194,20 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
         }
       };
 
-      // Steps run over (query block, head), query blocks from the sample's
-      // last one down and heads inner: every item of a sample starts at the
-      // same block, so items that run at the same time on one XCD read the
-      // same Q / dO rows (16 % less memory-side traffic than a walk up from
-      // each item's own first block).  (ch, cq0) is the step to compute
-      // next, (nh, nq0) the next one to copy.
-      const int qlast = qstart + (nqb - 1) * kQB;
-      int ch = item.head0, cq0 = qlast, nh = item.head0, nq0 = qlast;
+      // Steps run over (query block, head), heads inner, query blocks from
+      // the sample's last one down, or (LIBRA_ITEM_WALK_UP) from the item's
+      // first one up.  The planner pairs a chunk walking down with one
+      // walking up so that items started together on one XCD read the same
+      // Q / dO rows at every step.  (ch, cq0) is the step to compute next,
+      // (nh, nq0) the next one to copy.
+      const bool up = (item.flags & LIBRA_ITEM_WALK_UP) != 0;
+      const int qfirst = up ? qstart : qstart + (nqb - 1) * kQB;
+      const int qstep = up ? kQB : -kQB;
+      int ch = item.head0, cq0 = qfirst, nh = item.head0, nq0 = qfirst;
       auto advance = [&](int &hh, int &qq) {
         if (++hh == item.head0 + item.nheads) {
           hh = item.head0;
-          qq -= kQB;
+          qq += qstep;
         }
       };
       auto step = [&](int i, int buf) {

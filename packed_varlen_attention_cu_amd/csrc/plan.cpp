@@ -177,6 +177,65 @@ Queue place(const std::vector<libra_item> &units, int workers, int mode) {
   return q;
 }
 
+// dK/dV items in zigzag units.  For each KV head, the chunks whose last key
+// lies in the same sample form a group c_0 .. c_{m-1}; chunk c_i pairs with
+// c_{m-1-i} (the middle chunk of an odd group stands alone).  A pair is one
+// placement unit of cost f(c_i) + f(c_{m-1-i}), numbered by its first chunk;
+// its worker runs c_i walking the query blocks down from the sample's last
+// block, then c_{m-1-i} walking them up (LIBRA_ITEM_WALK_UP).  Pairs of a
+// group cost the same, and pairs that start together read the same query
+// block at every step, so the CUs sharing an L2 share the Q and dO rows.
+// Equal-cost pairs are coarser than single chunks: when one group holds most
+// of the work they leave too few small units to level the workers, so the
+// pairs are kept only if their largest worker load is within 0.5 % of that
+// of single chunks (all walking down); otherwise the single chunks are used.
+// kv_items are chunk-major with the KV head inner: item c * h_kv + kappa.
+Queue place_kv_zigzag(const std::vector<libra_item> &kv_items, const std::vector<int32_t> &last_sample,
+                      int h_kv, int workers, int mode) {
+  const int64_t nchunks = (int64_t)last_sample.size();
+  std::vector<int32_t> second(kv_items.size(), -2);   // -2: not a unit's first chunk, -1: alone
+  for (int64_t c0 = 0; c0 < nchunks;) {
+    int64_t c1 = c0;
+    while (c1 + 1 < nchunks && last_sample[c1 + 1] == last_sample[c0]) ++c1;
+    for (int64_t i = 0; c0 + i <= c1 - i; ++i)
+      for (int kv = 0; kv < h_kv; ++kv)
+        second[(c0 + i) * h_kv + kv] = c0 + i == c1 - i ? -1 : (int32_t)((c1 - i) * h_kv + kv);
+    c0 = c1 + 1;
+  }
+  std::vector<libra_item> units;   // each unit carries its first chunk, with the pair's cost
+  units.reserve(kv_items.size() / 2 + 1);
+  for (size_t i = 0; i < kv_items.size(); ++i)
+    if (second[i] != -2) {
+      libra_item u = kv_items[i];
+      if (second[i] >= 0) u.cost += kv_items[second[i]].cost;
+      units.push_back(u);
+    }
+  Queue uq = place(units, workers, mode);
+  Queue single = place(kv_items, workers, mode);
+  if (uq.load_max * 1000 > single.load_max * 1005) {
+    for (auto &it : single.items) it.flags = 0;
+    return single;
+  }
+  Queue q;
+  q.load_max = uq.load_max;
+  q.load_sum = uq.load_sum;
+  q.cu_off.assign(workers + 1, 0);
+  q.items.reserve(kv_items.size());
+  for (int r = 0; r < workers; ++r) {
+    for (int32_t k = uq.cu_off[r]; k < uq.cu_off[r + 1]; ++k) {
+      const int32_t a = uq.items[k].id;
+      q.items.push_back(kv_items[a]);
+      q.items.back().flags = 0;
+      if (second[a] >= 0) {
+        q.items.push_back(kv_items[second[a]]);
+        q.items.back().flags = LIBRA_ITEM_WALK_UP;
+      }
+    }
+    q.cu_off[r + 1] = (int32_t)q.items.size();
+  }
+  return q;
+}
+
 size_t align64(size_t x) { return (x + 63) & ~size_t(63); }
 
 // Byte offsets of the plan sections (written into hdr when it is not null)
@@ -383,6 +442,7 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
   std::vector<libra_item> kv_items;
   const int64_t nchunks = (L + kKvChunk - 1) / kKvChunk;
   kv_items.reserve(n_kv);
+  std::vector<int32_t> last_sample(nchunks);   // sample of each chunk's last key
   int jk = 0, je = 0;
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t lo = c * kKvChunk, hi = std::min<int64_t>(L, lo + kKvChunk);
@@ -390,6 +450,7 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
     const int64_t qstart = lo / libra::kKvQueryBlock * libra::kKvQueryBlock;
     const int64_t qblocks = (sample_end(cu, n, hi - 1, &je) - qstart + libra::kKvQueryBlock - 1) /
                             libra::kKvQueryBlock;
+    last_sample[c] = je;
     const int64_t executed = g * qblocks * libra::kKvQueryBlock * (hi - lo);
     for (int kv = 0; kv < p.h_kv; ++kv) {
       libra_item it{};
@@ -409,7 +470,7 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
   // The three queues are independent: place them on three host threads.
   Queue fq, dq, kq;
   std::thread t_dq([&] { dq = place(dq_items, workers, p.assign); });
-  std::thread t_kv([&] { kq = place(kv_items, workers, p.assign); });
+  std::thread t_kv([&] { kq = place_kv_zigzag(kv_items, last_sample, p.h_kv, workers, p.assign); });
   fq = place(items, workers, p.assign);
   t_dq.join();
   t_kv.join();

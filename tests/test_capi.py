@@ -80,6 +80,7 @@ def test_planner_matches_oracle(lens, h_q, h_kv, d, B, W, kw):
         for f in ("row0", "nrows", "kv_head", "head0", "nheads", "tile_id", "cost", "pairs"):
             assert int(g_[f]) == r[f], f
     assert info.load_max == max(load) and info.load_sum == sum(load)
+    assert not got_items["flags"].any() and not plan.dq_items["flags"].any()
     assert [int(t["n_items"]) for t in got] == [sum(1 for it in items if it["tile_id"] == t["tile_id"])
                                                for t in ref_tiles]
     # dQ items (the same tiles, cut for the dQ kernel) and their placement
@@ -95,10 +96,11 @@ def test_planner_matches_oracle(lens, h_q, h_kv, d, B, W, kw):
     assert info.dq_load_max == max(load) and info.dq_load_sum == sum(load)
     # key-major dK/dV items and their placement
     kv = P.kv_items(cu, L, h_q, h_kv, overhead=ov)
-    offsets, ids, load = P.queue([it["cost"] for it in kv], ncu, 0.03, mode)
+    offsets, ids, flags, load = P.kv_queue(cu, kv, ncu, 0.03, mode)
     assert list(plan.kv_cu_off) == offsets
     got_kv = plan.kv_items
     assert [int(x) for x in got_kv["id"]] == ids
+    assert [int(x) for x in got_kv["flags"]] == flags
     for g_, i in zip(got_kv, ids):
         r = kv[i]
         for f in ("row0", "nrows", "kv_head", "head0", "nheads", "tile_id", "cost", "pairs"):

@@ -138,3 +138,34 @@ def test_lpt_balances_better_than_round_robin():
     mean = sum(costs) / 16
     assert max(lpt) / mean < max(rr) / mean
     assert max(lpt) <= max(max(costs), 1.03 * mean + max(costs))
+
+
+def test_kv_zigzag_units_hand_worked():
+    """lens (1000, 500), one KV head: chunks of 192 keys end in sample 0 for c = 0..4 and in
+    sample 1 for c = 5..7 (chunk 5 straddles).  Pairs: (0, 4), (1, 3), 2 alone; (5, 7), 6 alone."""
+    cu = [0, 1000, 1500]
+    kv = P.kv_items(cu, 1500, 2, 1)
+    assert [it["row0"] for it in kv] == [0, 192, 384, 576, 768, 960, 1152, 1344]
+    assert P.kv_units(cu, kv) == [(0, 4), (1, 3), (2, None), (5, 7), (6, None)]
+    offsets, ids, flags, load = P.kv_queue(cu, kv, 1)      # one worker: pairs cannot unbalance
+    # every item once; a pair's second chunk follows its first and walks up
+    assert sorted(ids) == list(range(8))
+    for a, b in [(0, 4), (1, 3), (5, 7)]:
+        i = ids.index(a)
+        assert ids[i + 1] == b and flags[i] == 0 and flags[i + 1] == P.KV_WALK_UP
+    assert flags[ids.index(2)] == 0 and flags[ids.index(6)] == 0
+    # pairs of one group cost the same: each chunk's query-block walk shortens by 3 blocks per chunk
+    c = {it["id"]: it["cost"] for it in kv}
+    assert c[0] + c[4] == c[1] + c[3]
+
+
+def test_kv_zigzag_falls_back_when_pairs_unbalance():
+    """One long sample and one KV head over many workers: equal-cost pairs would leave some
+    workers a whole pair more than others, so the single chunks are placed, all walking down,
+    and their balance is what LPT over single chunks gives."""
+    cu = [0, 40000, 40100]
+    kv = P.kv_items(cu, 40100, 8, 1)
+    offsets, ids, flags, load = P.kv_queue(cu, kv, 64)
+    assert not any(flags)
+    s_off, s_ids, s_load = P.queue([it["cost"] for it in kv], 64)
+    assert (offsets, ids, load) == (s_off, s_ids, s_load)
