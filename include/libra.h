@@ -94,19 +94,24 @@ typedef struct {
  *   and nrows * nheads <= 384 (forward) or 256 (dQ).
  * dK/dV items (tile_id == -1): key rows [row0, row0 + nrows) of kv_head,
  *   nrows <= 192, gathering the gradient of all h_q / h_kv query heads of
- *   that KV head.  They walk the query blocks of their keys' sample down from
- *   its last block, or up from their own first block when flags has
- *   LIBRA_ITEM_WALK_UP.  The planner places them in pairs (chunk i and chunk
- *   n - 1 - i of the chunks ending in one sample, one KV head) that run back
- *   to back, the first walking down, the second up: pairs then cost the same
- *   and pairs started together read the same query block at every step. */
-#define LIBRA_ITEM_WALK_UP 1
+ *   that KV head.
+ * Walk order.  A forward or dQ item walks the key blocks of its rows from
+ *   the start of its first row's sample up to its last row; a dK/dV item
+ *   walks the query blocks its keys see from the end of its last key's
+ *   sample down to its first key.  With LIBRA_ITEM_REVERSE in flags the walk
+ *   runs the other way.  The planner places items in zigzag pairs (item i
+ *   and item m - 1 - i of the m items of one sample, KV head and first head,
+ *   in row order) that run back to back, the second reversed: pairs then
+ *   cost the same, and pairs started together read the same block at every
+ *   step.  A queue whose pairs would leave a CU more than 0.5 % above the
+ *   mean load gets single items, none reversed. */
+#define LIBRA_ITEM_REVERSE 1
 typedef struct {
   int32_t row0, nrows;
   int32_t kv_head, head0, nheads;
   int32_t tile_id;
   int32_t id;                       /* position in the planner's enumeration */
-  int32_t flags;                    /* LIBRA_ITEM_WALK_UP (dK/dV items); 0 otherwise */
+  int32_t flags;                    /* LIBRA_ITEM_REVERSE or 0 */
   int64_t cost;                     /* placement key: pairs + item_overhead */
   int64_t pairs;                    /* unmasked (query, key, head) triples */
 } libra_item;

@@ -41,21 +41,22 @@ it, masked or not: g heads x the query blocks of 64 rows from the chunk's
 first key rounded down to a multiple of 64 up to the end of the sample of its
 last key x 64 rows x its keys.
 
-Zigzag units of dK/dV items (a reading for one GPU: the pages place tiles,
-not items, and say nothing of walk order).  For each KV head, the chunks
-whose last key lies in the same sample form a group c_0 .. c_{n-1}; chunk c_i
-is paired with chunk c_{n-1-i} (the middle chunk of an odd group stands
-alone).  A pair is placed as one unit of cost f(c_i) + f(c_{n-1-i}), and its
-worker runs c_i first, walking the query blocks down from the sample's last
-block, then c_{n-1-i}, walking them up from its own first block (flag
-KV_WALK_UP).  Pairs of a group then cost the same, and pairs that start
-together read the same query block at every step, which is what lets the
-workers of one L2 share the streamed Q and dO rows.  Units are numbered by
-their first chunk's item id.  Pairs are coarser units than single chunks: they
-are kept only if their largest worker load is within 0.5 % of the largest
-load single chunks give; otherwise the single chunks are placed, all walking
-down (a pack dominated by one sample and one KV head, such as the 1M-token
-share, would otherwise lose its balance).
+Zigzag units (a reading for one GPU: the pages place tiles, not items, and
+say nothing of walk order).  A forward or dQ item walks the key blocks of its
+rows up from the start of its first row's sample; a dK/dV item walks the
+query blocks of its keys down from the end of its last key's sample.  Items
+of one group (the sample of the first row, or of the last key for dK/dV
+items; the KV head; the first head) are taken in row order u_0 .. u_{m-1};
+u_i is paired with u_{m-1-i} (the middle item of an odd group stands alone).
+A pair is placed as one unit of cost f(u_i) + f(u_{m-1-i}), numbered by its
+first item's id, and its worker runs u_i in the default order, then u_{m-1-i}
+in reverse (flag REVERSE).  Pairs of a group then cost the same, and pairs
+that start together read the same block at every step, which lets the
+workers of one L2 share the streamed rows.  Pairs are coarser units than
+single items: they are kept only if their largest worker load is within
+0.5 % of the mean load; otherwise the single items are placed, none
+reversed (a pack dominated by one sample and one KV head, such as the
+1M-token share, would otherwise lose its balance).
 
 Placement (Algorithm 2, section 5.4).  C = (1 + tau) * sum f / |W|.  Units go
 in order of decreasing f, then id.  Among workers whose load stays <= C the
@@ -71,7 +72,7 @@ ITEM_COLUMNS = 384                       # query positions x heads per forward i
 DQ_ITEM_COLUMNS = 256                    # query positions x heads per dQ item
 KV_CHUNK = 192                           # keys per dK/dV item
 KV_QUERY_BLOCK = 64                      # query rows per step of the dK/dV kernel
-KV_WALK_UP = 1                           # dK/dV item flag: walk the query blocks upward
+REVERSE = 1                              # item flag: walk in the reverse of the default order
 
 
 def _ranges(cu):
@@ -216,18 +217,20 @@ def queue(costs, n_workers, tau=0.03, mode="lpt"):
     return offsets, ids, load
 
 
-def kv_units(cu, kv) -> list:
-    """Zigzag units of the dK/dV items ``kv`` (in id order): [(first id, second id or None)],
-    numbered by the first chunk's id."""
-    ranges = _ranges(cu)
+def group_key(cu, it, last_key=False):
+    """Zigzag group of an item: (sample, KV head, first head), the sample being that of its
+    first row (forward, dQ items) or of its last key (dK/dV items)."""
+    r = it["row0"] + (it["nrows"] - 1 if last_key else 0)
+    j = next(j for j, (s, e) in enumerate(_ranges(cu)) if s <= r < e)
+    return (j, it["kv_head"], it["head0"])
 
-    def last_sample(it):
-        r = it["row0"] + it["nrows"] - 1
-        return next(j for j, (s, e) in enumerate(ranges) if s <= r < e)
 
+def zigzag_units(cu, items, last_key=False) -> list:
+    """Zigzag units of ``items`` (in id order): [(first id, second id or None)], numbered by the
+    first item's id."""
     groups = {}
-    for it in kv:
-        groups.setdefault((last_sample(it), it["kv_head"]), []).append(it)
+    for it in items:
+        groups.setdefault(group_key(cu, it, last_key), []).append(it)
     partner = {}
     for its in groups.values():
         its = sorted(its, key=lambda it: it["row0"])
@@ -238,16 +241,16 @@ def kv_units(cu, kv) -> list:
     return [(a, partner[a]) for a in sorted(partner)]
 
 
-def kv_queue(cu, kv, n_workers, tau=0.03, mode="lpt"):
-    """Per-worker dK/dV queues as CSR: (offsets, item ids, item flags, per-worker load).  Units
-    are placed like any other units; each expands into its first chunk (walking down), then its
-    second (walking up).  If the pairs' largest load exceeds that of single chunks by more than
-    0.5 %, the single chunks are placed instead, all walking down."""
-    units = kv_units(cu, kv)
-    costs = [kv[a]["cost"] + (kv[b]["cost"] if b is not None else 0) for a, b in units]
+def zigzag_queue(cu, items, n_workers, tau=0.03, mode="lpt", last_key=False):
+    """Per-worker queues as CSR: (offsets, item ids, item flags, per-worker load).  Units are
+    placed like any other units; each expands into its first item (default walk), then its
+    second (flag REVERSE).  If the pairs' largest load exceeds the mean load by more than
+    0.5 %, the single items are placed instead, none reversed."""
+    units = zigzag_units(cu, items, last_key)
+    costs = [items[a]["cost"] + (items[b]["cost"] if b is not None else 0) for a, b in units]
     u_off, u_ids, load = queue(costs, n_workers, tau, mode)
-    s_off, s_ids, s_load = queue([it["cost"] for it in kv], n_workers, tau, mode)
-    if max(load) * 1000 > max(s_load) * 1005:          # pairs too coarse: single chunks, walking down
+    if max(load) * 1000 * n_workers > sum(load) * 1005:     # pairs too coarse: single items
+        s_off, s_ids, s_load = queue([it["cost"] for it in items], n_workers, tau, mode)
         return s_off, s_ids, [0] * len(s_ids), s_load
     offsets, ids, flags = [0], [], []
     for r in range(n_workers):
@@ -257,7 +260,6 @@ def kv_queue(cu, kv, n_workers, tau=0.03, mode="lpt"):
             flags.append(0)
             if b is not None:
                 ids.append(b)
-                flags.append(KV_WALK_UP)
+                flags.append(REVERSE)
         offsets.append(len(ids))
     return offsets, ids, flags, load
-

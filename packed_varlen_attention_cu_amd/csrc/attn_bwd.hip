@@ -195,12 +195,12 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
       };
 
       // Steps run over (query block, head), heads inner, query blocks from
-      // the sample's last one down, or (LIBRA_ITEM_WALK_UP) from the item's
+      // the sample's last one down, or (LIBRA_ITEM_REVERSE) from the item's
       // first one up.  The planner pairs a chunk walking down with one
       // walking up so that items started together on one XCD read the same
       // Q / dO rows at every step.  (ch, cq0) is the step to compute next,
       // (nh, nq0) the next one to copy.
-      const bool up = (item.flags & LIBRA_ITEM_WALK_UP) != 0;
+      const bool up = (item.flags & LIBRA_ITEM_REVERSE) != 0;
       const int qfirst = up ? qstart : qstart + (nqb - 1) * kQB;
       const int qstep = up ? kQB : -kQB;
       int ch = item.head0, cq0 = qfirst, nh = item.head0, nq0 = qfirst;
@@ -415,6 +415,10 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     const int kstart = segment_start(a.cu, a.n_samples, row0) & ~(kKB - 1);
     const int kend = row0 + nrows;
     const int nkb = (kend - kstart + kKB - 1) / kKB;
+    // Step b's key block: up from the sample start, or (LIBRA_ITEM_REVERSE,
+    // the second item of a zigzag pair) down from the item's last block.
+    const bool rev = (item.flags & LIBRA_ITEM_REVERSE) != 0;
+    auto kblock = [&](int b) { return kstart + (rev ? nkb - 1 - b : b) * kKB; };
 
     f32x16 dqacc[ND];
 #pragma unroll
@@ -428,11 +432,11 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 
     auto block = [&](int b, int buf) {
       const uint16_t *bk = kv_lds + buf * 2 * BLK;
-      const int k0 = kstart + b * kKB;
+      const int k0 = kblock(b);
       wait_vmem_upto(b + 1 < nkb ? copies : 0);   // block b landed; block b + 1 may fly
       wait_lds();
       block_barrier();
-      if (b + kStages - 1 < nkb) issue(k0 + (kStages - 1) * kKB, buf == 0 ? kStages - 1 : buf - 1);
+      if (b + kStages - 1 < nkb) issue(kblock(b + kStages - 1), buf == 0 ? kStages - 1 : buf - 1);
       const bool touch = qok && (k0 <= qpos) && (k0 + kKB - 1 >= qss);
       const bool partial = qok && !((k0 >= qss) && (k0 + kKB - 1 <= qpos));
       if (wave_any(touch)) {
@@ -488,7 +492,7 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     block_barrier();                // the previous item's reads of every buffer are done
 #pragma unroll
     for (int b = 0; b < kStages - 1; ++b)
-      if (b < nkb) issue(kstart + b * kKB, b);
+      if (b < nkb) issue(kblock(b), b);
     for (int b = 0, buf = 0; b < nkb; ++b, buf = buf == kStages - 1 ? 0 : buf + 1) block(b, buf);
 
     if (qok) {

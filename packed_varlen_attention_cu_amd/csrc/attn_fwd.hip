@@ -7,7 +7,9 @@
 // waves owns 32 query positions of one query head (three waves per SIMD).
 //
 // Per item the workgroup walks key blocks of 64 from the start of the sample
-// holding the item's first row to its last row.  K and V blocks are copied
+// holding the item's first row to its last row (the second item of a zigzag
+// pair walks them in reverse, so that items started together read the same
+// block).  K and V blocks are copied
 // straight from HBM into LDS (a ring of kStages buffers, copies running
 // kStages - 1 blocks ahead) and read by every wave, so all query heads of a
 // GQA group share one copy.  Each wave computes S^T = K Q^T
@@ -122,6 +124,10 @@ void attn_fwd_kernel(FwdArgs a) {
     const int kstart = segment_start(a.cu, a.n_samples, row0) & ~(kBN - 1);
     const int kend = row0 + nrows;
     const int nblk = (kend - kstart + kBN - 1) / kBN;
+    // Step b's key block: up from the sample start, or (LIBRA_ITEM_REVERSE,
+    // the second item of a zigzag pair) down from the item's last block.
+    const bool rev = (item.flags & LIBRA_ITEM_REVERSE) != 0;
+    auto kblock = [&](int b) { return kstart + (rev ? nblk - 1 - b : b) * kBN; };
 
     f32x16 oacc[QT][ND];
 #pragma unroll
@@ -148,11 +154,11 @@ void attn_fwd_kernel(FwdArgs a) {
     // one barrier makes both true for every wave; then block b + kStages - 1
     // is queued into the buffer block b - 1 used, and block b is computed.
     auto block = [&](int b, int buf) {
-      const int k0 = kstart + b * kBN;
+      const int k0 = kblock(b);
       wait_vmem_upto(b + 1 < nblk ? copies : 0);
       wait_lds();
       block_barrier();
-      if (b + kStages - 1 < nblk) issue(k0 + (kStages - 1) * kBN, buf == 0 ? kStages - 1 : buf - 1);
+      if (b + kStages - 1 < nblk) issue(kblock(b + kStages - 1), buf == 0 ? kStages - 1 : buf - 1);
       const uint16_t *kb = kv_lds + buf * BUF;
       const uint16_t *vb = kb + KBLK;
 
@@ -256,7 +262,7 @@ void attn_fwd_kernel(FwdArgs a) {
     block_barrier();                // the previous item's reads of every buffer are done
 #pragma unroll
     for (int b = 0; b < kStages - 1; ++b)
-      if (b < nblk) issue(kstart + b * kBN, b);
+      if (b < nblk) issue(kblock(b), b);
     for (int b = 0, buf = 0; b < nblk; ++b, buf = buf == kStages - 1 ? 0 : buf + 1) block(b, buf);
 
 #pragma unroll

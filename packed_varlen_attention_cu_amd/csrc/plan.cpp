@@ -23,6 +23,7 @@
 #include <functional>
 #include <queue>
 #include <thread>
+#include <unordered_map>
 #include <vector>
 
 #include "libra.h"
@@ -177,58 +178,59 @@ Queue place(const std::vector<libra_item> &units, int workers, int mode) {
   return q;
 }
 
-// dK/dV items in zigzag units.  For each KV head, the chunks whose last key
-// lies in the same sample form a group c_0 .. c_{m-1}; chunk c_i pairs with
-// c_{m-1-i} (the middle chunk of an odd group stands alone).  A pair is one
-// placement unit of cost f(c_i) + f(c_{m-1-i}), numbered by its first chunk;
-// its worker runs c_i walking the query blocks down from the sample's last
-// block, then c_{m-1-i} walking them up (LIBRA_ITEM_WALK_UP).  Pairs of a
-// group cost the same, and pairs that start together read the same query
-// block at every step, so the CUs sharing an L2 share the Q and dO rows.
-// Equal-cost pairs are coarser than single chunks: when one group holds most
-// of the work they leave too few small units to level the workers, so the
-// pairs are kept only if their largest worker load is within 0.5 % of that
-// of single chunks (all walking down); otherwise the single chunks are used.
-// kv_items are chunk-major with the KV head inner: item c * h_kv + kappa.
-Queue place_kv_zigzag(const std::vector<libra_item> &kv_items, const std::vector<int32_t> &last_sample,
-                      int h_kv, int workers, int mode) {
-  const int64_t nchunks = (int64_t)last_sample.size();
-  std::vector<int32_t> second(kv_items.size(), -2);   // -2: not a unit's first chunk, -1: alone
-  for (int64_t c0 = 0; c0 < nchunks;) {
-    int64_t c1 = c0;
-    while (c1 + 1 < nchunks && last_sample[c1 + 1] == last_sample[c0]) ++c1;
-    for (int64_t i = 0; c0 + i <= c1 - i; ++i)
-      for (int kv = 0; kv < h_kv; ++kv)
-        second[(c0 + i) * h_kv + kv] = c0 + i == c1 - i ? -1 : (int32_t)((c1 - i) * h_kv + kv);
-    c0 = c1 + 1;
+// Zigzag units.  Items sharing a group key (for the dK/dV items: the sample
+// of the last key and the KV head; for forward and dQ items: the sample of
+// the first row, the KV head and the first head) are taken in row order
+// u_0 .. u_{m-1}; u_i pairs with u_{m-1-i} (the middle one of an odd group
+// stands alone).  A pair is one placement unit of cost f(u_i) + f(u_{m-1-i}),
+// numbered by its first item; its worker runs u_i in its kind's default walk
+// order, then u_{m-1-i} in reverse (LIBRA_ITEM_REVERSE).  The walks of a
+// pair then cover a fixed span, so pairs of a group cost the same and pairs
+// that start together read the same K / V (or Q / dO) block at every step:
+// the CUs sharing an L2 share the streamed rows.  Equal-cost pairs are
+// coarser than single items: when one group holds most of the work they leave
+// too few small units to level the workers, so the pairs are kept only if
+// their largest worker load is within 0.5 % of the mean load; otherwise the
+// single items are placed, all in the default order.
+// Items arrive in id order (id = index) and rows ascend within a group.
+Queue place_zigzag(const std::vector<libra_item> &items, const std::vector<int64_t> &group, int workers,
+                   int mode) {
+  const size_t n = items.size();
+  std::vector<int32_t> second(n, -2);   // -2: not a unit's first item, -1: alone
+  {
+    std::unordered_map<int64_t, std::vector<int32_t>> members;
+    members.reserve(n / 4 + 1);
+    for (size_t i = 0; i < n; ++i) members[group[i]].push_back((int32_t)i);
+    for (auto &kv : members) {
+      const std::vector<int32_t> &m = kv.second;
+      for (size_t i = 0; i + i + 1 <= m.size(); ++i) {
+        const size_t j = m.size() - 1 - i;
+        second[m[i]] = i == j ? -1 : m[j];
+      }
+    }
   }
-  std::vector<libra_item> units;   // each unit carries its first chunk, with the pair's cost
-  units.reserve(kv_items.size() / 2 + 1);
-  for (size_t i = 0; i < kv_items.size(); ++i)
+  std::vector<libra_item> units;   // each unit carries its first item, with the pair's cost
+  units.reserve(n / 2 + 1);
+  for (size_t i = 0; i < n; ++i)
     if (second[i] != -2) {
-      libra_item u = kv_items[i];
-      if (second[i] >= 0) u.cost += kv_items[second[i]].cost;
+      libra_item u = items[i];
+      if (second[i] >= 0) u.cost += items[second[i]].cost;
       units.push_back(u);
     }
   Queue uq = place(units, workers, mode);
-  Queue single = place(kv_items, workers, mode);
-  if (uq.load_max * 1000 > single.load_max * 1005) {
-    for (auto &it : single.items) it.flags = 0;
-    return single;
-  }
+  if (uq.load_max * 1000 * workers > uq.load_sum * 1005) return place(items, workers, mode);
   Queue q;
   q.load_max = uq.load_max;
   q.load_sum = uq.load_sum;
   q.cu_off.assign(workers + 1, 0);
-  q.items.reserve(kv_items.size());
+  q.items.reserve(n);
   for (int r = 0; r < workers; ++r) {
     for (int32_t k = uq.cu_off[r]; k < uq.cu_off[r + 1]; ++k) {
       const int32_t a = uq.items[k].id;
-      q.items.push_back(kv_items[a]);
-      q.items.back().flags = 0;
+      q.items.push_back(items[a]);
       if (second[a] >= 0) {
-        q.items.push_back(kv_items[second[a]]);
-        q.items.back().flags = LIBRA_ITEM_WALK_UP;
+        q.items.push_back(items[second[a]]);
+        q.items.back().flags = LIBRA_ITEM_REVERSE;
       }
     }
     q.cu_off[r + 1] = (int32_t)q.items.size();
@@ -442,7 +444,6 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
   std::vector<libra_item> kv_items;
   const int64_t nchunks = (L + kKvChunk - 1) / kKvChunk;
   kv_items.reserve(n_kv);
-  std::vector<int32_t> last_sample(nchunks);   // sample of each chunk's last key
   int jk = 0, je = 0;
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t lo = c * kKvChunk, hi = std::min<int64_t>(L, lo + kKvChunk);
@@ -450,7 +451,6 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
     const int64_t qstart = lo / libra::kKvQueryBlock * libra::kKvQueryBlock;
     const int64_t qblocks = (sample_end(cu, n, hi - 1, &je) - qstart + libra::kKvQueryBlock - 1) /
                             libra::kKvQueryBlock;
-    last_sample[c] = je;
     const int64_t executed = g * qblocks * libra::kKvQueryBlock * (hi - lo);
     for (int kv = 0; kv < p.h_kv; ++kv) {
       libra_item it{};
@@ -469,9 +469,20 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
 
   // The three queues are independent: place them on three host threads.
   Queue fq, dq, kq;
-  std::thread t_dq([&] { dq = place(dq_items, workers, p.assign); });
-  std::thread t_kv([&] { kq = place_kv_zigzag(kv_items, last_sample, p.h_kv, workers, p.assign); });
-  fq = place(items, workers, p.assign);
+  // Zigzag group keys: (sample, KV head, first head) of each item, the sample
+  // being that of the first row (forward, dQ) or of the last key (dK/dV).
+  auto group_keys = [&](const std::vector<libra_item> &v, bool last_key) {
+    std::vector<int64_t> key(v.size());
+    for (size_t i = 0; i < v.size(); ++i) {
+      const int64_t r = v[i].row0 + (last_key ? v[i].nrows - 1 : 0);
+      const int64_t j = std::upper_bound(cu, cu + n + 1, (int32_t)r) - cu - 1;
+      key[i] = j << 32 | (int64_t)v[i].kv_head << 16 | v[i].head0;
+    }
+    return key;
+  };
+  std::thread t_dq([&] { dq = place_zigzag(dq_items, group_keys(dq_items, false), workers, p.assign); });
+  std::thread t_kv([&] { kq = place_zigzag(kv_items, group_keys(kv_items, true), workers, p.assign); });
+  fq = place_zigzag(items, group_keys(items, false), workers, p.assign);
   t_dq.join();
   t_kv.join();
 

@@ -71,24 +71,25 @@ def test_planner_matches_oracle(lens, h_q, h_kv, d, B, W, kw):
     mode = "rr" if kw.get("assign", 0) == 1 else "lpt"
     ov = kw.get("item_overhead", 0)
     items = P.fwd_items(cu, L, h_q, h_kv, B, W, overhead=ov)
-    offsets, ids, load = P.queue([it["cost"] for it in items], ncu, 0.03, mode)
+    offsets, ids, flags, load = P.zigzag_queue(cu, items, ncu, 0.03, mode)
     assert list(plan.cu_off) == offsets
     got_items = plan.items
     assert [int(x) for x in got_items["id"]] == ids
+    assert [int(x) for x in got_items["flags"]] == flags
     for g_, i in zip(got_items, ids):
         r = items[i]
         for f in ("row0", "nrows", "kv_head", "head0", "nheads", "tile_id", "cost", "pairs"):
             assert int(g_[f]) == r[f], f
     assert info.load_max == max(load) and info.load_sum == sum(load)
-    assert not got_items["flags"].any() and not plan.dq_items["flags"].any()
     assert [int(t["n_items"]) for t in got] == [sum(1 for it in items if it["tile_id"] == t["tile_id"])
                                                for t in ref_tiles]
     # dQ items (the same tiles, cut for the dQ kernel) and their placement
     dq = P.fwd_items(cu, L, h_q, h_kv, B, W, overhead=ov, columns=P.DQ_ITEM_COLUMNS)
-    offsets, ids, load = P.queue([it["cost"] for it in dq], ncu, 0.03, mode)
+    offsets, ids, flags, load = P.zigzag_queue(cu, dq, ncu, 0.03, mode)
     assert list(plan.dq_cu_off) == offsets
     got_dq = plan.dq_items
     assert [int(x) for x in got_dq["id"]] == ids
+    assert [int(x) for x in got_dq["flags"]] == flags
     for g_, i in zip(got_dq, ids):
         r = dq[i]
         for f in ("row0", "nrows", "kv_head", "head0", "nheads", "tile_id", "cost", "pairs"):
@@ -96,7 +97,7 @@ def test_planner_matches_oracle(lens, h_q, h_kv, d, B, W, kw):
     assert info.dq_load_max == max(load) and info.dq_load_sum == sum(load)
     # key-major dK/dV items and their placement
     kv = P.kv_items(cu, L, h_q, h_kv, overhead=ov)
-    offsets, ids, flags, load = P.kv_queue(cu, kv, ncu, 0.03, mode)
+    offsets, ids, flags, load = P.zigzag_queue(cu, kv, ncu, 0.03, mode, last_key=True)
     assert list(plan.kv_cu_off) == offsets
     got_kv = plan.kv_items
     assert [int(x) for x in got_kv["id"]] == ids

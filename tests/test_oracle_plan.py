@@ -146,13 +146,13 @@ def test_kv_zigzag_units_hand_worked():
     cu = [0, 1000, 1500]
     kv = P.kv_items(cu, 1500, 2, 1)
     assert [it["row0"] for it in kv] == [0, 192, 384, 576, 768, 960, 1152, 1344]
-    assert P.kv_units(cu, kv) == [(0, 4), (1, 3), (2, None), (5, 7), (6, None)]
-    offsets, ids, flags, load = P.kv_queue(cu, kv, 1)      # one worker: pairs cannot unbalance
+    assert P.zigzag_units(cu, kv, last_key=True) == [(0, 4), (1, 3), (2, None), (5, 7), (6, None)]
+    offsets, ids, flags, load = P.zigzag_queue(cu, kv, 1, last_key=True)      # one worker: pairs cannot unbalance
     # every item once; a pair's second chunk follows its first and walks up
     assert sorted(ids) == list(range(8))
     for a, b in [(0, 4), (1, 3), (5, 7)]:
         i = ids.index(a)
-        assert ids[i + 1] == b and flags[i] == 0 and flags[i + 1] == P.KV_WALK_UP
+        assert ids[i + 1] == b and flags[i] == 0 and flags[i + 1] == P.REVERSE
     assert flags[ids.index(2)] == 0 and flags[ids.index(6)] == 0
     # pairs of one group cost the same: each chunk's query-block walk shortens by 3 blocks per chunk
     c = {it["id"]: it["cost"] for it in kv}
@@ -161,11 +161,23 @@ def test_kv_zigzag_units_hand_worked():
 
 def test_kv_zigzag_falls_back_when_pairs_unbalance():
     """One long sample and one KV head over many workers: equal-cost pairs would leave some
-    workers a whole pair more than others, so the single chunks are placed, all walking down,
-    and their balance is what LPT over single chunks gives."""
+    workers a whole pair more than others (more than 0.5 % above the mean), so the single
+    chunks are placed, all walking down, exactly as LPT over single chunks places them."""
     cu = [0, 40000, 40100]
     kv = P.kv_items(cu, 40100, 8, 1)
-    offsets, ids, flags, load = P.kv_queue(cu, kv, 64)
+    offsets, ids, flags, load = P.zigzag_queue(cu, kv, 64, last_key=True)
     assert not any(flags)
     s_off, s_ids, s_load = P.queue([it["cost"] for it in kv], 64)
     assert (offsets, ids, load) == (s_off, s_ids, s_load)
+
+
+def test_fwd_zigzag_pairs_hand_worked():
+    """One sample of 1000 tokens, 4 query heads on one KV head, tiles of 500 x 4 heads: forward
+    items of 96 rows x 4 heads, cut per tile (rows 0-479 in 5 items, 480-499 alone; the same
+    for 500-999).  In row order the 12 items pair first-with-last: (0, 11), (1, 10), ..."""
+    cu = [0, 1000]
+    items = P.fwd_items(cu, 1000, 4, 1, 500, 4)
+    assert [(it["row0"], it["nrows"]) for it in items] == [(0, 96), (96, 96), (192, 96), (288, 96), (384, 96),
+                                                          (480, 20), (500, 96), (596, 96), (692, 96),
+                                                          (788, 96), (884, 96), (980, 20)]
+    assert P.zigzag_units(cu, items) == [(0, 11), (1, 10), (2, 9), (3, 8), (4, 7), (5, 6)]
