@@ -16,6 +16,10 @@
 //   * query-major dQ: items cut from the forward's SH-Tiles (256 query
 //     columns each, the forward's are 384) and placed like them, each wave
 //     owning 32 query positions of one head and walking its key blocks.
+// Both passes avoid atomics: summing dQ over key items with fp32 atomic adds
+// would move about 30 times the dQ bytes, at a quarter of the store rate.
+// Both walk their blocks in the order the planner's zigzag pairs ask for
+// (LIBRA_ITEM_REVERSE), so that items started together share L2 lines.
 // Operand blocks are copied straight from HBM into LDS; operands that need
 // the transposed layout (Q^T, dO^T, K^T) come from transposing LDS reads of
 // the row-major blocks.  A first phase computes D = rowsum(dO * O) (fp32)
