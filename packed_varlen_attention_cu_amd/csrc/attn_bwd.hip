@@ -17,7 +17,8 @@
 //     columns each, the forward's are 384) and placed like them, each wave
 //     owning 32 query positions of one head and walking its key blocks.
 // Both passes avoid atomics: summing dQ over key items with fp32 atomic adds
-// would move about 30 times the dQ bytes, at a quarter of the store rate.
+// would move about 40 times the bytes of an fp32 dQ, at a quarter of the
+// store rate.
 // Both walk their blocks in the order the planner's zigzag pairs ask for
 // (LIBRA_ITEM_REVERSE), so that items started together share L2 lines.
 // Operand blocks are copied straight from HBM into LDS; operands that need
