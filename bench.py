@@ -425,7 +425,7 @@ def pooled_inputs(workload, seed, names):
 
 
 def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, warmup=2, cpu=True,
-            calibrate_copy=0, quiet=False, tiling=None):
+            calibrate_copy=0, quiet=False, tiling=None, dump_records=None, speed_calibration=True):
     """Time `steps` steps of the hot path on cuda:0; returns the JSON record.  `tiling`
     = (tile_tokens, tile_heads) replaces the workload's SH-Tile shape."""
     import torch
@@ -512,11 +512,32 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
                                                           scale, ws_b, wsb, r_q, sh))
 
     nxt = planner.submit(make_plan)
+    plan = None
     for _ in range(warmup):
         plan = nxt.result()
         nxt = planner.submit(make_plan)
         step(plan, 0, False)
     torch.cuda.synchronize()
+    speed = None
+    if plan is not None and speed_calibration and assign == 0:
+        # The eight XCDs sustain different clocks; the last warm-up launch's per-CU records give
+        # each one's rate, and the timed steps' plans place work by finish time on it.
+        r = rec.cpu().numpy()
+        parts = [(lib.QUEUE_FWD, r[:ncu * 32])]
+        if do_bwd:
+            parts += [(lib.QUEUE_KV, r[ncu * 32:2 * ncu * 32]), (lib.QUEUE_DQ, r[2 * ncu * 32:])]
+        num = np.zeros(8)
+        den = 0.0
+        for q_, rr in parts:
+            rec_ = rr.view(lib.RECORD_DTYPE)[:ncu]
+            b_ = float((rec_["t_end"] - rec_["t_start"]).astype(np.float64).sum())
+            num += b_ * lib.libra_worker_speed(plan.host, q_, rec_).astype(np.float64)
+            den += b_
+        speed = [int(round(x)) for x in num / den] if den > 0 else None
+        if speed:
+            plan_kw["worker_speed"] = speed
+            nxt.result()
+            nxt = planner.submit(make_plan)                             # re-plan with the speeds
     plan_ms.clear()
 
     torch.cuda.synchronize()
@@ -531,6 +552,27 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
     wall = time.perf_counter() - t0
     nxt.result()
     planner.shutdown()
+
+    if dump_records:
+        # per-workgroup busy time (constant-rate clock ticks) next to the planner's load of the
+        # same queue, for the last timed step
+        import packed_varlen_attention_cu_amd as lib_
+        r = recs[steps - 1].cpu().numpy()
+        out_ = {}
+        for n, rr, its, off in (("fwd", r[:ncu * 32], plan.items, plan.cu_off),
+                                ("bwd_dkdv", r[ncu * 32:2 * ncu * 32], plan.kv_items, plan.kv_cu_off),
+                                ("bwd_dq", r[2 * ncu * 32:], plan.dq_items, plan.dq_cu_off)):
+            if n.startswith("bwd") and not do_bwd:
+                continue
+            rec_ = rr.view(lib_.RECORD_DTYPE)[:ncu]
+            cost = its["cost"].astype(np.int64)
+            out_[n] = [{"w": w_, "xcc": int(rec_["xcc_id"][w_]), "hw": int(rec_["hw_id"][w_]),
+                        "busy": int(rec_["t_end"][w_] - rec_["t_start"][w_]), "n_items": int(rec_["n_items"][w_]),
+                        "planned": int(cost[off[w_]:off[w_ + 1]].sum()),
+                        "items": [int(x) for x in its["id"][off[w_]:off[w_ + 1]]]}
+                       for w_ in range(ncu)]
+        with open(dump_records, "w") as f:
+            json.dump(out_, f)
 
     busy = {"fwd": [], "bwd_dkdv": [], "bwd_dq": []}
     for i in range(steps):
@@ -579,6 +621,7 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
         "plan_ms": round(float(np.mean(plan_ms)), 3),
         "cu_busy_max_over_mean": {n: round(float(np.mean(b)), 4) for n, b in busy.items() if b},
         "plan_load_max_over_mean": round(plan0.info.load_max / (plan0.info.load_sum / ncu), 5),
+        "worker_speed": speed,
         "plan_sizes": {"tiles": plan0.info.n_tiles, "fwd_items": plan0.info.n_items,
                        "dq_items": plan0.info.n_dq_items, "kv_items": plan0.info.n_kv_items},
         "flops_fwd": fwd_flops,
@@ -614,6 +657,10 @@ def main():
                     help="run the sustained bf16 MFMA probe (constant vs random operands, ~3 s each)")
     ap.add_argument("--vrsp", action="store_true",
                     help="host-only: variance-reduced sequence placement timing and pool balance")
+    ap.add_argument("--no-speed-calibration", action="store_true",
+                    help="plan with equal worker speeds instead of the per-XCD rates of the warm-up")
+    ap.add_argument("--dump-records", metavar="PATH",
+                    help="write each workgroup's busy time and planned load (last timed step) as JSON")
     ap.add_argument("--atomic-rate", action="store_true",
                     help="run the fp32 atomic-add vs store throughput probe (dQ-shaped tiles)")
     ap.add_argument("--granularity", action="store_true",
@@ -655,7 +702,8 @@ def main():
         granularity()
         return
     out = measure(args.workload, args.seed, args.assign, args.fwd_only, args.steps, args.warmup,
-                  not args.no_cpu_baseline, args.calibrate_copy)
+                  not args.no_cpu_baseline, args.calibrate_copy, dump_records=args.dump_records,
+                  speed_calibration=not args.no_speed_calibration)
     print(json.dumps(out), flush=True)
 
 

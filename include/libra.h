@@ -58,7 +58,7 @@ enum {
 };
 
 #define LIBRA_PLAN_MAGIC 0x4152424Cu   /* "LBRA" little-endian */
-#define LIBRA_PLAN_VERSION 3u
+#define LIBRA_PLAN_VERSION 4u
 
 /* Planner inputs.  SH-Tiles (Libra technical review, section 5.1, eq. 6)
  * are tile_tokens (B) tokens by tile_heads (W = h_q / H) query heads. */
@@ -74,6 +74,13 @@ typedef struct {
   float tau;              /* soft-target slack of Algorithm 2 (0.03 on the pages) */
   int32_t assign;         /* LIBRA_ASSIGN_* */
   int64_t item_overhead;  /* cost added to every work item, in causal-pair units */
+  /* Relative speed of the workers of each class, worker w being of class
+   * w mod 8 (on MI355X workgroup w runs on XCD w mod 8), in thousandths; 0
+   * means 1000.  Algorithm 2 then sends each unit to the worker that would
+   * finish it first, (load + cost) / speed, instead of the least loaded one;
+   * equal speeds give exactly the unweighted placement.  libra_worker_speed
+   * estimates the speeds from the records of a previous launch. */
+  uint16_t worker_speed[8];
 } libra_plan_params;
 
 /* One SH-Tile t = (block, shard), tile_id = block * (h_q / W) + shard.
@@ -143,6 +150,19 @@ typedef struct {
   uint32_t hw_id, xcc_id, n_items, reserved;
   uint64_t t_start, t_end;
 } libra_cu_record;
+
+/* Queues of a plan. */
+enum { LIBRA_QUEUE_FWD = 0, LIBRA_QUEUE_DQ = 1, LIBRA_QUEUE_KV = 2 };
+
+/* Speed of each worker class (worker mod 8), in thousandths of the mean,
+ * from one completed launch of `queue` of this plan (host function, no device
+ * work): class x's rate is the planned cost of its workers over their busy
+ * ticks (t_end - t_start of records[w], w < num_cus), and speed_out[x] is
+ * 1000 x rate_x / mean rate, clamped to [500, 2000]; classes that ran nothing
+ * get 1000.  records: host copy of the launch's num_cus records.
+ * LIBRA_EINVAL for a bad plan, queue or pointer. */
+libra_status libra_worker_speed(const void *plan_host, int32_t queue, const libra_cu_record *records,
+                                uint16_t speed_out[8]);
 
 /* Build a plan on the host (pure function, thread-safe, no device work).
  * cu_seqlens: host int32[num_samples + 1].  buf == NULL: only *bytes is set to

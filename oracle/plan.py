@@ -176,8 +176,28 @@ def kv_items(cu, total_tokens, h_q, h_kv, overhead=0) -> list:
     return items
 
 
-def place(costs, n_workers: int, tau: float = 0.03, dcomm=None):
-    """Algorithm 2: returns (worker of each unit, units in placement order)."""
+def _speeds(speed):
+    s = [int(x) if x else 1000 for x in (speed if speed is not None else [0] * 8)]
+    return s, all(x == s[0] for x in s)
+
+
+def place(costs, n_workers: int, tau: float = 0.03, dcomm=None, speed=None):
+    """Algorithm 2: returns (worker of each unit, units in placement order).  With worker
+    speeds (eight classes, worker r in class r mod 8, in thousandths, 0 = 1000) that are not
+    all equal, each unit goes to the worker that would finish it first, (load + cost) / speed,
+    ties to the lower worker id (an extension for workers of unequal speed; dcomm must be 0)."""
+    s, uniform = _speeds(speed)
+    if not uniform:
+        assert dcomm is None
+        from fractions import Fraction
+        order = sorted(range(len(costs)), key=lambda t: (-costs[t], t))
+        load = [0] * n_workers
+        sigma = [None] * len(costs)
+        for t in order:
+            r = min(range(n_workers), key=lambda r: (Fraction(load[r] + costs[t], s[r % 8]), r))
+            sigma[t] = r
+            load[r] += costs[t]
+        return sigma, order
     n = len(costs)
     dcomm = dcomm or (lambda t, r: 0)
     C = (1.0 + tau) * float(sum(costs)) / n_workers
@@ -199,10 +219,10 @@ def round_robin(n_units: int, n_workers: int):
     return [i % n_workers for i in range(n_units)], list(range(n_units))
 
 
-def queue(costs, n_workers, tau=0.03, mode="lpt"):
+def queue(costs, n_workers, tau=0.03, mode="lpt", speed=None):
     """Per-worker queues as CSR: (offsets[n_workers + 1], unit ids, per-worker load)."""
     if mode == "lpt":
-        sigma, order = place(costs, n_workers, tau)
+        sigma, order = place(costs, n_workers, tau, speed=speed)
     else:
         sigma, order = round_robin(len(costs), n_workers)
     per = [[] for _ in range(n_workers)]
@@ -241,16 +261,27 @@ def zigzag_units(cu, items, last_key=False) -> list:
     return [(a, partner[a]) for a in sorted(partner)]
 
 
-def zigzag_queue(cu, items, n_workers, tau=0.03, mode="lpt", last_key=False):
+def finish_max_over_mean(load, n_workers, speed=None):
+    """Largest finish time load / speed over the mean one (float64, summed in worker order)."""
+    s, _ = _speeds(speed)
+    mx = sm = 0.0
+    for r in range(n_workers):
+        f = float(load[r]) / float(s[r % 8])
+        mx = max(mx, f)
+        sm += f
+    return mx * n_workers / sm if sm > 0 else 1.0
+
+
+def zigzag_queue(cu, items, n_workers, tau=0.03, mode="lpt", last_key=False, speed=None):
     """Per-worker queues as CSR: (offsets, item ids, item flags, per-worker load).  Units are
     placed like any other units; each expands into its first item (default walk), then its
-    second (flag REVERSE).  If the pairs' largest load exceeds the mean load by more than
-    0.5 %, the single items are placed instead, none reversed."""
+    second (flag REVERSE).  If the pairs' largest finish time (load / speed) exceeds the mean
+    one by more than 0.5 %, the single items are placed instead, none reversed."""
     units = zigzag_units(cu, items, last_key)
     costs = [items[a]["cost"] + (items[b]["cost"] if b is not None else 0) for a, b in units]
-    u_off, u_ids, load = queue(costs, n_workers, tau, mode)
-    if max(load) * 1000 * n_workers > sum(load) * 1005:     # pairs too coarse: single items
-        s_off, s_ids, s_load = queue([it["cost"] for it in items], n_workers, tau, mode)
+    u_off, u_ids, load = queue(costs, n_workers, tau, mode, speed)
+    if finish_max_over_mean(load, n_workers, speed) > 1.005:     # pairs too coarse: single items
+        s_off, s_ids, s_load = queue([it["cost"] for it in items], n_workers, tau, mode, speed)
         return s_off, s_ids, [0] * len(s_ids), s_load
     offsets, ids, flags = [0], [], []
     for r in range(n_workers):

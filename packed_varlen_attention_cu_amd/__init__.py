@@ -22,6 +22,7 @@ LIB_PATH = os.environ.get("LIBRA_LIB") or os.path.join(_HERE, "_lib", "liblibra.
 
 LIBRA_OK, LIBRA_EINVAL, LIBRA_ESIZE, LIBRA_EUNSUPPORTED, LIBRA_EHIP = 0, -1, -2, -3, -4
 ASSIGN_PLACER, ASSIGN_ROUND_ROBIN = 0, 1
+QUEUE_FWD, QUEUE_DQ, QUEUE_KV = 0, 1, 2
 PLAN_MAGIC, PLAN_VERSION = 0x4152424C, 1
 
 
@@ -37,7 +38,7 @@ class PlanParams(ctypes.Structure):
                 ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("tile_tokens", ctypes.c_int32), ("tile_heads", ctypes.c_int32),
                 ("num_cus", ctypes.c_int32), ("tau", ctypes.c_float), ("assign", ctypes.c_int32),
-                ("item_overhead", ctypes.c_int64)]
+                ("item_overhead", ctypes.c_int64), ("worker_speed", ctypes.c_uint16 * 8)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -65,7 +66,7 @@ ITEM_DTYPE = np.dtype([("row0", "<i4"), ("nrows", "<i4"), ("kv_head", "<i4"), ("
 RECORD_DTYPE = np.dtype([("hw_id", "<u4"), ("xcc_id", "<u4"), ("n_items", "<u4"), ("reserved", "<u4"),
                          ("t_start", "<u8"), ("t_end", "<u8")])
 
-assert ctypes.sizeof(PlanParams) == 48 and ctypes.sizeof(PlanInfo) == 208
+assert ctypes.sizeof(PlanParams) == 64 and ctypes.sizeof(PlanInfo) == 224
 assert TILE_DTYPE.itemsize == 48 and ITEM_DTYPE.itemsize == 48 and RECORD_DTYPE.itemsize == 32
 
 
@@ -98,6 +99,7 @@ def _load():
     lib.libra_last_hip_error.restype = ctypes.c_char_p
     lib.libra_pack_workload.argtypes = [vp, ctypes.c_int32, vp]
     lib.libra_vrsp.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
+    lib.libra_worker_speed.argtypes = [vp, ctypes.c_int32, vp, vp]
     for name in ("libra_plan", "libra_plan_check", "libra_attn_bwd_workspace", "libra_attn_fwd",
                  "libra_attn_bwd", "libra_device_clock_khz", "libra_attn_bwd_prepare", "libra_attn_bwd_dkdv",
                  "libra_attn_bwd_dq", "libra_pack_workload", "libra_vrsp"):
@@ -165,6 +167,17 @@ def libra_vrsp(workload, pool_size: int):
     return pool_of, order, pool_load[:pools]
 
 
+def libra_worker_speed(plan_host: np.ndarray, queue: int, records) -> np.ndarray:
+    """Speed of each worker class (worker mod 8), in thousandths of the mean, from the records of
+    one completed launch of ``queue`` (QUEUE_FWD, QUEUE_DQ, QUEUE_KV) of this plan.  ``records``:
+    host bytes or array holding the launch's num_cus records."""
+    rec = np.ascontiguousarray(np.asarray(records).view(np.uint8))
+    out = np.zeros(8, dtype=np.uint16)
+    _check(_lib.libra_worker_speed(_ptr(plan_host), int(queue), rec.ctypes.data, out.ctypes.data),
+           "libra_worker_speed")
+    return out
+
+
 def libra_plan_check(buf: np.ndarray) -> PlanInfo:
     info = PlanInfo()
     _check(_lib.libra_plan_check(buf.ctypes.data, buf.nbytes, ctypes.byref(info)), "libra_plan_check")
@@ -226,11 +239,12 @@ class Plan:
     """A host plan buffer, typed views of its sections, and (lazily) its device copy."""
 
     def __init__(self, cu_seqlens, *, total_tokens, h_q, h_kv, head_dim, tile_tokens, tile_heads,
-                 num_cus=0, tau=0.03, assign=ASSIGN_PLACER, item_overhead=0):
+                 num_cus=0, tau=0.03, assign=ASSIGN_PLACER, item_overhead=0, worker_speed=None):
         cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        speed = (ctypes.c_uint16 * 8)(*([int(x) for x in worker_speed] if worker_speed is not None else [0] * 8))
         self.params = PlanParams(int(total_tokens), int(cu.size - 1), int(h_q), int(h_kv), int(head_dim),
                                  int(tile_tokens), int(tile_heads), int(num_cus), float(tau), int(assign),
-                                 int(item_overhead))
+                                 int(item_overhead), speed)
         self.cu_seqlens = cu
         self.host = libra_plan(cu, self.params)
         # the header of a buffer the library just built (libra_plan_check verifies foreign ones)

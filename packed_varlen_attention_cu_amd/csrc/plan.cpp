@@ -104,13 +104,78 @@ inline bool lighter(const Load &x, const Load &y) {
   return x.load != y.load ? x.load < y.load : x.worker < y.worker;
 }
 
-Queue place(const std::vector<libra_item> &units, int workers, int mode) {
+// Worker speeds of a plan: the eight class speeds, 0 read as 1000.
+struct Speeds {
+  int64_t s[8];
+  bool uniform;
+  explicit Speeds(const uint16_t *v) {
+    for (int x = 0; x < 8; ++x) s[x] = v[x] ? v[x] : 1000;
+    uniform = true;
+    for (int x = 1; x < 8; ++x) uniform = uniform && s[x] == s[0];
+  }
+};
+
+// Units heaviest first (ties: lower index) onto workers of different speeds:
+// each goes to the worker that would finish it first, (load + cost) / speed,
+// ties to the lower worker id.  Within a speed class the candidate is the
+// class's least loaded worker, so one min-heap per class and a scan of the
+// eight class tops suffice.  (load + cost) * speed < 2^43 * 2^16 fits int64.
+void place_weighted(const std::vector<int64_t> &costs_sorted, const std::vector<int32_t> &idx_sorted,
+                    int workers, const Speeds &sp, std::vector<int32_t> &worker, std::vector<int64_t> &load) {
+  std::vector<Load> heap[8];
+  for (int32_t r = 0; r < workers; ++r) heap[r % 8].push_back({0, r});   // ascending ids: valid heaps
+  for (size_t k = 0; k < costs_sorted.size(); ++k) {
+    const int64_t c = costs_sorted[k];
+    int best = -1;
+    for (int x = 0; x < 8; ++x) {
+      if (heap[x].empty()) continue;
+      if (best < 0) {
+        best = x;
+        continue;
+      }
+      const Load &t = heap[x][0], &b = heap[best][0];
+      const int64_t lhs = (t.load + c) * sp.s[best], rhs = (b.load + c) * sp.s[x];
+      if (lhs < rhs || (lhs == rhs && t.worker < b.worker)) best = x;
+    }
+    std::vector<Load> &h = heap[best];
+    Load top = h[0];
+    worker[idx_sorted[k]] = top.worker;
+    top.load += c;
+    load[top.worker] = top.load;
+    size_t i = 0;                                             // sift the grown root down
+    for (;;) {
+      const size_t l = 2 * i + 1, r = l + 1;
+      size_t m = i;
+      const Load *bst = &top;
+      if (l < h.size() && lighter(h[l], *bst)) { m = l; bst = &h[l]; }
+      if (r < h.size() && lighter(h[r], *bst)) { m = r; bst = &h[r]; }
+      if (m == i) break;
+      h[i] = h[m];
+      i = m;
+    }
+    h[i] = top;
+  }
+}
+
+Queue place(const std::vector<libra_item> &units, int workers, int mode, const Speeds &sp) {
   Queue q;
   const size_t n = units.size();
   std::vector<int32_t> worker(n);
   std::vector<int32_t> order(n);
   std::vector<int64_t> load(workers, 0);
-  if (mode == LIBRA_ASSIGN_PLACER) {
+  if (mode == LIBRA_ASSIGN_PLACER && !sp.uniform) {
+    std::vector<int32_t> idx(n);
+    for (size_t i = 0; i < n; ++i) idx[i] = (int32_t)i;
+    std::sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
+      return units[a].cost != units[b].cost ? units[a].cost > units[b].cost : a < b;
+    });
+    std::vector<int64_t> cs(n);
+    for (size_t k = 0; k < n; ++k) {
+      cs[k] = units[idx[k]].cost;
+      order[k] = idx[k];
+    }
+    place_weighted(cs, idx, workers, sp, worker, load);
+  } else if (mode == LIBRA_ASSIGN_PLACER) {
     struct Key {
       int64_t cost;
       int32_t idx;
@@ -178,6 +243,20 @@ Queue place(const std::vector<libra_item> &units, int workers, int mode) {
   return q;
 }
 
+// Largest finish time (load / speed) over the mean one; with equal speeds,
+// the largest load over the mean load.
+double finish_max_over_mean(const Queue &q, int workers, const Speeds &sp) {
+  double mx = 0, sum = 0;
+  for (int r = 0; r < workers; ++r) {
+    int64_t l = 0;
+    for (int32_t k = q.cu_off[r]; k < q.cu_off[r + 1]; ++k) l += q.items[k].cost;
+    const double f = (double)l / (double)sp.s[r % 8];
+    mx = std::max(mx, f);
+    sum += f;
+  }
+  return sum > 0 ? mx * workers / sum : 1.0;
+}
+
 // Zigzag units.  Items sharing a group key (for the dK/dV items: the sample
 // of the last key and the KV head; for forward and dQ items: the sample of
 // the first row, the KV head and the first head) are taken in row order
@@ -190,11 +269,11 @@ Queue place(const std::vector<libra_item> &units, int workers, int mode) {
 // the CUs sharing an L2 share the streamed rows.  Equal-cost pairs are
 // coarser than single items: when one group holds most of the work they leave
 // too few small units to level the workers, so the pairs are kept only if
-// their largest worker load is within 0.5 % of the mean load; otherwise the
-// single items are placed, all in the default order.
+// their largest finish time (load / speed) is within 0.5 % of the mean one;
+// otherwise the single items are placed, all in the default order.
 // Items arrive in id order (id = index) and rows ascend within a group.
 Queue place_zigzag(const std::vector<libra_item> &items, const std::vector<int64_t> &group, int workers,
-                   int mode) {
+                   int mode, const Speeds &sp) {
   const size_t n = items.size();
   std::vector<int32_t> second(n, -2);   // -2: not a unit's first item, -1: alone
   {
@@ -217,8 +296,8 @@ Queue place_zigzag(const std::vector<libra_item> &items, const std::vector<int64
       if (second[i] >= 0) u.cost += items[second[i]].cost;
       units.push_back(u);
     }
-  Queue uq = place(units, workers, mode);
-  if (uq.load_max * 1000 * workers > uq.load_sum * 1005) return place(items, workers, mode);
+  Queue uq = place(units, workers, mode, sp);
+  if (finish_max_over_mean(uq, workers, sp) > 1.005) return place(items, workers, mode, sp);
   Queue q;
   q.load_max = uq.load_max;
   q.load_sum = uq.load_sum;
@@ -480,9 +559,10 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
     }
     return key;
   };
-  std::thread t_dq([&] { dq = place_zigzag(dq_items, group_keys(dq_items, false), workers, p.assign); });
-  std::thread t_kv([&] { kq = place_zigzag(kv_items, group_keys(kv_items, true), workers, p.assign); });
-  fq = place_zigzag(items, group_keys(items, false), workers, p.assign);
+  const Speeds sp(p.worker_speed);
+  std::thread t_dq([&] { dq = place_zigzag(dq_items, group_keys(dq_items, false), workers, p.assign, sp); });
+  std::thread t_kv([&] { kq = place_zigzag(kv_items, group_keys(kv_items, true), workers, p.assign, sp); });
+  fq = place_zigzag(items, group_keys(items, false), workers, p.assign, sp);
   t_dq.join();
   t_kv.join();
 
@@ -542,6 +622,43 @@ extern "C" libra_status libra_plan_check(const void *plan, size_t bytes, libra_p
     if (e > bytes) return LIBRA_EINVAL;
   if (libra::plan_checksum(plan, bytes) != hdr.checksum) return LIBRA_EINVAL;
   if (info) *info = hdr;
+  return LIBRA_OK;
+}
+
+extern "C" libra_status libra_worker_speed(const void *plan_host, int32_t queue, const libra_cu_record *records,
+                                           uint16_t speed_out[8]) {
+  libra_plan_info h;
+  if (!plan_host || !records || !speed_out) return LIBRA_EINVAL;
+  if (libra::plan_header(plan_host, &h) != LIBRA_OK) return LIBRA_EINVAL;
+  if (queue < LIBRA_QUEUE_FWD || queue > LIBRA_QUEUE_KV) return LIBRA_EINVAL;
+  const uint8_t *base = static_cast<const uint8_t *>(plan_host);
+  const uint64_t off_items[] = {h.off_items, h.off_dq_items, h.off_kv_items};
+  const uint64_t off_cu[] = {h.off_cu_off, h.off_dq_cu_off, h.off_kv_cu_off};
+  const libra_item *items = reinterpret_cast<const libra_item *>(base + off_items[queue]);
+  const int32_t *cu_off = reinterpret_cast<const int32_t *>(base + off_cu[queue]);
+  double load[8] = {0}, busy[8] = {0};
+  for (int w = 0; w < h.num_cus; ++w) {
+    int64_t l = 0;
+    for (int32_t k = cu_off[w]; k < cu_off[w + 1]; ++k) l += items[k].cost;
+    const uint64_t t0 = records[w].t_start, t1 = records[w].t_end;
+    if (l <= 0 || t1 <= t0) continue;
+    load[w % 8] += (double)l;
+    busy[w % 8] += (double)(t1 - t0);
+  }
+  double rate[8], mean = 0;
+  int classes = 0;
+  for (int x = 0; x < 8; ++x) {
+    rate[x] = busy[x] > 0 ? load[x] / busy[x] : 0.0;
+    if (rate[x] > 0) {
+      mean += rate[x];
+      ++classes;
+    }
+  }
+  if (classes) mean /= classes;
+  for (int x = 0; x < 8; ++x) {
+    const double v = rate[x] > 0 ? 1000.0 * rate[x] / mean : 1000.0;
+    speed_out[x] = (uint16_t)std::lround(std::min(2000.0, std::max(500.0, v)));
+  }
   return LIBRA_OK;
 }
 

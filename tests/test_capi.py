@@ -48,6 +48,10 @@ CASES = [
      {"num_cus": 32}),
     ([7, 300, 1, 1, 250], 12, 4, 64, 100, 6, {"num_cus": 9}),
     ([400, 600], 8, 2, 128, 128, 8, {"assign": 1, "num_cus": 7}),
+    # workers of unequal speed (eight classes, worker mod 8)
+    (list(synth.make_lengths(synth.WORKLOADS["train_256k"].with_tokens(7000), 1)), 32, 4, 128, 1000, 4,
+     {"num_cus": 24, "worker_speed": [1000, 940, 1010, 950, 1060, 1000, 990, 940]}),
+    ([1024, 512, 256, 256], 4, 4, 64, 256, 2, {"num_cus": 13, "worker_speed": [500, 2000, 0, 1000, 1500, 800, 0, 700]}),
 ]
 
 
@@ -71,7 +75,8 @@ def test_planner_matches_oracle(lens, h_q, h_kv, d, B, W, kw):
     mode = "rr" if kw.get("assign", 0) == 1 else "lpt"
     ov = kw.get("item_overhead", 0)
     items = P.fwd_items(cu, L, h_q, h_kv, B, W, overhead=ov)
-    offsets, ids, flags, load = P.zigzag_queue(cu, items, ncu, 0.03, mode)
+    sp = kw.get("worker_speed")
+    offsets, ids, flags, load = P.zigzag_queue(cu, items, ncu, 0.03, mode, speed=sp)
     assert list(plan.cu_off) == offsets
     got_items = plan.items
     assert [int(x) for x in got_items["id"]] == ids
@@ -85,7 +90,7 @@ def test_planner_matches_oracle(lens, h_q, h_kv, d, B, W, kw):
                                                for t in ref_tiles]
     # dQ items (the same tiles, cut for the dQ kernel) and their placement
     dq = P.fwd_items(cu, L, h_q, h_kv, B, W, overhead=ov, columns=P.DQ_ITEM_COLUMNS)
-    offsets, ids, flags, load = P.zigzag_queue(cu, dq, ncu, 0.03, mode)
+    offsets, ids, flags, load = P.zigzag_queue(cu, dq, ncu, 0.03, mode, speed=sp)
     assert list(plan.dq_cu_off) == offsets
     got_dq = plan.dq_items
     assert [int(x) for x in got_dq["id"]] == ids
@@ -97,7 +102,7 @@ def test_planner_matches_oracle(lens, h_q, h_kv, d, B, W, kw):
     assert info.dq_load_max == max(load) and info.dq_load_sum == sum(load)
     # key-major dK/dV items and their placement
     kv = P.kv_items(cu, L, h_q, h_kv, overhead=ov)
-    offsets, ids, flags, load = P.zigzag_queue(cu, kv, ncu, 0.03, mode, last_key=True)
+    offsets, ids, flags, load = P.zigzag_queue(cu, kv, ncu, 0.03, mode, last_key=True, speed=sp)
     assert list(plan.kv_cu_off) == offsets
     got_kv = plan.kv_items
     assert [int(x) for x in got_kv["id"]] == ids
@@ -140,7 +145,8 @@ def test_plan_check_rejects_corruption():
 
 def _params(**over):
     p = dict(total_tokens=10, num_samples=2, h_q=4, h_kv=2, head_dim=128, tile_tokens=4, tile_heads=2,
-             num_cus=0, tau=0.03, assign=0, item_overhead=0)
+             num_cus=0, tau=0.03, assign=0, item_overhead=0,
+             worker_speed=(ctypes.c_uint16 * 8)(*([0] * 8)))
     p.update(over)
     return lib.PlanParams(*[p[f] for f, _ in lib.PlanParams._fields_])
 
@@ -295,3 +301,23 @@ def test_library_shares_torchs_hip_runtime():
     maps = open(f"/proc/{os.getpid()}/maps").read()
     paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(paths) == 1, paths
+
+
+def test_worker_speed_recovers_class_rates():
+    """Records whose busy ticks are load x 1000 / speed of the worker's class give back those
+    speeds, scaled to a mean of 1000 (host function, synthetic records)."""
+    lens = list(synth.make_lengths(synth.WORKLOADS["train_256k"].with_tokens(20000), 0))
+    plan, cu = make_plan(lens, 32, 4, 128, 4096, 4, num_cus=64)
+    speed = np.array([1000, 900, 1100, 950, 1050, 1000, 980, 1020], dtype=np.float64)
+    for q, items, off in ((lib.QUEUE_FWD, plan.items, plan.cu_off), (lib.QUEUE_DQ, plan.dq_items, plan.dq_cu_off),
+                          (lib.QUEUE_KV, plan.kv_items, plan.kv_cu_off)):
+        rec = np.zeros(64, dtype=lib.RECORD_DTYPE)
+        for w in range(64):
+            load = int(items["cost"][off[w]:off[w + 1]].sum())
+            rec["t_start"][w] = 1000
+            rec["t_end"][w] = 1000 + int(round(load * 1000 / speed[w % 8] / 1000))
+        got = lib.libra_worker_speed(plan.host, q, rec).astype(np.float64)
+        expect = 1000 * speed / speed.mean()
+        assert np.all(np.abs(got - expect) <= 1.0), (q, got, expect)
+    with pytest.raises(lib.LibraError):
+        lib.libra_worker_speed(plan.host, 3, np.zeros(64, dtype=lib.RECORD_DTYPE))

@@ -181,3 +181,11 @@ def test_fwd_zigzag_pairs_hand_worked():
                                                           (480, 20), (500, 96), (596, 96), (692, 96),
                                                           (788, 96), (884, 96), (980, 20)]
     assert P.zigzag_units(cu, items) == [(0, 11), (1, 10), (2, 9), (3, 8), (4, 7), (5, 6)]
+
+
+def test_weighted_placement_hand_worked():
+    """Two workers, worker 0 twice as fast: 6 -> worker 0 (finishes at 3 vs 6); 4 -> worker 1
+    (4 vs 5); 3 -> worker 0 (4.5 vs 7).  Equal speeds give plain LPT."""
+    sigma, order = P.place([6, 4, 3], 2, speed=[2000, 1000, 0, 0, 0, 0, 0, 0])
+    assert order == [0, 1, 2] and sigma == [0, 1, 0]
+    assert P.place([6, 4, 3], 2, speed=[700] * 8) == P.place([6, 4, 3], 2)
