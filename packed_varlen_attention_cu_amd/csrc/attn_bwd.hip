@@ -379,9 +379,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kDqWaves * 64, kDqWaves * 
 void attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = kDqWaves;
   constexpr int NS = D / 16, ND = D / 32;
-  constexpr int BLK = kKB * PadRows<D>::kStride;   // elements of one padded block
+  constexpr int RS = PadRows<D>::kStride;          // K rows: direct and transposing reads
+  constexpr int RV = PadRows<D>::kDirectStride;    // V rows: direct reads only
+  constexpr int KBLK = kKB * RS, BUF = KBLK + kKB * RV;
   // kStages buffers of a K and a V block; block b uses buffer b mod kStages.
-  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[kStages * 2 * BLK];
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[kStages * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int half = lane >> 5, col = lane & 31;
@@ -390,12 +392,16 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const int beg = a.cu_off[w], end = a.cu_off[w + 1];
   const float c = a.scale_log2;
   const uint32_t kv_base = lds_addr(kv_lds);
-  const int dlo = direct_lane_off<PadRows<D>::kStride>(lane);        // K / V operand reads
-  const int tlo = tr_lane_off<PadRows<D>::kStride>(lane);            // K^T operand reads
+  const int dlo = direct_lane_off<RS>(lane);       // K operand reads
+  const int dlo_v = direct_lane_off<RV>(lane);     // V operand reads
+  const int tlo = tr_lane_off<RS>(lane);           // K^T operand reads
   const int64_t kv_stride = (int64_t)a.h_kv * D;
-  RowCopy<D, kKB, NW> kvcopy;
-  kvcopy.init(wave, lane, kv_stride);
-  const int copies = 2 * RowCopy<D, kKB, NW>::count(wave);   // this wave's copies per block
+  RowCopy<D, kKB, NW, RS> kcopy;
+  RowCopy<D, kKB, NW, RV> vcopy;
+  kcopy.init(wave, lane, kv_stride);
+  vcopy.init(wave, lane, kv_stride);
+  // this wave's copies per block
+  const int copies = RowCopy<D, kKB, NW, RS>::count(wave) + RowCopy<D, kKB, NW, RV>::count(wave);
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -430,13 +436,13 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     for (int dt = 0; dt < ND; ++dt) dqacc[dt] = zero16();
 
     auto issue = [&](int k0, int buf) {   // rows past L are masked; clamped to row L - 1
-      const uint32_t dst = kv_base + buf * 4 * BLK;   // bytes
-      kvcopy.issue(dst, wave, a.k + kvh * D, kv_stride, k0, a.L);
-      kvcopy.issue(dst + 2 * BLK, wave, a.v + kvh * D, kv_stride, k0, a.L);
+      const uint32_t dst = kv_base + buf * 2 * BUF;   // bytes
+      kcopy.issue(dst, wave, a.k + kvh * D, kv_stride, k0, a.L);
+      vcopy.issue(dst + 2 * KBLK, wave, a.v + kvh * D, kv_stride, k0, a.L);
     };
 
     auto block = [&](int b, int buf) {
-      const uint16_t *bk = kv_lds + buf * 2 * BLK;
+      const uint16_t *bk = kv_lds + buf * BUF;
       const int k0 = kblock(b);
       wait_vmem_upto(b + 1 < nkb ? copies : 0);   // block b landed; block b + 1 may fly
       wait_lds();
@@ -446,7 +452,7 @@ void attn_bwd_dq_kernel(BwdArgs a) {
       const bool partial = qok && !((k0 >= qss) && (k0 + kKB - 1 <= qpos));
       if (wave_any(touch)) {
         const bool masked = wave_any(partial);
-        const uint16_t *k_l = bk, *v_l = bk + BLK;
+        const uint16_t *k_l = bk, *v_l = bk + KBLK;
         const int lo = qok ? qss : 1, hi = qok ? qpos : 0;
         // One 32-key tile at a time keeps S^T, dP^T and dS^T of a single tile live.
 #pragma unroll
@@ -454,9 +460,8 @@ void attn_bwd_dq_kernel(BwdArgs a) {
           f32x16 sacc = zero16(), pacc = zero16();   // S^T and dP^T (lane = query)
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
-            const int off = dlo + direct_off<PadRows<D>::kStride>(kt, s);
-            const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(k_l + off));
-            const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(v_l + off));
+            const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(k_l + dlo + direct_off<RS>(kt, s)));
+            const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(v_l + dlo_v + direct_off<RV>(kt, s)));
             sacc = mfma32x32x16(ka, qop[s], sacc);
             pacc = mfma32x32x16(va, dop[s], pacc);
           }
@@ -485,8 +490,8 @@ void attn_bwd_dq_kernel(BwdArgs a) {
           for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {   // K^T operand read transposed from the row-major K block
-              const bf16x8 ka = lds_tr_operand(k_l + tlo + tr_off<PadRows<D>::kStride>(kt * 32 + 16 * t, dt * 32, 0),
-                                               k_l + tlo + tr_off<PadRows<D>::kStride>(kt * 32 + 16 * t, dt * 32, 1));
+              const bf16x8 ka = lds_tr_operand(k_l + tlo + tr_off<RS>(kt * 32 + 16 * t, dt * 32, 0),
+                                               k_l + tlo + tr_off<RS>(kt * 32 + 16 * t, dt * 32, 1));
               dqacc[dt] = mfma32x32x16(ka, as_bf16x8(dsw[t]), dqacc[dt]);
             }
         }

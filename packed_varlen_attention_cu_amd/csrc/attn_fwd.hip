@@ -72,7 +72,7 @@ void attn_fwd_kernel(FwdArgs a) {
   constexpr int QW = 32 * QT;                   // query positions per wave
   constexpr int NS = D / 16;                    // reduction slabs of d
   constexpr int ND = D / 32;                    // 32-row tiles of d in O^T
-  constexpr int RS = PadRows<D>::kStride;      // K rows: direct operand reads
+  constexpr int RS = PadRows<D>::kDirectStride;   // K rows: direct operand reads only
   constexpr int RV = PadRows<D>::kTrStride;    // V rows: transposing reads only
   // kStages buffers, each a K and a V block [kBN][D] in padded rows; block b
   // uses buffer b mod kStages and is copied kStages - 1 blocks ahead.  The V^T

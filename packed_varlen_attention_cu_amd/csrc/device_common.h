@@ -198,14 +198,21 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
 // (here 16 rows at one column), an 8-byte transposing read 32 lanes (here 4
 // rows x 64 bytes).  The first is conflict-free when the stride in 16-byte
 // units is odd, the second when the stride is an odd multiple of 64 bytes;
-// no stride is both, so blocks read only by transposing reads get their own:
-//   kStride   = 152 elements (D = 128) or 72 (D = 64): direct reads;
-//   kTrStride = 160 elements (D = 128) or 96 (D = 64): transposing reads.
+// no stride is both, so each block takes the stride of the reads it serves:
+//   kStride       = 152 elements (D = 128) or 72 (D = 64): blocks read both ways
+//                   (direct reads conflict-free, transposing reads one extra
+//                   cycle in two);
+//   kDirectStride = 136 (D = 128) or 72 (D = 64): blocks read only directly,
+//                   the shortest conflict-free rows (17 copy instructions per
+//                   64-row block instead of 19);
+//   kTrStride     = 160 (D = 128) or 96 (D = 64): blocks read only through
+//                   transposing reads.
 // Every operand address stays a per-lane base plus a compile-time offset.
 template <int D>
 struct PadRows {
   static_assert(D == 128 || D == 64, "head_dim 64 or 128");
   static constexpr int kStride = D == 128 ? 152 : 72;     // elements per row
+  static constexpr int kDirectStride = D == 128 ? 136 : 72;
   static constexpr int kTrStride = D == 128 ? 160 : 96;
 };
 
