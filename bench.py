@@ -347,6 +347,54 @@ def granularity():
             torch.cuda.empty_cache()
 
 
+def simulate(packs=3, seed=0):
+    """Configuration simulator (host only; the single-GPU counterpart of the pages' replay of
+    VRSP and the placer over windows for candidate configurations).  For packs of train_256k's
+    shape and each SH-Tile shape (B tokens x W heads): the planner's intra-GPU imbalance per
+    queue (largest over mean planned load) and the bytes the kernels stream into LDS (each item
+    copies its K/V blocks, or its Q/dO blocks for dK/dV, once), which is what smaller tiles cost
+    on one GPU in place of the pages' exchange volume.  Inter-pool imbalance is VRSP's
+    (--vrsp); it does not depend on B or W."""
+    import synth
+    import packed_varlen_attention_cu_amd as lib
+    w0 = synth.WORKLOADS["train_256k"]
+    d, blk = w0.head_dim, 64
+    print("| tile tokens B | tile heads W | tiles | fwd items | fwd planned max/mean | dQ planned max/mean | "
+          "dK/dV planned max/mean | streamed K/V + Q/dO bytes (GB) | plan ms |")
+    print("|---|---|---|---|---|---|---|---|---|", flush=True)
+    lens = [synth.make_lengths(w0, seed + i) for i in range(packs)]
+    for b_ in (512, 2048, 8192, 32768):
+        for w_ in (1, 2, 4, 8):
+            agg = {"tiles": 0, "items": 0, "f": [], "q": [], "k": [], "bytes": 0.0, "ms": []}
+            for ln in lens:
+                cu = synth.cu_seqlens(ln)
+                t0 = time.perf_counter()
+                p_ = lib.Plan(cu, total_tokens=w0.total_tokens, h_q=w0.h_q, h_kv=w0.h_kv, head_dim=d,
+                              tile_tokens=b_, tile_heads=w_)
+                agg["ms"].append((time.perf_counter() - t0) * 1e3)
+                i_ = p_.info
+                n = i_.num_cus
+                agg["tiles"] += i_.n_tiles
+                agg["items"] += i_.n_items
+                agg["f"].append(i_.load_max / (i_.load_sum / n))
+                agg["q"].append(i_.dq_load_max / (i_.dq_load_sum / n))
+                agg["k"].append(i_.kv_load_max / (i_.kv_load_sum / n))
+                starts = cu[np.searchsorted(cu, np.arange(w0.total_tokens), side="right") - 1]
+                for its in (p_.items, p_.dq_items):       # K and V blocks per item
+                    r0 = its["row0"].astype(np.int64)
+                    ks = starts[r0] & ~(blk - 1)
+                    nb = (r0 + its["nrows"] - ks + blk - 1) // blk
+                    agg["bytes"] += float(nb.sum()) * 2 * blk * d * 2
+                kv = p_.kv_items                          # Q and dO blocks of every head per step
+                r0 = kv["row0"].astype(np.int64)
+                ends = np.searchsorted(cu, r0 + kv["nrows"] - 1, side="right")
+                qb = (cu[ends] - (r0 & ~(blk - 1)) + blk - 1) // blk
+                agg["bytes"] += float((qb * kv["nheads"]).sum()) * 2 * blk * d * 2
+            print(f"| {b_} | {w_} | {agg['tiles'] // packs} | {agg['items'] // packs} | "
+                  f"{np.mean(agg['f']):.4f} | {np.mean(agg['q']):.4f} | {np.mean(agg['k']):.4f} | "
+                  f"{agg['bytes'] / packs / 1e9:.1f} | {np.median(agg['ms']):.1f} |", flush=True)
+
+
 def vrsp_report(windows=20, seed=0):
     """Variance-reduced sequence placement (host only): time per window, and the residual
     inter-pool imbalance R - 1 (max / mean pool workload - 1) under the sampler's index order,
@@ -655,6 +703,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", help="markdown table of rocprofv3 --pmc runs")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="run the sustained bf16 MFMA probe (constant vs random operands, ~3 s each)")
+    ap.add_argument("--simulate", action="store_true",
+                    help="host-only configuration simulator: planner imbalance and streamed bytes per SH-Tile shape")
     ap.add_argument("--vrsp", action="store_true",
                     help="host-only: variance-reduced sequence placement timing and pool balance")
     ap.add_argument("--no-speed-calibration", action="store_true",
@@ -682,6 +732,9 @@ def main():
         return
     if args.vrsp:
         vrsp_report()
+        return
+    if args.simulate:
+        simulate()
         return
     if args.mfma_ceiling or args.atomic_rate:
         import subprocess

@@ -54,7 +54,7 @@ typedef enum {
 
 enum {
   LIBRA_ASSIGN_PLACER = 0,       /* Algorithm 2 (FLOPs-aware, heaviest first) */
-  LIBRA_ASSIGN_ROUND_ROBIN = 1   /* item i -> CU i mod num_cus (ablation) */
+  LIBRA_ASSIGN_ROUND_ROBIN = 1   /* placement unit i -> CU i mod num_cus (ablation) */
 };
 
 #define LIBRA_PLAN_MAGIC 0x4152424Cu   /* "LBRA" little-endian */
