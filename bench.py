@@ -30,7 +30,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6       # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "packed varlen causal attn TFLOP/s (fwd, fwd+bwd), % bf16 MFMA peak, CU max/mean"
-DEVICE_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "device_common.h"]
+# what the device code is compiled from (package-relative), flags included
+DEVICE_SOURCES = ["csrc/attn_fwd.hip", "csrc/attn_bwd.hip", "csrc/attn_bwd_dq.hip", "csrc/bwd_common.h",
+                  "csrc/device_common.h", "csrc/plan_layout.h", "build.py"]
 # Algorithmic FLOPs per unmasked (query, key, head) pair for each kernel:
 #   forward: QK^T and PV (2 x 2d); dK/dV pass: S recompute, dP, dV, dK (4 x 2d);
 #   dQ pass: dQ (2d) -- its S and dP recomputations are not algorithmic work.
@@ -44,7 +46,7 @@ def source_hash() -> str:
     import re
     h = hashlib.sha256()
     for name in DEVICE_SOURCES:
-        with open(os.path.join(ROOT, "packed_varlen_attention_cu_amd", "csrc", name)) as f:
+        with open(os.path.join(ROOT, "packed_varlen_attention_cu_amd", name)) as f:
             text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
         for line in text.splitlines():
             line = re.sub(r"//.*", "", line).strip()

@@ -22,7 +22,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["plan.cpp", "vrsp.cpp"]
-DEVICE_SOURCES = ["attn_fwd.hip", "attn_bwd.hip"]
+DEVICE_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip"]
+# Instruction scheduling per source: LLVM's max-ILP strategy makes the forward
+# 4.5 % and the dQ pass 2 % faster but the dK/dV pass 3 % slower (measured), so
+# it is given to the sources whose kernels gain from it.
+SOURCE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+                "attn_bwd_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 PROBES = ["mfma_ceiling", "mem_probes"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-I", INCLUDE, "-I", CSRC, "-Wall"]
@@ -52,7 +57,8 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
         jobs.append([HIPCC, *COMMON, "-x", "c++", "-c", os.path.join(CSRC, src),
                      "-o", os.path.join(objdir, src + ".o")])
     for src in DEVICE_SOURCES:
-        jobs.append([HIPCC, *COMMON, *DEVICE_FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
+        jobs.append([HIPCC, *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), *[f"-D{d}" for d in defines],
+                     "-c", os.path.join(CSRC, src),
                      "-o", os.path.join(objdir, src + ".o")])
     with ThreadPoolExecutor(min(8, len(jobs))) as ex:
         for r in ex.map(_run, jobs):
