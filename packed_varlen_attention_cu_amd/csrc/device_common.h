@@ -292,6 +292,76 @@ struct RowCopy {
   }
 };
 
+// Copy of two blocks of NR rows each (D elements per row, row r at src +
+// r * stride), the first into LDS rows of RA elements and the second into
+// rows of RB, as one list of NA + NB one-kilobyte LDS-DMA instructions:
+// instruction g is issued by wave g mod NW.  When NW divides NA + NB, every
+// wave issues exactly kPerWave copies per pair of blocks, so the count a
+// wave waits for is a compile-time constant and no wave branches on whether
+// it has a copy to issue.  Padding slots re-copy the row's first chunk, as
+// in RowCopy.
+template <int D, int NR, int NW, int RA, int RB>
+struct PairCopy {
+  static constexpr int NA = (NR * RA * 2 + 1023) / 1024;
+  static constexpr int NB = (NR * RB * 2 + 1023) / 1024;
+  static constexpr int NI = NA + NB;
+  static constexpr int NJ = (NI + NW - 1) / NW;
+  static constexpr bool kUniform = NI % NW == 0;
+  static constexpr int kPerWave = NI / NW;
+  static_assert(NA * 1024 == NR * RA * 2 && NB * 1024 == NR * RB * 2, "the blocks fill whole copy instructions");
+  uint32_t voff[NJ];                         // byte offset of the lane's source: row * stride + col
+
+  // Copy instructions a wave issues per pair of blocks.
+  static __device__ __forceinline__ int count(int wave) { return wave < NI ? (NI - 1 - wave) / NW + 1 : 0; }
+
+  __device__ __forceinline__ void init(int wave, int lane, int64_t stride) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int g = wave + j * NW;
+      const bool in_a = g < NA;
+      const int rs = in_a ? RA : RB;
+      const int e = 512 * (in_a ? g : g - NA) + 8 * lane;   // element offset of the lane's slot
+      const int row = e / rs, c = e - row * rs;
+      const int col = c < D ? c : 0;
+      voff[j] = g < NI ? (uint32_t)(2 * ((int64_t)row * stride + col)) : 0u;
+    }
+  }
+  // Rows r0 .. r0 + NR - 1 of both tensors; rows at or past `rows` (only in
+  // the pack's last block) are replaced by row rows - 1, recovering the
+  // lane's row and column from its offset behind an empty asm statement so
+  // that none of it is hoisted out of the caller's loops.
+  __device__ __forceinline__ void issue(uint32_t lds_a, uint32_t lds_b, int wave, const uint16_t *base_a,
+                                        const uint16_t *base_b, int64_t stride, int r0, int rows) const {
+    const void *ba = uniform_ptr(base_a + (int64_t)r0 * stride);
+    const void *bb = uniform_ptr(base_b + (int64_t)r0 * stride);
+    if (r0 + NR <= rows) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int g = wave + j * NW;
+        if (kUniform || g < NI) {
+          const bool in_a = g < NA;
+          lds_dma16_s(in_a ? ba : bb, voff[j], in_a ? lds_a + 1024 * g : lds_b + 1024 * (g - NA));
+        }
+      }
+    } else {
+      const uint32_t st = (uint32_t)stride;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int g = wave + j * NW;
+        if (kUniform || g < NI) {
+          const bool in_a = g < NA;
+          uint32_t vo = voff[j];
+          asm volatile("" : "+v"(vo));
+          const uint32_t e = vo >> 1;            // row * stride + col
+          const uint32_t row = e / st, col = e - row * st;
+          const uint32_t rr = (uint32_t)min(r0 + (int)row, rows - 1) - (uint32_t)r0;
+          lds_dma16_s(in_a ? ba : bb, 2 * (rr * st + col), in_a ? lds_a + 1024 * g : lds_b + 1024 * (g - NA));
+        }
+      }
+    }
+  }
+};
+
 // Direct A operand: lane (col, half) reads row sigma_row(col) + 32 t of the
 // block, reduction elements 16 s + 8 half .. + 7.  direct_lane_off is the
 // lane's part; slab (t, s) adds direct_off(t, s).
