@@ -60,10 +60,17 @@ constexpr int kDkdvGroups = kKvItemKeys / 32;   // key groups of 32
 constexpr int kDkdvWaves = 2 * kDkdvGroups;      // a P wave and a dS wave per group
 static_assert(kDkdvWaves % 4 == 0, "whole waves per SIMD");
 
+// Q blocks take 152-element rows (D = 128; 72 at D = 64) and dO blocks 168
+// (72): both are read directly and through transposing reads, and 168 has
+// the same conflict profile as 152.  A Q and a dO block then fill 19 + 21 =
+// 40 copy instructions; with the eight row-vector copies (LSE, D) that makes
+// four per wave for each of the twelve waves at D = 128.
 template <int D>
 struct DkdvLds {
-  static constexpr int kRow = kQB * PadRows<D>::kStride;   // elements of one padded block
-  static constexpr int kBuf = 2 * kRow + 2 * kQB * 2;      // Q, dO + LSE and D (fp32), in uint16 units
+  static constexpr int kRQ = PadRows<D>::kStride;          // Q row stride (elements)
+  static constexpr int kRO = D == 128 ? 168 : PadRows<D>::kStride;   // dO row stride
+  static constexpr int kRowQ = kQB * kRQ, kRowO = kQB * kRO;   // elements of one padded block
+  static constexpr int kBuf = kRowQ + kRowO + 2 * kQB * 2;  // Q, dO + LSE and D (fp32), in uint16 units
   static constexpr int kP = kDkdvGroups * 32 * kQB;       // bf16 P of every key group
 };
 
@@ -74,7 +81,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NW = kDkdvWaves;
   constexpr int NS = D / 16, ND = D / 32;
   static_assert(2 * kQB <= NW * 16, "LSE and D copies: 16 values per wave");
-  constexpr int ROW = DkdvLds<D>::kRow;
+  constexpr int RQ = DkdvLds<D>::kRQ, RO = DkdvLds<D>::kRO;
+  constexpr int ROWQ = DkdvLds<D>::kRowQ, ROWO = DkdvLds<D>::kRowO;
   // kStages buffers of a step's Q, dO, LSE and D; step i uses buffer i mod kStages.
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[kStages * DkdvLds<D>::kBuf];
   __shared__ __attribute__((aligned(16))) uint16_t p_lds[DkdvLds<D>::kP];
@@ -88,18 +96,27 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   const float c = a.scale_log2;
   const uint32_t q_base = lds_addr(q_lds);
   u32x4 *p_mine = reinterpret_cast<u32x4 *>(p_lds + kg * 32 * kQB) + lane;   // [4 slabs][64 lanes]
-  const int dlo = direct_lane_off<PadRows<D>::kStride>(lane);        // Q / dO operand reads
-  const int tlo = tr_lane_off<PadRows<D>::kStride>(lane);            // Q^T / dO^T operand reads
   const int64_t q_stride = (int64_t)a.h_q * D;
-  RowCopy<D, kQB, NW> qcopy;
-  qcopy.init(wave, lane, q_stride);
-  const bool rowvec = wave * 16 < 2 * kQB;         // the wave copies 16 LSE / D values
-  const int copies = 2 * RowCopy<D, kQB, NW>::count(wave) + (rowvec ? 1 : 0);   // this wave's copies per step
+  using QOCopy = PairCopy<D, kQB, NW, RQ, RO>;
+  QOCopy qocopy;
+  qocopy.init(wave, lane, q_stride);
+  // The last kRowVec waves copy 16 LSE / D values each; they are the waves
+  // with one Q / dO copy fewer whenever kUniformStep holds.
+  constexpr int kRowVec = 2 * kQB / 16;
+  constexpr bool kUniformStep = QOCopy::NI % NW == NW - kRowVec;
+  constexpr int kStepCopies = QOCopy::NI / NW + 1;
+  const int rv = wave - (NW - kRowVec);            // row-vector copy of this wave, if >= 0
+  const bool rowvec = rv >= 0;
+  const int copies = QOCopy::count(wave) + (rowvec ? 1 : 0);   // this wave's copies per step
 
   // The two roles are separate instantiations, so each allocates registers
   // for its own path only; both pass the same barriers.
   auto run = [&](auto role) {
     constexpr bool pwave = decltype(role)::value;
+    // Direct reads: Q (P wave) or dO (dS wave); transposing reads: the other.
+    constexpr int RA = pwave ? RQ : RO, RT = pwave ? RO : RQ;
+    const int dlo = direct_lane_off<RA>(lane);
+    const int tlo = tr_lane_off<RT>(lane);
     for (int it = beg; it < end; ++it) {
       const libra_item item = a.items[it];
       const int row0 = item.row0, nrows = item.nrows, kvh = item.kv_head;
@@ -129,15 +146,14 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
       // are masked, so their addresses are clamped to row L - 1.
       auto issue = [&](int h, int q0, int buf) {
         const uint32_t dst = q_base + buf * 2 * DkdvLds<D>::kBuf;   // bytes
-        qcopy.issue(dst, wave, a.q + h * D, q_stride, q0, a.L);
-        qcopy.issue(dst + 2 * ROW, wave, a.dout + h * D, q_stride, q0, a.L);   // byte offsets
-        // LSE * log2(e) then D of the block's queries: lanes 0..15 of the first
-        // 2 kQB / 16 waves copy 16 values each.
+        qocopy.issue(dst, dst + 2 * ROWQ, wave, a.q + h * D, a.dout + h * D, q_stride, q0, a.L);   // byte offsets
+        // LSE * log2(e) then D of the block's queries: lanes 0..15 of the last
+        // kRowVec waves copy 16 values each.
         if (rowvec && lane < 16) {
-          const int e = wave * 16 + lane;             // 0 .. 2 kQB - 1
+          const int e = rv * 16 + lane;               // 0 .. 2 kQB - 1
           const int qq = min(q0 + (e & (kQB - 1)), a.L - 1);
           const float *src = (e < kQB ? a.lse2 : a.dvec) + (int64_t)h * a.L + qq;
-          lds_dma4(src, dst + 4 * ROW + wave * 64);
+          lds_dma4(src, dst + 2 * (ROWQ + ROWO) + rv * 64);
         }
       };
 
@@ -161,7 +177,12 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
         const uint16_t *bq = q_lds + buf * DkdvLds<D>::kBuf;
         const int q0 = cq0;
         advance(ch, cq0);
-        wait_vmem_upto(i + 1 < nsteps ? copies : 0);   // step i landed; step i + 1 may fly
+        // step i landed; step i + 1 may fly
+        if (kUniformStep) {
+          if (i + 1 < nsteps) wait_vmem<kStepCopies>(); else wait_vmem<0>();
+        } else {
+          wait_vmem_upto(i + 1 < nsteps ? copies : 0);
+        }
         wait_lds();                   // own LDS accesses of step i - 1 done
         block_barrier();
         if (i + kStages - 1 < nsteps) {
@@ -172,8 +193,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
         const bool full = !kok || ((key <= q0) && (q0 + kQB - 1 < kend));
         const bool act = wave_any(touch);     // identical for the two waves of a key group
         const bool masked = wave_any(!full);
-        const uint16_t *q_l = bq, *do_l = bq + ROW;
-        const float *lse_l = reinterpret_cast<const float *>(bq + 2 * ROW);
+        const uint16_t *q_l = bq, *do_l = bq + ROWQ;
+        const float *lse_l = reinterpret_cast<const float *>(bq + ROWQ + ROWO);
         const float *dd_l = lse_l + kQB;
 
         // First product of query tile qt: S (P wave, A = Q) or dP (dS wave, A = dO).
@@ -182,7 +203,7 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
           f32x16 out = zero16();
 #pragma unroll
           for (int s = 0; s < NS; ++s)
-            out = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4 *>(a_l + direct_off<PadRows<D>::kStride>(qt, s))),
+            out = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4 *>(a_l + direct_off<RA>(qt, s))),
                                bop[s], out);
           return out;
         };
@@ -193,8 +214,8 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
           for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt) {
-              const bf16x8 av = lds_tr_operand(t_l + tr_off<PadRows<D>::kStride>(qt * 32 + 16 * t, dt * 32, 0),
-                                               t_l + tr_off<PadRows<D>::kStride>(qt * 32 + 16 * t, dt * 32, 1));
+              const bf16x8 av = lds_tr_operand(t_l + tr_off<RT>(qt * 32 + 16 * t, dt * 32, 0),
+                                               t_l + tr_off<RT>(qt * 32 + 16 * t, dt * 32, 1));
               acc[dt] = mfma32x32x16(av, as_bf16x8(wv[t]), acc[dt]);
             }
         };

@@ -55,7 +55,10 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = kDqWaves;
   constexpr int NS = D / 16, ND = D / 32;
   constexpr int RS = PadRows<D>::kStride;          // K rows: direct and transposing reads
-  constexpr int RV = PadRows<D>::kDirectStride;    // V rows: direct reads only
+  // V rows, read only directly, take the conflict-free 168 (D = 128) or 120
+  // (D = 64) elements, so that a K and a V block fill 19 + 21 = 40 (9 + 15 =
+  // 24) copy instructions, the same number for each of the eight waves.
+  constexpr int RV = D == 128 ? 168 : 120;
   constexpr int KBLK = kKB * RS, BUF = KBLK + kKB * RV;
   // kStages buffers of a K and a V block; block b uses buffer b mod kStages.
   __shared__ __attribute__((aligned(16))) uint16_t kv_lds[kStages * BUF];
@@ -71,12 +74,10 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const int dlo_v = direct_lane_off<RV>(lane);     // V operand reads
   const int tlo = tr_lane_off<RS>(lane);           // K^T operand reads
   const int64_t kv_stride = (int64_t)a.h_kv * D;
-  RowCopy<D, kKB, NW, RS> kcopy;
-  RowCopy<D, kKB, NW, RV> vcopy;
-  kcopy.init(wave, lane, kv_stride);
-  vcopy.init(wave, lane, kv_stride);
-  // this wave's copies per block
-  const int copies = RowCopy<D, kKB, NW, RS>::count(wave) + RowCopy<D, kKB, NW, RV>::count(wave);
+  using KVCopy = PairCopy<D, kKB, NW, RS, RV>;
+  static_assert(KVCopy::kUniform, "every wave issues the same number of copies");
+  KVCopy kvcopy;
+  kvcopy.init(wave, lane, kv_stride);
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -112,14 +113,14 @@ void attn_bwd_dq_kernel(BwdArgs a) {
 
     auto issue = [&](int k0, int buf) {   // rows past L are masked; clamped to row L - 1
       const uint32_t dst = kv_base + buf * 2 * BUF;   // bytes
-      kcopy.issue(dst, wave, a.k + kvh * D, kv_stride, k0, a.L);
-      vcopy.issue(dst + 2 * KBLK, wave, a.v + kvh * D, kv_stride, k0, a.L);
+      kvcopy.issue(dst, dst + 2 * KBLK, wave, a.k + kvh * D, a.v + kvh * D, kv_stride, k0, a.L);
     };
 
     auto block = [&](int b, int buf) {
       const uint16_t *bk = kv_lds + buf * BUF;
       const int k0 = kblock(b);
-      wait_vmem_upto(b + 1 < nkb ? copies : 0);   // block b landed; block b + 1 may fly
+      // block b landed; block b + 1 may fly
+      if (b + 1 < nkb) wait_vmem<KVCopy::kPerWave>(); else wait_vmem<0>();
       wait_lds();
       block_barrier();
       if (b + kStages - 1 < nkb) issue(kblock(b + kStages - 1), buf == 0 ? kStages - 1 : buf - 1);
