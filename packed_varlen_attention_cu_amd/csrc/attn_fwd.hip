@@ -37,7 +37,7 @@
 namespace libra {
 
 constexpr int kBN = 64;          // keys per block
-constexpr int kStages = 3;       // LDS buffers: copies run kStages - 1 blocks ahead
+constexpr int kStages = 4;       // LDS buffers: copies run kStages - 1 blocks ahead
 
 struct FwdArgs {
   const libra_item *items;
@@ -153,15 +153,20 @@ void attn_fwd_kernel(FwdArgs a) {
     };
 
     // One key block.  Once this wave's copies of block b have landed (those of
-    // block b + 1 may still fly) and its reads of block b - 1 have completed,
+    // later blocks may still fly) and its reads of block b - 1 have completed,
     // one barrier makes both true for every wave; then block b + kStages - 1
     // is queued into the buffer block b - 1 used, and block b is computed.
     auto block = [&](int b, int buf) {
       const int k0 = kblock(b);
+      // The copies of up to kStages - 2 later blocks may still fly.
+      const int later = min(kStages - 2, nblk - 1 - b);
       if (KVCopy::kUniform) {
-        if (b + 1 < nblk) wait_vmem<KVCopy::kPerWave>(); else wait_vmem<0>();
+        static_assert((kStages - 2) * KVCopy::kPerWave < 64, "vmcnt range");
+        if (kStages > 3 && later >= 2) wait_vmem<2 * KVCopy::kPerWave>();
+        else if (later >= 1) wait_vmem<KVCopy::kPerWave>();
+        else wait_vmem<0>();
       } else {
-        wait_vmem_upto(b + 1 < nblk ? copies : 0);
+        wait_vmem_upto(later * copies);
       }
       wait_lds();
       block_barrier();
