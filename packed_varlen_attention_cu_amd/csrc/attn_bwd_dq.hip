@@ -133,6 +133,7 @@ void attn_bwd_dq_kernel(BwdArgs a) {
         // One 32-key tile at a time keeps S^T, dP^T and dS^T of a single tile live.
 #pragma unroll
         for (int kt = 0; kt < kKB / 32; ++kt) {
+          __builtin_amdgcn_sched_barrier(0);   // the groups below cover this tile's S^T and dP^T only
           f32x16 sacc = zero16(), pacc = zero16();   // S^T and dP^T (lane = query)
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
@@ -140,6 +141,18 @@ void attn_bwd_dq_kernel(BwdArgs a) {
             const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(v_l + dlo_v + direct_off<RV>(kt, s)));
             sacc = mfma32x32x16(ka, qop[s], sacc);
             pacc = mfma32x32x16(va, dop[s], pacc);
+          }
+          // Two K / V operand reads first, then one read after each product:
+          // every product finds its operand loaded while the next read flies.
+          {
+            constexpr int kReads = 2 * NS, kAhead = 2;
+            __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+            for (int i = 0; i < kReads - kAhead; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
           }
           if (masked) {             // rare: blocks on a sample start or the diagonal
 #pragma unroll
