@@ -24,11 +24,11 @@ ARCH = "gfx950"
 HOST_SOURCES = ["plan.cpp", "vrsp.cpp"]
 DEVICE_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip"]
 # Instruction scheduling per source, as measured: LLVM's max-ILP strategy makes
-# the forward 4.5 % and the dQ pass 2 % faster but the dK/dV pass 3 % slower;
-# the dK/dV pass gains 0.5 % from the iterative max-occupancy strategy.
+# the forward 3-5 % and the dQ pass up to 2 % faster but the dK/dV pass 3 %
+# slower; the dK/dV pass keeps the default strategy (0.5-1 % ahead of the
+# iterative max-occupancy one since its copies were made uniform).
 SOURCE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
-                "attn_bwd_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
-                "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-maxocc"]}
+                "attn_bwd_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 PROBES = ["mfma_ceiling", "mem_probes"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-I", INCLUDE, "-I", CSRC, "-Wall"]
