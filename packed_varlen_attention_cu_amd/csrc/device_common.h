@@ -204,92 +204,16 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
 //                   cycle in two);
 //   kDirectStride = 136 (D = 128) or 72 (D = 64): blocks read only directly,
 //                   the shortest conflict-free rows (17 copy instructions per
-//                   64-row block instead of 19);
-//   kTrStride     = 160 (D = 128) or 96 (D = 64): blocks read only through
-//                   transposing reads.
+//                   64-row block instead of 19).
+// Blocks read only through transposing reads would be conflict-free at 160
+// (D = 128); the kernels pick strides so that the copies of a block pair
+// divide evenly among their waves (PairCopy) instead.
 // Every operand address stays a per-lane base plus a compile-time offset.
 template <int D>
 struct PadRows {
   static_assert(D == 128 || D == 64, "head_dim 64 or 128");
   static constexpr int kStride = D == 128 ? 152 : 72;     // elements per row
   static constexpr int kDirectStride = D == 128 ? 136 : 72;
-  static constexpr int kTrStride = D == 128 ? 160 : 96;
-};
-
-// Copy of a block of NR rows (D elements each, row r at src + r * stride)
-// into LDS in padded rows.  The block takes exactly NI one-kilobyte LDS-DMA
-// instructions (no lane falls past the last row); instruction i is issued by
-// wave i mod NW.  A lane whose 16-byte slot is a row's padding copies that
-// row's first chunk into the padding, which is never read, so no lane is
-// switched off.  The lane's offsets are fixed per kernel and computed once.
-template <int D, int NR, int NW, int RS = PadRows<D>::kStride>
-struct RowCopy {
-  static constexpr int NI = (NR * RS * 2 + 1023) / 1024;
-  static constexpr int NJ = (NI + NW - 1) / NW;
-  static_assert(NI * 1024 == NR * RS * 2, "the block fills whole copy instructions");
-  uint32_t voff[NJ];                         // byte offset of the lane's source: row * stride + col
-
-  // Copy instructions a wave issues per block.
-  static __device__ __forceinline__ int count(int wave) { return wave < NI ? (NI - 1 - wave) / NW + 1 : 0; }
-  // Block row and column (element) the lane copies in the wave's j-th copy;
-  // lanes that land in a row's padding re-copy column 0.
-  static __device__ __forceinline__ void slot(int wave, int lane, int j, int &row, int &col) {
-    const int e = 512 * (wave + j * NW) + 8 * lane;   // element offset of the lane's slot
-    row = e / RS;
-    const int c = e - row * RS;
-    col = c < D ? c : 0;
-  }
-
-  __device__ __forceinline__ void init(int wave, int lane, int64_t stride) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      int row, col;
-      slot(wave, lane, j, row, col);
-      voff[j] = (uint32_t)(2 * ((int64_t)row * stride + col));
-    }
-  }
-  // Rows r0 .. r0 + NR - 1 of the tensor at base (whose row r starts at
-  // base + r * stride), for blocks that end at or before row `rows`: one
-  // scalar base address per block, the lanes' offsets fixed for the kernel.
-  __device__ __forceinline__ void issue_full(uint32_t lds, int wave, const uint16_t *base, int64_t stride,
-                                             int r0) const {
-    const void *b = uniform_ptr(base + (int64_t)r0 * stride);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int i = wave + j * NW;
-      if (i < NI) lds_dma16_s(b, voff[j], lds + 1024 * i);
-    }
-  }
-  // The same for a block that runs past row `rows` (only the pack's last
-  // block): rows at or past `rows` are replaced by row rows - 1.  The lane's
-  // row and column are recovered from its offset here, behind an empty asm
-  // statement, so that none of this arithmetic is hoisted out of the loops
-  // that call it (it would hold registers for the whole kernel).
-  __device__ __forceinline__ void issue_tail(uint32_t lds, int wave, const uint16_t *base, int64_t stride, int r0,
-                                             int rows) const {
-    const void *b = uniform_ptr(base + (int64_t)r0 * stride);
-    const uint32_t st = (uint32_t)stride;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int i = wave + j * NW;
-      if (i < NI) {
-        uint32_t vo = voff[j];
-        asm volatile("" : "+v"(vo));
-        const uint32_t e = vo >> 1;              // row * stride + col
-        const uint32_t row = e / st, col = e - row * st;
-        const uint32_t rr = (uint32_t)min(r0 + (int)row, rows - 1) - (uint32_t)r0;
-        lds_dma16_s(b, 2 * (rr * st + col), lds + 1024 * i);
-      }
-    }
-  }
-  // Either of the two, chosen per block (wave-uniform).
-  __device__ __forceinline__ void issue(uint32_t lds, int wave, const uint16_t *base, int64_t stride, int r0,
-                                        int rows) const {
-    if (r0 + NR <= rows)
-      issue_full(lds, wave, base, stride, r0);
-    else
-      issue_tail(lds, wave, base, stride, r0, rows);
-  }
 };
 
 // Copy of two blocks of NR rows each (D elements per row, row r at src +
@@ -298,8 +222,9 @@ struct RowCopy {
 // instruction g is issued by wave g mod NW.  When NW divides NA + NB, every
 // wave issues exactly kPerWave copies per pair of blocks, so the count a
 // wave waits for is a compile-time constant and no wave branches on whether
-// it has a copy to issue.  Padding slots re-copy the row's first chunk, as
-// in RowCopy.
+// it has a copy to issue.  A lane whose 16-byte slot is a row's padding
+// copies that row's first chunk into the padding, which is never read, so no
+// lane is switched off.  The lane's offsets are fixed per kernel.
 template <int D, int NR, int NW, int RA, int RB>
 struct PairCopy {
   static constexpr int NA = (NR * RA * 2 + 1023) / 1024;
