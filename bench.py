@@ -39,6 +39,7 @@ DEVICE_SOURCES = ["csrc/attn_fwd.hip", "csrc/attn_bwd.hip", "csrc/attn_bwd_dq.hi
 KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 2}
 KERNEL_SYMBOL = {"fwd": "attn_fwd_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel",
                  "bwd_dq": "attn_bwd_dq_kernel"}
+PLACEMENT_NAMES = {0: "algorithm2", 1: "round_robin", 2: "algorithm2_l2"}
 
 
 def source_hash() -> str:
@@ -330,6 +331,30 @@ def sweep():
                 torch.cuda.empty_cache()
 
 
+def ab_table(workloads, rounds=2):
+    """Plan variants side by side: Algorithm 2 with executed-work item costs (the default), with
+    eq. 8 pair costs, and with the L2 residency term; rounds interleave the variants so that
+    drifting clocks hit them alike."""
+    import torch
+    variants = [("algorithm2, executed cost", 0, 0), ("algorithm2, pair cost", 0, 1),
+                ("algorithm2 + L2 term, executed cost", 2, 0)]
+    print("| workload | plan | round | fwd ms | fwd TFLOP/s | dK/dV ms | dQ ms | step TFLOP/s | "
+          "CU busy max/mean fwd / dK/dV / dQ |")
+    print("|---|---|---|---|---|---|---|---|---|", flush=True)
+    for wl in workloads:
+        fwd_only = wl != "train_256k"
+        for rnd in range(rounds):
+            for label, assign, cost in variants:
+                o = measure(wl, 0, assign, fwd_only, 5, 2, False, quiet=True, cost=cost)
+                km, busy = o["kernel_ms"], o["cu_busy_max_over_mean"]
+                print(f"| {wl} | {label} | {rnd} | {km['fwd']:.3f} | {o['fwd_tflops']:.1f} | "
+                      f"{km.get('bwd_dkdv', float('nan')):.3f} | {km.get('bwd_dq', float('nan')):.3f} | "
+                      f"{o['value'] if not fwd_only else float('nan'):.1f} | "
+                      + " / ".join(f"{busy[k]:.3f}" for k in ("fwd", "bwd_dkdv", "bwd_dq") if k in busy) + " |",
+                      flush=True)
+                torch.cuda.empty_cache()
+
+
 def granularity():
     """Forward of train_256k at seed 0 for SH-Tiles of B tokens x W heads: the planner cuts
     work items inside tiles, so B and W set where items are cut and how many query heads
@@ -455,9 +480,22 @@ def vrsp_report(windows=20, seed=0):
                   f"{np.mean(vr):.5f} | {np.mean(lb):.5f} |", flush=True)
 
 
+_INPUTS = {}
+
+
 def pooled_inputs(workload, seed, names):
     """Workload, sample lengths and bf16 tensors of one pack, or of a pool "a+b+...": the packs
-    concatenated into one (the block-diagonal mask keeps them apart), planned and launched once."""
+    concatenated into one (the block-diagonal mask keeps them apart), planned and launched once.
+    Kept for the next call with the same arguments (the A/B tables time several plans of one
+    pack)."""
+    key = (workload, seed, tuple(names))
+    if key not in _INPUTS:
+        _INPUTS.clear()
+        _INPUTS[key] = _make_inputs(workload, seed, names)
+    return _INPUTS[key]
+
+
+def _make_inputs(workload, seed, names):
     import synth
     parts = [synth.WORKLOADS[n] for n in workload.split("+")]
     w0 = parts[0]
@@ -475,7 +513,8 @@ def pooled_inputs(workload, seed, names):
 
 
 def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, warmup=2, cpu=True,
-            calibrate_copy=0, quiet=False, tiling=None, dump_records=None, speed_calibration=True):
+            calibrate_copy=0, quiet=False, tiling=None, dump_records=None, speed_calibration=True,
+            cost=0, item_overhead=0):
     """Time `steps` steps of the hot path on cuda:0; returns the JSON record.  `tiling`
     = (tile_tokens, tile_heads) replaces the workload's SH-Tile shape."""
     import torch
@@ -502,7 +541,7 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
 
     tile_tokens, tile_heads = tiling if tiling else (w.tile_tokens, w.tile_heads)
     plan_kw = dict(total_tokens=L, h_q=w.h_q, h_kv=w.h_kv, head_dim=d, tile_tokens=tile_tokens,
-                   tile_heads=tile_heads, assign=assign)
+                   tile_heads=tile_heads, assign=assign, cost=cost, item_overhead=item_overhead)
     plan0 = lib.Plan(cu, **plan_kw)
     ncu = plan0.info.num_cus
     ws_b = torch.empty(max(1, lib.libra_attn_bwd_workspace(plan0.host)), dtype=torch.uint8, device=dev)
@@ -569,7 +608,7 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
         step(plan, 0, False)
     torch.cuda.synchronize()
     speed = None
-    if plan is not None and speed_calibration and assign == 0:
+    if plan is not None and speed_calibration and assign in (0, 2):
         # The eight XCDs sustain different clocks; the last warm-up launch's per-CU records give
         # each one's rate, and the timed steps' plans place work by finish time on it.
         r = rec.cpu().numpy()
@@ -664,7 +703,8 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
         "config": {"workload": workload, "total_tokens": L, "h_q": w.h_q, "h_kv": w.h_kv,
                    "head_dim": d, "sh_tile": [tile_tokens, tile_heads], "samples": int(len(lengths)),
                    "max_sample": int(lengths.max()), "seed": seed, "pass": "fwd+bwd" if do_bwd else "fwd",
-                   "placement": "algorithm2" if assign == 0 else "round_robin", "num_cus": ncu},
+                   "placement": PLACEMENT_NAMES[assign], "item_cost": ("executed", "pairs")[cost],
+                   "num_cus": ncu},
         "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
         "fwd_frac_peak": round(fwd_flops / (avg["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": {n: round(t, 4) for n, t in avg.items()},
@@ -695,7 +735,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="train_256k")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--assign", type=int, default=0, help="0: Algorithm 2 placement, 1: round-robin")
+    ap.add_argument("--assign", type=int, default=0,
+                    help="0: Algorithm 2 placement, 1: round-robin, 2: Algorithm 2 with the L2 residency term")
+    ap.add_argument("--cost", choices=("executed", "pairs"), default="executed",
+                    help="forward / dQ item cost: executed query-key slots or eq. 8 pairs")
+    ap.add_argument("--item-overhead", type=int, default=0, help="cost added to every work item")
+    ap.add_argument("--ab", nargs="+", metavar="WORKLOAD",
+                    help="plan variants side by side (executed vs pair cost, L2 term) on these workloads")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
@@ -703,8 +749,6 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="DIR", help="markdown table of a rocprofv3 --kernel-trace run")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR", help="markdown table of rocprofv3 --pmc runs")
-    ap.add_argument("--mfma-ceiling", action="store_true",
-                    help="run the sustained bf16 MFMA probe (constant vs random operands, ~3 s each)")
     ap.add_argument("--simulate", action="store_true",
                     help="host-only configuration simulator: planner imbalance and streamed bytes per SH-Tile shape")
     ap.add_argument("--vrsp", action="store_true",
@@ -713,8 +757,6 @@ def main():
                     help="plan with equal worker speeds instead of the per-XCD rates of the warm-up")
     ap.add_argument("--dump-records", metavar="PATH",
                     help="write each workgroup's busy time and planned load (last timed step) as JSON")
-    ap.add_argument("--atomic-rate", action="store_true",
-                    help="run the fp32 atomic-add vs store throughput probe (dQ-shaped tiles)")
     ap.add_argument("--granularity", action="store_true",
                     help="forward of train_256k against the SH-Tile shape (tile tokens x tile heads)")
     ap.add_argument("--sweep", action="store_true",
@@ -738,13 +780,6 @@ def main():
     if args.simulate:
         simulate()
         return
-    if args.mfma_ceiling or args.atomic_rate:
-        import subprocess
-        name, argv = ("mfma_ceiling", []) if args.mfma_ceiling else ("mem_probes", ["atomic"])
-        probe = os.path.join(ROOT, "packed_varlen_attention_cu_amd", "_lib", name)
-        if not os.path.exists(probe):
-            sys.exit(f"{probe} is missing: build the package first")
-        sys.exit(subprocess.run([probe, *argv]).returncode)
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); sharding this path over "
               "several GPUs is a design note and is not run here.", file=sys.stderr)
@@ -756,9 +791,13 @@ def main():
     if args.granularity:
         granularity()
         return
+    if args.ab:
+        ab_table(args.ab)
+        return
     out = measure(args.workload, args.seed, args.assign, args.fwd_only, args.steps, args.warmup,
                   not args.no_cpu_baseline, args.calibrate_copy, dump_records=args.dump_records,
-                  speed_calibration=not args.no_speed_calibration)
+                  speed_calibration=not args.no_speed_calibration, cost=("executed", "pairs").index(args.cost),
+                  item_overhead=args.item_overhead)
     print(json.dumps(out), flush=True)
 
 

@@ -49,16 +49,50 @@ typedef enum {
   LIBRA_EINVAL = -1,        /* malformed argument: pointer, cu_seqlens, shape, plan */
   LIBRA_ESIZE = -2,         /* a caller buffer is too small (required size returned) */
   LIBRA_EUNSUPPORTED = -3,  /* well formed but not supported (e.g. head_dim) */
-  LIBRA_EHIP = -4           /* the HIP runtime rejected a launch */
+  LIBRA_EHIP = -4,          /* the HIP runtime rejected a launch */
+  LIBRA_EHOST = -5          /* the host ran out of memory or could not start a thread */
 } libra_status;
 
+/* Placement of the work items on the workers (libra_plan_params::assign).
+ * Algorithm 2 (Libra technical review, section 5.4) sends units heaviest
+ * first to a worker that stays within the soft target (1 + tau) x the even
+ * share, preferring the smallest communication term of eq. 9, then the
+ * least load, then the lowest id; if none stays within it, to the least
+ * loaded worker.  On one GPU nothing is sent over a network:
+ *   LIBRA_ASSIGN_PLACER     the communication term is 0, so the rule reduces
+ *                           to least-loaded (earliest-finish) placement;
+ *   LIBRA_ASSIGN_PLACER_L2  the term is eq. 9's KV part with the XCD's L2 in
+ *                           the role of the worker's memory: worker w runs on
+ *                           XCD w mod 8, a unit's KV groups are the (sample,
+ *                           KV head) pairs its rows meet, and the term is the
+ *                           token count of the groups not yet committed to
+ *                           that XCD (a group joins the XCD's set once a unit
+ *                           holding it is placed there);
+ *   LIBRA_ASSIGN_ROUND_ROBIN unit i -> worker i mod num_cus (ablation). */
 enum {
-  LIBRA_ASSIGN_PLACER = 0,       /* Algorithm 2 (FLOPs-aware, heaviest first) */
-  LIBRA_ASSIGN_ROUND_ROBIN = 1   /* placement unit i -> CU i mod num_cus (ablation) */
+  LIBRA_ASSIGN_PLACER = 0,
+  LIBRA_ASSIGN_ROUND_ROBIN = 1,
+  LIBRA_ASSIGN_PLACER_L2 = 2
+};
+
+/* Cost of a forward or dQ work item (libra_plan_params::cost).  The pages
+ * cost a tile by its unmasked causal pairs (eq. 8); a kernel that computes
+ * whole 64-key blocks executes more than that on blocks that straddle a
+ * sample start or the diagonal, most of all on short samples.
+ *   LIBRA_COST_EXECUTED  the query-key slots the kernel computes: for each of
+ *                        the item's waves (32 query positions of one head),
+ *                        32 x 64 per 64-key block holding a key one of its
+ *                        rows may see;
+ *   LIBRA_COST_PAIRS     the item's eq. 8 pairs.
+ * Either way item_overhead is added.  dK/dV items are always costed by the
+ * work their kernel executes (see libra_item). */
+enum {
+  LIBRA_COST_EXECUTED = 0,
+  LIBRA_COST_PAIRS = 1
 };
 
 #define LIBRA_PLAN_MAGIC 0x4152424Cu   /* "LBRA" little-endian */
-#define LIBRA_PLAN_VERSION 4u
+#define LIBRA_PLAN_VERSION 5u
 
 /* Planner inputs.  SH-Tiles (Libra technical review, section 5.1, eq. 6)
  * are tile_tokens (B) tokens by tile_heads (W = h_q / H) query heads. */
@@ -73,7 +107,7 @@ typedef struct {
   int32_t num_cus;        /* workers = persistent workgroups; 0 means 256 */
   float tau;              /* soft-target slack of Algorithm 2 (0.03 on the pages) */
   int32_t assign;         /* LIBRA_ASSIGN_* */
-  int64_t item_overhead;  /* cost added to every work item, in causal-pair units */
+  int64_t item_overhead;  /* cost added to every work item, in query-key slots */
   /* Relative speed of the workers of each class, worker w being of class
    * w mod 8 (on MI355X workgroup w runs on XCD w mod 8), in thousandths; 0
    * means 1000.  Algorithm 2 then sends each unit to the worker that would
@@ -81,6 +115,8 @@ typedef struct {
    * equal speeds give exactly the unweighted placement.  libra_worker_speed
    * estimates the speeds from the records of a previous launch. */
   uint16_t worker_speed[8];
+  int32_t cost;           /* LIBRA_COST_* for forward and dQ items */
+  int32_t reserved;       /* 0 */
 } libra_plan_params;
 
 /* One SH-Tile t = (block, shard), tile_id = block * (h_q / W) + shard.
@@ -110,8 +146,9 @@ typedef struct {
  *   and item m - 1 - i of the m items of one sample, KV head and first head,
  *   in row order) that run back to back, the second reversed: pairs then
  *   cost the same, and pairs started together read the same block at every
- *   step.  A queue whose pairs would leave a CU more than 0.5 % above the
- *   mean load gets single items, none reversed. */
+ *   step.  A queue whose pairs, placed by least finish time, would leave a
+ *   CU more than 0.5 % above the mean load gets single items, none
+ *   reversed. */
 #define LIBRA_ITEM_REVERSE 1
 typedef struct {
   int32_t row0, nrows;
@@ -119,7 +156,11 @@ typedef struct {
   int32_t tile_id;
   int32_t id;                       /* position in the planner's enumeration */
   int32_t flags;                    /* LIBRA_ITEM_REVERSE or 0 */
-  int64_t cost;                     /* placement key: pairs + item_overhead */
+  int64_t cost;                     /* placement key (query-key slots): forward and dQ items
+                                       by libra_plan_params::cost; dK/dV items by the slots
+                                       their kernel executes, g heads x 64-row query blocks
+                                       from the first key (rounded down to 64) to the end of
+                                       the last key's sample x 64 x nrows; + item_overhead */
   int64_t pairs;                    /* unmasked (query, key, head) triples */
 } libra_item;
 
@@ -145,9 +186,13 @@ typedef struct {
 
 /* Per-workgroup record of a persistent kernel (optional output).  hw_id and
  * xcc_id identify the physical CU; t_start / t_end are ticks of the
- * constant-rate device clock (libra_device_clock_khz). */
+ * constant-rate device clock (libra_device_clock_khz).  flags holds
+ * LIBRA_RECORD_PLAN_MISMATCH when the workgroup found that the device copy
+ * of the plan is not a copy of the host plan it was launched with (its
+ * checksum differs) and therefore ran no item. */
+#define LIBRA_RECORD_PLAN_MISMATCH 1u
 typedef struct {
-  uint32_t hw_id, xcc_id, n_items, reserved;
+  uint32_t hw_id, xcc_id, n_items, flags;
   uint64_t t_start, t_end;
 } libra_cu_record;
 

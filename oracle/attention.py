@@ -208,57 +208,3 @@ def backward(q, k, v, dout, cu_seqlens, scale):
             dk[start:end, kv] = b
             dv[start:end, kv] = c
     return dq, dk, dv
-
-
-
-# --------------------------------------------------------------------------
-# The bf16 yardstick of the tolerance.  The Libra paper (section 6.7,
-# "Numerical Fidelity") states the tolerance as FlashAttention's test-suite
-# criterion: errors against a high-precision reference stay within 2x the
-# errors of a bf16 PyTorch reference.  The functions below evaluate that bf16
-# reference: the same definition, each operation computed in float64 (standing
-# in for fp32 accumulation) with its output rounded to bf16 (round to nearest
-# even), as a plain bf16 implementation rounds every tensor it produces.  They
-# give the yardstick only; the results above remain what the path must match.
-
-def round_bf16(x: np.ndarray) -> np.ndarray:
-    """Nearest bf16 value (ties to even) of float64 values, as float64.  The value passes through
-    float32 first, as an fp32 result does before a bf16 implementation rounds it."""
-    f = np.asarray(x, dtype=np.float64).astype(np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    out = u.astype(np.uint32).view(np.float32).astype(np.float64)
-    return np.where(np.isfinite(f), out, f.astype(np.float64))
-
-
-def backward_bf16_reference(q, k, v, dout, cu_seqlens, scale):
-    """O and dq, dk, dv of a plain bf16 evaluation (every product, the scaling, the softmax
-    and its backward round their outputs to bf16; dk and dv sum the group's heads, then round).
-    Returns (o [L, h_q, d], dq, dk, dv), float64 holding bf16 values."""
-    L, h_q, d = q.shape
-    h_kv = k.shape[1]
-    g = _group(h_q, h_kv)
-    o = np.zeros((L, h_q, d))
-    dq = np.zeros((L, h_q, d))
-    dk = np.zeros((L, h_kv, d))
-    dv = np.zeros((L, h_kv, d))
-    for start, end in sample_ranges(cu_seqlens, L):
-        n = end - start
-        if n == 0:
-            continue
-        causal = np.tril(np.ones((n, n), dtype=bool))
-        for h in range(h_q):
-            kv = kv_head(h, h_q, h_kv)
-            Q, K, V, dO = q[start:end, h], k[start:end, kv], v[start:end, kv], dout[start:end, h]
-            S = round_bf16(round_bf16(Q @ K.T) * scale)
-            S = np.where(causal, S, -np.inf)
-            E = np.exp(S - S.max(axis=1, keepdims=True))
-            P = round_bf16(E / E.sum(axis=1, keepdims=True))
-            o[start:end, h] = round_bf16(P @ V)
-            dv[start:end, kv] += round_bf16(P.T @ dO)
-            dP = round_bf16(dO @ V.T)
-            dS = round_bf16(P * (dP - (dP * P).sum(axis=1, keepdims=True)))
-            dS = round_bf16(dS * scale)
-            dq[start:end, h] = round_bf16(dS @ K)
-            dk[start:end, kv] += round_bf16(dS.T @ Q)
-    return o, dq, round_bf16(dk), round_bf16(dv)

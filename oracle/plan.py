@@ -27,19 +27,28 @@ its own items and places them the same way:
     H = shard ∩ group(kappa) are cut into groups of nh heads, nh = 4 if |H| is a
     multiple of 4, else 2 if even, else 1;
   * each head group takes the tile's rows in chunks of c / nh positions.
-An item's pairs are eq. 8 restricted to its rows and heads; its cost is its
-pairs plus a fixed per-item overhead (a planner parameter).
-Items are numbered in (tile_id, kappa, head group, row chunk) order.
+An item's pairs are eq. 8 restricted to its rows and heads.  Items are
+numbered in (tile_id, kappa, head group, row chunk) order.
+
+Item cost (a reading: the pages cost a tile by its causal pairs, eq. 8, which
+measures the useful work but not what a kernel that computes whole 64-key
+blocks executes).  An item's workgroup runs c / 32 waves; wave w holds the 32
+query positions row0 + 32 * (w div nh) .. + 31 (clipped to the item) of head
+head0 + w mod nh, and computes every 64-key block that holds a key one of its
+rows may see: for a row r of sample j, the blocks floor(start_j / 64) ..
+floor(r / 64).  The executed cost counts 32 x 64 query-key slots for every
+(wave, block) so computed, plus a fixed per-item overhead (a planner
+parameter).  The "pairs" cost model (eq. 8 pairs plus the overhead) is kept
+for comparison.
 
 Key-major items for the dK/dV pass: keys are cut at global positions into
 chunks of 192 (the dK/dV kernel's six key groups of 32); item (chunk c, KV
 head kappa) has id c * h_kv + kappa and covers all g = h_q / h_kv query heads
 of kappa.  Its pairs count, for every key k in the chunk, the queries q >= k
-of k's sample: g * sum_k (end(k) - k).  Its cost (a reading: the pages
-define no cost for backward work) is the work the dK/dV kernel executes for
-it, masked or not: g heads x the query blocks of 64 rows from the chunk's
-first key rounded down to a multiple of 64 up to the end of the sample of its
-last key x 64 rows x its keys.
+of k's sample: g * sum_k (end(k) - k).  Its cost is the work the dK/dV kernel
+executes for it, masked or not: g heads x the query blocks of 64 rows from
+the chunk's first key rounded down to a multiple of 64 up to the end of the
+sample of its last key x 64 rows x its keys, plus the overhead.
 
 Zigzag units (a reading for one GPU: the pages place tiles, not items, and
 say nothing of walk order).  A forward or dQ item walks the key blocks of its
@@ -53,26 +62,48 @@ first item's id, and its worker runs u_i in the default order, then u_{m-1-i}
 in reverse (flag REVERSE).  Pairs of a group then cost the same, and pairs
 that start together read the same block at every step, which lets the
 workers of one L2 share the streamed rows.  Pairs are coarser units than
-single items: they are kept only if their largest worker load is within
-0.5 % of the mean load; otherwise the single items are placed, none
-reversed (a pack dominated by one sample and one KV head, such as the
-1M-token share, would otherwise lose its balance).
+single items: they are kept only if plain least-finish placement of the pairs
+leaves the largest worker finish time within 0.5 % of the mean one;
+otherwise the single items are placed, none reversed (a pack dominated by
+one sample and one KV head, such as the 1M-token share, would otherwise lose
+its balance).
 
-Placement (Algorithm 2, section 5.4).  C = (1 + tau) * sum f / |W|.  Units go
-in order of decreasing f, then id.  Among workers whose load stays <= C the
-placer takes the minimum of (dcomm, load, worker id); if there is none it
-takes the minimum of (load, dcomm, worker id).  On one GPU every tensor is
-already in HBM, so dcomm is 0 unless a caller passes a cost function.  A
-worker runs its units in the order they were placed.  The round-robin mode
-(unit i to worker i mod |W|) is the no-placement ablation.
+Placement (Algorithm 2, section 5.4).  Units go out heaviest first, equal
+costs in id order.  A unit goes to a worker that stays within the soft
+target of (1 + tau) times the even share if there is one -- among those the
+one whose communication term is smallest, then the least loaded, then the
+lowest id -- and otherwise to the least loaded worker, then smallest
+communication, then lowest id.  Loads are read as finish times load / speed:
+worker r belongs to speed class r mod 8 (the XCD that runs workgroup r),
+speeds in thousandths with 0 read as 1000 (an extension for workers of
+unequal speed; equal speeds give the section's rule exactly).  A worker
+runs its units in the order they were placed.
+
+The communication term (eq. 9) on one GPU.  Every tensor is in HBM, so
+nothing is sent; what an XCD fetches into its L2 plays the part of what a
+worker fetches over the network.  A unit's KV groups are (sample j, KV head
+kappa) for each non-empty sample j its rows meet (its key rows for dK/dV
+items; for a zigzag pair, the union of both items' groups), each of volume
+l_j tokens.  C_x is the set of groups already committed to XCD x, and
+dcomm(t, r) is the summed volume of t's groups not in C_{r mod 8}; after t
+goes to r, its groups join C_{r mod 8}.  Eq. 9's second term (Q and output
+away from a Q-home worker) has no counterpart: there is no Q home on one GPU.
+Mode "lpt" takes dcomm = 0, mode "l2" the residency term, mode "rr" is the
+no-placement ablation (unit i to worker i mod |W|).
 """
 from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
 
 ITEM_COLUMNS = 384                       # query positions x heads per forward item
 DQ_ITEM_COLUMNS = 256                    # query positions x heads per dQ item
 KV_CHUNK = 192                           # keys per dK/dV item
 KV_QUERY_BLOCK = 64                      # query rows per step of the dK/dV kernel
 REVERSE = 1                              # item flag: walk in the reverse of the default order
+QUERY_TILE = 32                          # query positions per wave of the forward and dQ kernels
+KEY_BLOCK = 64                           # keys per block the forward and dQ kernels compute
 
 
 def _ranges(cu):
@@ -132,8 +163,25 @@ def _head_group_size(n: int) -> int:
     return 1
 
 
-def fwd_items(cu, total_tokens, h_q, h_kv, B, W, overhead=0, columns=ITEM_COLUMNS) -> list:
-    """Forward work items in id order (dQ items: columns=DQ_ITEM_COLUMNS)."""
+def executed_slots(ranges, row0: int, nrows: int, nheads: int, columns: int) -> int:
+    """Query-key slots a forward or dQ workgroup computes for one item: for every wave, the
+    64-key blocks holding a key that one of its rows may see, times 32 x 64."""
+    total = 0
+    for w in range(columns // QUERY_TILE):
+        a = row0 + QUERY_TILE * (w // nheads)
+        e = min(row0 + nrows, a + QUERY_TILE)
+        blocks = set()
+        for s, end in ranges:          # rows of one sample add nested ranges: take its last row
+            last = min(e, end) - 1
+            if s < end and max(a, s) <= last:
+                blocks.update(range(s // KEY_BLOCK, last // KEY_BLOCK + 1))
+        total += len(blocks)
+    return total * QUERY_TILE * KEY_BLOCK
+
+
+def fwd_items(cu, total_tokens, h_q, h_kv, B, W, overhead=0, columns=ITEM_COLUMNS, cost="executed") -> list:
+    """Forward work items in id order (dQ items: columns=DQ_ITEM_COLUMNS); cost "executed" or
+    "pairs"."""
     g = h_q // h_kv
     ranges = _ranges(cu)
     items = []
@@ -147,9 +195,11 @@ def fwd_items(cu, total_tokens, h_q, h_kv, B, W, overhead=0, columns=ITEM_COLUMN
                 for r0 in range(t["tok_begin"], t["tok_end"], rows):
                     r1 = min(t["tok_end"], r0 + rows)
                     per_head, _ = _block_pairs(ranges, r0, r1)
+                    work = (nh * per_head if cost == "pairs"
+                            else executed_slots(ranges, r0, r1 - r0, nh, columns))
                     items.append(dict(id=len(items), tile_id=t["tile_id"], row0=r0, nrows=r1 - r0,
                                       kv_head=kappa, head0=heads[gi * nh], nheads=nh,
-                                      pairs=nh * per_head, cost=nh * per_head + overhead))
+                                      pairs=nh * per_head, cost=work + overhead))
     return items
 
 
@@ -181,37 +231,43 @@ def _speeds(speed):
     return s, all(x == s[0] for x in s)
 
 
-def place(costs, n_workers: int, tau: float = 0.03, dcomm=None, speed=None):
-    """Algorithm 2: returns (worker of each unit, units in placement order).  With worker
-    speeds (eight classes, worker r in class r mod 8, in thousandths, 0 = 1000) that are not
-    all equal, each unit goes to the worker that would finish it first, (load + cost) / speed,
-    ties to the lower worker id (an extension for workers of unequal speed; dcomm must be 0)."""
-    s, uniform = _speeds(speed)
-    if not uniform:
-        assert dcomm is None
-        from fractions import Fraction
-        order = sorted(range(len(costs)), key=lambda t: (-costs[t], t))
-        load = [0] * n_workers
-        sigma = [None] * len(costs)
-        for t in order:
-            r = min(range(n_workers), key=lambda r: (Fraction(load[r] + costs[t], s[r % 8]), r))
-            sigma[t] = r
-            load[r] += costs[t]
-        return sigma, order
+def _f32(x: float) -> float:
+    """The value a float parameter has once stored as a C float (the plan holds tau so)."""
+    return float(np.float32(x))
+
+
+def place(costs, n_workers: int, tau: float = 0.03, dcomm=None, speed=None, commit=None):
+    """Algorithm 2: returns (worker of each unit, units in placement order).
+
+    One argmin per unit over a key that ranks every worker within the soft
+    target ahead of every worker beyond it: (0, dcomm, finish, r) within,
+    (1, finish, dcomm, r) beyond, where finish = (load + cost) / speed.  Within
+    the target means finish <= (1 + tau) * sum(cost) / sum(speed), evaluated
+    as (load + cost) * sum(speed) <= (1 + tau) * sum(cost) * speed in double
+    precision.  dcomm(t, r) is the communication term (0 when None);
+    commit(t, r), if given, is told of each placement."""
+    s, _ = _speeds(speed)
     n = len(costs)
-    dcomm = dcomm or (lambda t, r: 0)
-    C = (1.0 + tau) * float(sum(costs)) / n_workers
-    order = sorted(range(n), key=lambda t: (-costs[t], t))
+    speed_sum = float(sum(s[r % 8] for r in range(n_workers)))
+    budget = (1.0 + _f32(tau)) * float(sum(costs))
     load = [0] * n_workers
     sigma = [None] * n
+    order = sorted(range(n), key=lambda t: (-costs[t], t))
     for t in order:
-        fits = [r for r in range(n_workers) if float(load[r] + costs[t]) <= C]
-        if fits:
-            r = min(fits, key=lambda r: (dcomm(t, r), load[r], r))
-        else:
-            r = min(range(n_workers), key=lambda r: (load[r], dcomm(t, r), r))
+        f = costs[t]
+
+        def key(r):
+            d = dcomm(t, r) if dcomm else 0
+            finish = Fraction(load[r] + f, s[r % 8])
+            if float(load[r] + f) * speed_sum <= budget * float(s[r % 8]):
+                return (0, d, finish, r)
+            return (1, finish, d, r)
+
+        r = min(range(n_workers), key=key)
         sigma[t] = r
-        load[r] += costs[t]
+        load[r] += f
+        if commit:
+            commit(t, r)
     return sigma, order
 
 
@@ -219,10 +275,31 @@ def round_robin(n_units: int, n_workers: int):
     return [i % n_workers for i in range(n_units)], list(range(n_units))
 
 
-def queue(costs, n_workers, tau=0.03, mode="lpt", speed=None):
-    """Per-worker queues as CSR: (offsets[n_workers + 1], unit ids, per-worker load)."""
+class L2Residency:
+    """Eq. 9's KV term on one GPU: the groups each XCD (worker r mod 8) has committed to."""
+
+    def __init__(self, unit_groups, volume, n_xcd=8):
+        self.groups = unit_groups          # per unit: set of group ids
+        self.volume = volume               # group id -> volume (tokens)
+        self.n_xcd = n_xcd
+        self.held = [set() for _ in range(n_xcd)]
+
+    def dcomm(self, t, r):
+        held = self.held[r % self.n_xcd]
+        return sum(self.volume[g] for g in self.groups[t] if g not in held)
+
+    def commit(self, t, r):
+        self.held[r % self.n_xcd] |= self.groups[t]
+
+
+def queue(costs, n_workers, tau=0.03, mode="lpt", speed=None, residency=None):
+    """Per-worker queues as CSR: (offsets[n_workers + 1], unit ids, per-worker load).  Mode
+    "l2" needs ``residency`` (an L2Residency over the same units)."""
     if mode == "lpt":
         sigma, order = place(costs, n_workers, tau, speed=speed)
+    elif mode == "l2":
+        sigma, order = place(costs, n_workers, tau, dcomm=residency.dcomm, speed=speed,
+                             commit=residency.commit)
     else:
         sigma, order = round_robin(len(costs), n_workers)
     per = [[] for _ in range(n_workers)]
@@ -243,6 +320,17 @@ def group_key(cu, it, last_key=False):
     r = it["row0"] + (it["nrows"] - 1 if last_key else 0)
     j = next(j for j, (s, e) in enumerate(_ranges(cu)) if s <= r < e)
     return (j, it["kv_head"], it["head0"])
+
+
+def kv_groups(cu, it, h_kv):
+    """KV groups of an item (eq. 7): (sample, KV head) of every non-empty sample its rows meet,
+    as ids j * h_kv + kappa."""
+    lo, hi = it["row0"], it["row0"] + it["nrows"]
+    return {j * h_kv + it["kv_head"] for j, (s, e) in enumerate(_ranges(cu)) if s < hi and e > lo and e > s}
+
+
+def group_volumes(cu, h_kv):
+    return {j * h_kv + kappa: e - s for j, (s, e) in enumerate(_ranges(cu)) for kappa in range(h_kv)}
 
 
 def zigzag_units(cu, items, last_key=False) -> list:
@@ -272,17 +360,25 @@ def finish_max_over_mean(load, n_workers, speed=None):
     return mx * n_workers / sm if sm > 0 else 1.0
 
 
-def zigzag_queue(cu, items, n_workers, tau=0.03, mode="lpt", last_key=False, speed=None):
+def zigzag_queue(cu, items, n_workers, tau=0.03, mode="lpt", last_key=False, speed=None, h_kv=None):
     """Per-worker queues as CSR: (offsets, item ids, item flags, per-worker load).  Units are
     placed like any other units; each expands into its first item (default walk), then its
-    second (flag REVERSE).  If the pairs' largest finish time (load / speed) exceeds the mean
-    one by more than 0.5 %, the single items are placed instead, none reversed."""
+    second (flag REVERSE).  If least-finish placement of the pairs leaves the largest finish time
+    more than 0.5 % above the mean one, the single items are placed instead, none reversed.
+    Mode "l2" (Algorithm 2 with the L2 residency term) needs h_kv."""
     units = zigzag_units(cu, items, last_key)
     costs = [items[a]["cost"] + (items[b]["cost"] if b is not None else 0) for a, b in units]
-    u_off, u_ids, load = queue(costs, n_workers, tau, mode, speed)
-    if finish_max_over_mean(load, n_workers, speed) > 1.005:     # pairs too coarse: single items
-        s_off, s_ids, s_load = queue([it["cost"] for it in items], n_workers, tau, mode, speed)
-        return s_off, s_ids, [0] * len(s_ids), s_load
+    trial = "rr" if mode == "rr" else "lpt"
+    _, _, trial_load = queue(costs, n_workers, tau, trial, speed)
+    if finish_max_over_mean(trial_load, n_workers, speed) > 1.005:     # pairs too coarse: single items
+        units = [(it["id"], None) for it in items]
+        costs = [it["cost"] for it in items]
+    residency = None
+    if mode == "l2":
+        groups = [kv_groups(cu, items[a], h_kv) | (kv_groups(cu, items[b], h_kv) if b is not None else set())
+                  for a, b in units]
+        residency = L2Residency(groups, group_volumes(cu, h_kv))
+    u_off, u_ids, load = queue(costs, n_workers, tau, mode, speed, residency)
     offsets, ids, flags = [0], [], []
     for r in range(n_workers):
         for u in u_ids[u_off[r]:u_off[r + 1]]:

@@ -20,10 +20,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # with different tuning macros); by default the in-tree build is loaded.
 LIB_PATH = os.environ.get("LIBRA_LIB") or os.path.join(_HERE, "_lib", "liblibra.so")
 
-LIBRA_OK, LIBRA_EINVAL, LIBRA_ESIZE, LIBRA_EUNSUPPORTED, LIBRA_EHIP = 0, -1, -2, -3, -4
-ASSIGN_PLACER, ASSIGN_ROUND_ROBIN = 0, 1
+LIBRA_OK, LIBRA_EINVAL, LIBRA_ESIZE, LIBRA_EUNSUPPORTED, LIBRA_EHIP, LIBRA_EHOST = 0, -1, -2, -3, -4, -5
+ASSIGN_PLACER, ASSIGN_ROUND_ROBIN, ASSIGN_PLACER_L2 = 0, 1, 2
+COST_EXECUTED, COST_PAIRS = 0, 1
 QUEUE_FWD, QUEUE_DQ, QUEUE_KV = 0, 1, 2
-PLAN_MAGIC, PLAN_VERSION = 0x4152424C, 1
+PLAN_MAGIC, PLAN_VERSION = 0x4152424C, 5
+RECORD_PLAN_MISMATCH = 1
 
 
 class LibraError(RuntimeError):
@@ -38,7 +40,8 @@ class PlanParams(ctypes.Structure):
                 ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("tile_tokens", ctypes.c_int32), ("tile_heads", ctypes.c_int32),
                 ("num_cus", ctypes.c_int32), ("tau", ctypes.c_float), ("assign", ctypes.c_int32),
-                ("item_overhead", ctypes.c_int64), ("worker_speed", ctypes.c_uint16 * 8)]
+                ("item_overhead", ctypes.c_int64), ("worker_speed", ctypes.c_uint16 * 8),
+                ("cost", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -63,10 +66,10 @@ TILE_DTYPE = np.dtype([("tile_id", "<i4"), ("block", "<i4"), ("shard", "<i4"), (
 ITEM_DTYPE = np.dtype([("row0", "<i4"), ("nrows", "<i4"), ("kv_head", "<i4"), ("head0", "<i4"),
                        ("nheads", "<i4"), ("tile_id", "<i4"), ("id", "<i4"), ("flags", "<i4"),
                        ("cost", "<i8"), ("pairs", "<i8")])
-RECORD_DTYPE = np.dtype([("hw_id", "<u4"), ("xcc_id", "<u4"), ("n_items", "<u4"), ("reserved", "<u4"),
+RECORD_DTYPE = np.dtype([("hw_id", "<u4"), ("xcc_id", "<u4"), ("n_items", "<u4"), ("flags", "<u4"),
                          ("t_start", "<u8"), ("t_end", "<u8")])
 
-assert ctypes.sizeof(PlanParams) == 64 and ctypes.sizeof(PlanInfo) == 224
+assert ctypes.sizeof(PlanParams) == 72 and ctypes.sizeof(PlanInfo) == 232
 assert TILE_DTYPE.itemsize == 48 and ITEM_DTYPE.itemsize == 48 and RECORD_DTYPE.itemsize == 32
 
 
@@ -239,12 +242,13 @@ class Plan:
     """A host plan buffer, typed views of its sections, and (lazily) its device copy."""
 
     def __init__(self, cu_seqlens, *, total_tokens, h_q, h_kv, head_dim, tile_tokens, tile_heads,
-                 num_cus=0, tau=0.03, assign=ASSIGN_PLACER, item_overhead=0, worker_speed=None):
+                 num_cus=0, tau=0.03, assign=ASSIGN_PLACER, item_overhead=0, worker_speed=None,
+                 cost=COST_EXECUTED):
         cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
         speed = (ctypes.c_uint16 * 8)(*([int(x) for x in worker_speed] if worker_speed is not None else [0] * 8))
         self.params = PlanParams(int(total_tokens), int(cu.size - 1), int(h_q), int(h_kv), int(head_dim),
                                  int(tile_tokens), int(tile_heads), int(num_cus), float(tau), int(assign),
-                                 int(item_overhead), speed)
+                                 int(item_overhead), speed, int(cost), 0)
         self.cu_seqlens = cu
         self.host = libra_plan(cu, self.params)
         # the header of a buffer the library just built (libra_plan_check verifies foreign ones)
@@ -298,14 +302,44 @@ def _stream_handle(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _check_tensors(plan: Plan, **tensors):
+    """Shapes, dtypes, contiguity and device of the tensors of one call, against the plan.  Every
+    check runs before any pointer reaches the library (a tensor shorter than the plan's packing
+    would let the kernels read or write past its end)."""
+    import torch
+    p = plan.params
+    L, d = p.total_tokens, p.head_dim
+    want = {"q": ((L, p.h_q, d), torch.bfloat16), "o": ((L, p.h_q, d), torch.bfloat16),
+            "dout": ((L, p.h_q, d), torch.bfloat16), "k": ((L, p.h_kv, d), torch.bfloat16),
+            "v": ((L, p.h_kv, d), torch.bfloat16), "lse": ((p.h_q, L), torch.float32)}
+    device = None
+    for name, t in tensors.items():
+        shape, dtype = want[name]
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, the plan needs {shape}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name}: dtype {t.dtype}, needs {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {device}")
+    if device is None or device.type != "cuda":
+        raise ValueError(f"the tensors must be on a GPU (got {device})")
+    return device
+
+
 def attn_fwd(plan: Plan, q, k, v, softmax_scale=None, *, out=None, lse=None, records=None):
-    """Forward pass on torch tensors (bf16, [L, h, d], contiguous); returns (o, lse)."""
+    """Forward pass on torch tensors (bf16 q [L, h_q, d], k and v [L, h_kv, d], contiguous, on one
+    GPU); returns (o, lse)."""
     import torch
     p = plan.params
     scale = 1.0 / math.sqrt(p.head_dim) if softmax_scale is None else softmax_scale
-    dev = q.device
+    extra = {n: t for n, t in (("o", out), ("lse", lse)) if t is not None}
+    dev = _check_tensors(plan, q=q, k=k, v=v, **extra)
     plan_dev, cu_dev = plan.device(dev)
-    o = torch.empty_like(q) if out is None else out
+    o = torch.empty((p.total_tokens, p.h_q, p.head_dim), dtype=torch.bfloat16, device=dev) if out is None else out
     lse = torch.empty((p.h_q, p.total_tokens), dtype=torch.float32, device=dev) if lse is None else lse
     libra_attn_fwd(plan.host, plan_dev, q, k, v, cu_dev, o, lse, scale, records, _stream_handle(dev))
     return o, lse
@@ -316,12 +350,16 @@ def attn_bwd(plan: Plan, q, k, v, o, lse, dout, softmax_scale=None, *, workspace
     import torch
     p = plan.params
     scale = 1.0 / math.sqrt(p.head_dim) if softmax_scale is None else softmax_scale
-    dev = q.device
+    dev = _check_tensors(plan, q=q, k=k, v=v, o=o, lse=lse, dout=dout)
     plan_dev, cu_dev = plan.device(dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=dev)
+    dk = torch.empty(tuple(k.shape), dtype=torch.bfloat16, device=dev)
+    dv = torch.empty(tuple(v.shape), dtype=torch.bfloat16, device=dev)
     ws_bytes = libra_attn_bwd_workspace(plan.host)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.numel() * workspace.element_size() < ws_bytes:
+        raise ValueError(f"workspace: needs {ws_bytes} bytes on {dev}")
     libra_attn_bwd(plan.host, plan_dev, q, k, v, o, dout, lse, cu_dev, dq, dk, dv, scale, workspace,
-                   workspace.numel(), records, _stream_handle(dev))
+                   workspace.numel() * workspace.element_size(), records, _stream_handle(dev))
     return dq, dk, dv

@@ -1,6 +1,7 @@
 """Build the in-tree shared library ``_lib/liblibra.so`` with hipcc for gfx950.
 
-Usage: ``python -m packed_varlen_attention_cu_amd.build`` (or ``build()``).
+Usage: ``python -m packed_varlen_attention_cu_amd.build`` (or ``build_all()``):
+builds ``_lib/liblibra.so`` and the counting build ``_lib/liblibra_debug.so``.
 Every call compiles from source; nothing is cached.
 """
 from __future__ import annotations
@@ -17,6 +18,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "liblibra.so")
+# The counting build: the forward kernel also counts the (query, key, head)
+# triples it leaves unmasked (include/libra_debug.h); tests only.
+DEBUG_LIB = os.path.join(LIBDIR, "liblibra_debug.so")
+DEBUG_DEFINES = ("LIBRA_COUNT_PAIRS",)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -29,7 +34,6 @@ DEVICE_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip"]
 # iterative max-occupancy one since its copies were made uniform).
 SOURCE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
                 "attn_bwd_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
-PROBES = ["mfma_ceiling", "mem_probes"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-I", INCLUDE, "-I", CSRC, "-Wall"]
 # Packed fp32 VALU forms are kept out of the generated code on purpose.
@@ -70,16 +74,15 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp])
     os.replace(tmp, out)
     shutil.rmtree(objdir, ignore_errors=True)
-    if os.path.abspath(out) == LIB:
-        # measurement tools that bench.py runs: the sustained-MFMA probe
-        # (--mfma-ceiling) and the atomic / LDS-bank probes (--atomic-rate, --lds-banks)
-        for name in PROBES:
-            probe = os.path.join(libdir, name)
-            _run([HIPCC, "-O3", "-std=c++17", *DEVICE_FLAGS, os.path.join(CSRC, name + ".hip"),
-                  "-o", probe + ".tmp"])
-            os.replace(probe + ".tmp", probe)
     return out
 
 
+def build_all(verbose: bool = False):
+    """The library and its counting build, compiled in parallel."""
+    with ThreadPoolExecutor(2) as ex:
+        jobs = [ex.submit(build, verbose), ex.submit(build, verbose, DEBUG_LIB, DEBUG_DEFINES)]
+        return [j.result() for j in jobs]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build_all(verbose=True))

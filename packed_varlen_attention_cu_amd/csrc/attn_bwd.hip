@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstddef>
 #include <initializer_list>
 #include <type_traits>
 
@@ -92,7 +93,9 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int kg = wave % kDkdvGroups;               // key group
   const int w = blockIdx.x;
   const uint64_t t_start = wall_clock64();
-  const int beg = a.cu_off[w], end = a.cu_off[w + 1];
+  // A device plan that is not a copy of the host plan runs no item.
+  const bool plan_ok = *a.plan_sum_dev == a.plan_sum;
+  const int beg = plan_ok ? a.cu_off[w] : 0, end = plan_ok ? a.cu_off[w + 1] : 0;
   const float c = a.scale_log2;
   const uint32_t q_base = lds_addr(q_lds);
   u32x4 *p_mine = reinterpret_cast<u32x4 *>(p_lds + kg * 32 * kQB) + lane;   // [4 slabs][64 lanes]
@@ -325,11 +328,11 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   if (wave < kDkdvGroups) run(std::true_type{});
   else run(std::false_type{});
   __syncthreads();
-  if (a.records != nullptr && tid == 0) write_record(a, w, end - beg, t_start);
+  if (a.records != nullptr && tid == 0) write_record(a, w, end - beg, t_start, plan_ok);
 }
 
 libra_status check_header(const void *plan, libra_plan_info *h) {
-  if (plan_header(plan, h) != LIBRA_OK) return LIBRA_EINVAL;
+  if (plan_validate(plan, h) != LIBRA_OK) return LIBRA_EINVAL;
   if (h->params.head_dim != 64 && h->params.head_dim != 128) return LIBRA_EUNSUPPORTED;
   return LIBRA_OK;
 }
@@ -400,6 +403,8 @@ libra_status launch_dkdv(const libra_plan_info &h, BwdArgs a, const void *plan_d
   const char *pd = static_cast<const char *>(plan_dev);
   a.items = reinterpret_cast<const libra_item *>(pd + h.off_kv_items);
   a.cu_off = reinterpret_cast<const int32_t *>(pd + h.off_kv_cu_off);
+  a.plan_sum_dev = reinterpret_cast<const uint64_t *>(pd + offsetof(libra_plan_info, checksum));
+  a.plan_sum = h.checksum;
   a.dk = static_cast<uint16_t *>(dk);
   a.dv = static_cast<uint16_t *>(dv);
   a.records = records;

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstddef>
 
 #include "bwd_common.h"
 
@@ -67,7 +68,9 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const int half = lane >> 5, col = lane & 31;
   const int w = blockIdx.x;
   const uint64_t t_start = wall_clock64();
-  const int beg = a.cu_off[w], end = a.cu_off[w + 1];
+  // A device plan that is not a copy of the host plan runs no item.
+  const bool plan_ok = *a.plan_sum_dev == a.plan_sum;
+  const int beg = plan_ok ? a.cu_off[w] : 0, end = plan_ok ? a.cu_off[w + 1] : 0;
   const float c = a.scale_log2;
   const uint32_t kv_base = lds_addr(kv_lds);
   const int dlo = direct_lane_off<RS>(lane);       // K operand reads
@@ -208,7 +211,7 @@ void attn_bwd_dq_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  if (a.records != nullptr && tid == 0) write_record(a, w, end - beg, t_start);
+  if (a.records != nullptr && tid == 0) write_record(a, w, end - beg, t_start, plan_ok);
 }
 
 }  // namespace
@@ -239,6 +242,8 @@ libra_status launch_dq(const libra_plan_info &h, BwdArgs a, const void *plan_dev
   const char *pd = static_cast<const char *>(plan_dev);
   a.items = reinterpret_cast<const libra_item *>(pd + h.off_dq_items);
   a.cu_off = reinterpret_cast<const int32_t *>(pd + h.off_dq_cu_off);
+  a.plan_sum_dev = reinterpret_cast<const uint64_t *>(pd + offsetof(libra_plan_info, checksum));
+  a.plan_sum = h.checksum;
   a.dq = static_cast<uint16_t *>(dq);
   a.records = records;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstddef>
 #include <cstring>
 #include <type_traits>
 
@@ -42,6 +43,8 @@ constexpr int kStages = 4;       // LDS buffers: copies run kStages - 1 blocks a
 struct FwdArgs {
   const libra_item *items;
   const int32_t *cu_off;
+  const uint64_t *plan_sum_dev;   // checksum field of the device copy of the plan
+  uint64_t plan_sum;              // checksum of the host plan the launch was made from
   const uint16_t *q, *k, *v;
   const int32_t *cu;
   uint16_t *o;
@@ -66,6 +69,13 @@ static_assert(kFwdWaves % 4 == 0, "whole waves per SIMD");
 // rescaled rarely; in between, P = 2^(s c - m) stays below 2^kRescaleSlack.
 constexpr float kRescaleSlack = 8.0f;
 
+#ifdef LIBRA_COUNT_PAIRS
+// Debug build only: the unmasked (query, key, head) triples the forward
+// computed, summed over every launch since the last reset (eq. 8 counts
+// exactly these).
+__device__ unsigned long long g_unmasked_pairs;
+#endif
+
 template <int D, int QT, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void attn_fwd_kernel(FwdArgs a) {
@@ -89,7 +99,9 @@ void attn_fwd_kernel(FwdArgs a) {
   const int half = lane >> 5, col = lane & 31;
   const int w = blockIdx.x;
   const uint64_t t_start = wall_clock64();
-  const int beg = a.cu_off[w], end = a.cu_off[w + 1];
+  // A device plan that is not a copy of the host plan runs no item.
+  const bool plan_ok = *a.plan_sum_dev == a.plan_sum;
+  const int beg = plan_ok ? a.cu_off[w] : 0, end = plan_ok ? a.cu_off[w + 1] : 0;
   const float sl2 = a.scale_log2;
   const uint32_t kv_base = lds_addr(kv_lds);
   const float NEG_INF = -__builtin_inff();
@@ -102,6 +114,9 @@ void attn_fwd_kernel(FwdArgs a) {
   kvcopy.init(wave, lane, kv_stride);
   // this wave's copies per block
   const int copies = KVCopy::count(wave);
+#ifdef LIBRA_COUNT_PAIRS
+  uint32_t counted = 0;   // unmasked (query, key) slots this lane computed
+#endif
 
   for (int it = beg; it < end; ++it) {
     const libra_item item = a.items[it];
@@ -224,6 +239,21 @@ void attn_fwd_kernel(FwdArgs a) {
               }
           }
         }
+#ifdef LIBRA_COUNT_PAIRS
+        // Unmasked (query, key) slots of this lane's 32 keys of the block.
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          if (!qok[qt]) continue;
+          if (!masked) {
+            counted += 32;
+          } else {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) counted += sacc[kt][qt][r] != NEG_INF ? 1u : 0u;
+          }
+        }
+#endif
         // Block maximum per query; raise the running maximum only when it is
         // exceeded by more than the slack (then rescale O and l).
         float mxs[QT];
@@ -312,13 +342,21 @@ void attn_fwd_kernel(FwdArgs a) {
     }
   }
 
+#ifdef LIBRA_COUNT_PAIRS
+  {
+    uint64_t wave_sum = counted;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) wave_sum += __shfl_xor(wave_sum, off);
+    if (lane == 0) atomicAdd(&g_unmasked_pairs, (unsigned long long)wave_sum);
+  }
+#endif
   __syncthreads();
   if (a.records != nullptr && tid == 0) {
     libra_cu_record rec;
     rec.hw_id = hw_id_reg();
     rec.xcc_id = xcc_id_reg();
     rec.n_items = (uint32_t)(end - beg);
-    rec.reserved = 0;
+    rec.flags = plan_ok ? 0u : LIBRA_RECORD_PLAN_MISMATCH;
     rec.t_start = t_start;
     rec.t_end = wall_clock64();
     a.records[w] = rec;
@@ -347,7 +385,7 @@ using namespace libra;
 namespace {
 
 libra_status check_header(const void *plan, libra_plan_info *h) {
-  if (plan_header(plan, h) != LIBRA_OK) return LIBRA_EINVAL;
+  if (plan_validate(plan, h) != LIBRA_OK) return LIBRA_EINVAL;
   if (h->params.head_dim != 64 && h->params.head_dim != 128) return LIBRA_EUNSUPPORTED;
   return LIBRA_OK;
 }
@@ -373,6 +411,8 @@ libra_status launch_fwd(const libra_plan_info &h, const void *plan_dev, const vo
   const char *pd = static_cast<const char *>(plan_dev);
   a.items = reinterpret_cast<const libra_item *>(pd + h.off_items);
   a.cu_off = reinterpret_cast<const int32_t *>(pd + h.off_cu_off);
+  a.plan_sum_dev = reinterpret_cast<const uint64_t *>(pd + offsetof(libra_plan_info, checksum));
+  a.plan_sum = h.checksum;
   a.q = static_cast<const uint16_t *>(q);
   a.k = static_cast<const uint16_t *>(k);
   a.v = static_cast<const uint16_t *>(v);
@@ -420,3 +460,19 @@ extern "C" libra_status libra_device_clock_khz(int32_t *khz) {
   *khz = v;
   return LIBRA_OK;
 }
+
+#ifdef LIBRA_COUNT_PAIRS
+extern "C" libra_status libra_debug_unmasked_pairs(uint64_t *count) {
+  if (!count) return LIBRA_EINVAL;
+  unsigned long long v = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_unmasked_pairs), sizeof v) != hipSuccess) return LIBRA_EHIP;
+  *count = v;
+  return LIBRA_OK;
+}
+
+extern "C" libra_status libra_debug_reset_unmasked_pairs(void) {
+  const unsigned long long zero = 0;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(g_unmasked_pairs), &zero, sizeof zero) != hipSuccess) return LIBRA_EHIP;
+  return LIBRA_OK;
+}
+#endif

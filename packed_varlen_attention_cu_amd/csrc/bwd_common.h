@@ -22,6 +22,8 @@ inline int64_t round_up64(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 struct BwdArgs {
   const libra_item *items;     // dK/dV: key-major queue; dQ: forward queue
   const int32_t *cu_off;
+  const uint64_t *plan_sum_dev;   // checksum field of the device copy of the plan
+  uint64_t plan_sum;              // checksum of the host plan the launch was made from
   const uint16_t *q, *k, *v, *dout;
   const float *lse, *dvec, *lse2;  // [h_q][L]: LSE, D = rowsum(dO * O), LSE * log2(e)
   const int32_t *cu;
@@ -31,12 +33,12 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
-__device__ __forceinline__ void write_record(const BwdArgs &a, int w, int n, uint64_t t0) {
+__device__ __forceinline__ void write_record(const BwdArgs &a, int w, int n, uint64_t t0, bool plan_ok) {
   libra_cu_record rec;
   rec.hw_id = hw_id_reg();
   rec.xcc_id = xcc_id_reg();
   rec.n_items = (uint32_t)n;
-  rec.reserved = 0;
+  rec.flags = plan_ok ? 0u : LIBRA_RECORD_PLAN_MISMATCH;
   rec.t_start = t0;
   rec.t_end = wall_clock64();
   a.records[w] = rec;

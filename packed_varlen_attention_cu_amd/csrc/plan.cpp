@@ -5,21 +5,26 @@
 // query heads into shards of W heads (eq. 6); a tile's KV groups are the
 // samples its block intersects (eq. 7); its cost is the exact number of
 // unmasked causal pairs, sum over those samples of sum_{q=a}^{e-1} (q + 1),
-// times W (eq. 8).  Algorithm 2 (section 5.4) places work heaviest first on
-// the least-loaded worker under a soft target C = (1 + tau) * mean.
+// times W (eq. 8).
 //
-// On one GPU the workers are the CUs, every tensor is already in HBM (the
-// communication term of eq. 9 is zero), and a tile is cut into work items of
-// 256 query columns (positions x heads) that one workgroup executes (see
-// libra.h).  With a zero communication term both branches of Algorithm 2
-// pick the worker of least (load, id) -- whenever any worker fits under C the
-// least loaded one does -- so the placement is a binary heap keyed by
-// (load, worker id).
+// On one GPU the workers are the CUs.  A tile is cut into work items that one
+// workgroup executes: forward items of at most 384 query columns (positions
+// x heads), dQ items of at most 256, and key-major dK/dV items of 192 keys
+// (see libra.h).  Items are costed by the work their kernel executes (or, on
+// request, by eq. 8 pairs), grouped into zigzag pairs, and placed by
+// Algorithm 2 (section 5.4): heaviest first, onto a worker within the soft
+// target (1 + tau) x the even share that adds the least communication (eq.
+// 9), else the least loaded one.  With no communication term the rule
+// reduces to least-loaded placement, which runs as a binary heap keyed by
+// (load, worker id); the L2 term of LIBRA_ASSIGN_PLACER_L2 (the XCD's L2
+// standing in for the worker's memory) runs over one heap per XCD.
 //
-// Everything here is integer arithmetic and bitwise deterministic.
+// Everything here is integer arithmetic (the soft-target test excepted, done
+// in double precision in a fixed order) and bitwise deterministic.
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <exception>
 #include <functional>
 #include <queue>
 #include <thread>
@@ -70,6 +75,35 @@ int64_t sample_end(const int32_t *cu, int n, int64_t pos, int *j) {
 
 int head_group(int n) { return n % 4 == 0 ? 4 : (n % 2 == 0 ? 2 : 1); }
 
+// Index of the sample holding position pos (pos < L): the last j with cu[j] <= pos.
+int sample_of(const int32_t *cu, int n, int64_t pos) {
+  return (int)(std::upper_bound(cu, cu + n + 1, (int32_t)pos) - cu) - 1;
+}
+
+// 64-key blocks one wave of a forward or dQ workgroup computes for query rows
+// [a, e): for a row r of sample j, the blocks start_j / 64 .. r / 64; the
+// union over the rows, taken sample by sample (the ranges ascend).
+int64_t wave_blocks(const int32_t *cu, int n, int64_t a, int64_t e) {
+  int64_t count = 0, done = -1;   // blocks up to `done` are counted
+  for (int j = sample_of(cu, n, a); j < n && cu[j] < e; ++j) {
+    if (cu[j + 1] <= std::max<int64_t>(a, cu[j])) continue;   // empty, or before a
+    const int64_t lo = std::max<int64_t>(cu[j] / libra::kKeyBlock, done + 1);
+    const int64_t hi = (std::min<int64_t>(e, cu[j + 1]) - 1) / libra::kKeyBlock;
+    if (hi >= lo) count += hi - lo + 1;
+    done = std::max(done, hi);
+  }
+  return count;
+}
+
+// Query-key slots a forward or dQ workgroup computes for an item of rows
+// [row0, row0 + nrows) and nh heads: each row range of 32 is held by nh waves.
+int64_t executed_slots(const int32_t *cu, int n, int64_t row0, int64_t nrows, int nh) {
+  int64_t blocks = 0;
+  for (int64_t a = row0; a < row0 + nrows; a += libra::kQueryTile)
+    blocks += wave_blocks(cu, n, a, std::min(row0 + nrows, a + libra::kQueryTile));
+  return nh * blocks * libra::kQueryTile * libra::kKeyBlock;
+}
+
 libra_status validate(const int32_t *cu, const libra_plan_params *p) {
   if (!cu || !p) return LIBRA_EINVAL;
   if (p->total_tokens < 0 || p->num_samples < 0) return LIBRA_EINVAL;
@@ -77,7 +111,11 @@ libra_status validate(const int32_t *cu, const libra_plan_params *p) {
   if (p->tile_tokens <= 0 || p->tile_heads <= 0 || p->h_q % p->tile_heads) return LIBRA_EINVAL;
   if (p->num_cus < 0 || p->num_cus > kMaxCus) return LIBRA_EINVAL;
   if (!(p->tau >= 0.0f) || !std::isfinite(p->tau)) return LIBRA_EINVAL;
-  if (p->assign != LIBRA_ASSIGN_PLACER && p->assign != LIBRA_ASSIGN_ROUND_ROBIN) return LIBRA_EINVAL;
+  if (p->assign != LIBRA_ASSIGN_PLACER && p->assign != LIBRA_ASSIGN_ROUND_ROBIN &&
+      p->assign != LIBRA_ASSIGN_PLACER_L2)
+    return LIBRA_EINVAL;
+  if (p->cost != LIBRA_COST_EXECUTED && p->cost != LIBRA_COST_PAIRS) return LIBRA_EINVAL;
+  if (p->reserved != 0) return LIBRA_EINVAL;
   if (p->item_overhead < 0) return LIBRA_EINVAL;
   if (cu[0] != 0) return LIBRA_EINVAL;
   for (int j = 0; j < p->num_samples; ++j)
@@ -93,15 +131,29 @@ struct Queue {
   int64_t load_max = 0, load_sum = 0;
 };
 
-// Algorithm 2 with a zero communication term (or round-robin), emitted as CSR.
-// Units are taken heaviest first (ties: lower enumeration index) and each goes
-// to the worker of least (load, worker id), kept in a binary min-heap.
+// A worker's load and id; heaps of them are ordered by (load, worker id).
 struct Load {
   int64_t load;
   int32_t worker;
 };
 inline bool lighter(const Load &x, const Load &y) {
   return x.load != y.load ? x.load < y.load : x.worker < y.worker;
+}
+
+// Give the root of a min-heap the load `top` and restore the heap order.
+void sift_root(std::vector<Load> &h, Load top) {
+  size_t i = 0;
+  for (;;) {
+    const size_t l = 2 * i + 1, r = l + 1;
+    size_t m = i;
+    const Load *best = &top;
+    if (l < h.size() && lighter(h[l], *best)) { m = l; best = &h[l]; }
+    if (r < h.size() && lighter(h[r], *best)) { m = r; best = &h[r]; }
+    if (m == i) break;
+    h[i] = h[m];
+    i = m;
+  }
+  h[i] = top;
 }
 
 // Worker speeds of a plan: the eight class speeds, 0 read as 1000.
@@ -115,119 +167,131 @@ struct Speeds {
   }
 };
 
-// Units heaviest first (ties: lower index) onto workers of different speeds:
-// each goes to the worker that would finish it first, (load + cost) / speed,
-// ties to the lower worker id.  Within a speed class the candidate is the
-// class's least loaded worker, so one min-heap per class and a scan of the
-// eight class tops suffice.  (load + cost) * speed < 2^43 * 2^16 fits int64.
-void place_weighted(const std::vector<int64_t> &costs_sorted, const std::vector<int32_t> &idx_sorted,
-                    int workers, const Speeds &sp, std::vector<int32_t> &worker, std::vector<int64_t> &load) {
+// The KV groups of every placement unit and their volumes, for the L2 term:
+// unit u holds groups ids[off[u] .. off[u + 1]), group g has volume vol[g].
+struct UnitGroups {
+  std::vector<int64_t> off;
+  std::vector<int32_t> ids;
+  std::vector<int64_t> vol;
+  int32_t n_groups = 0;
+};
+
+// Algorithm 2 over workers in eight speed classes (worker r in class r mod 8,
+// the XCD that runs workgroup r), with the L2 communication term when
+// `groups` is given and none otherwise.  Within a class every worker has the
+// same speed and the same communication term, so the class's candidate is
+// its least loaded worker (a heap top): a unit goes to the best of the eight
+// tops under the key (within target, term, finish, id) / (beyond target,
+// finish, term, id), finish = (load + cost) / speed compared exactly by
+// cross-multiplication.  (load + cost) * speed < 2^47 * 2^11 fits int64.
+void place_classes(const std::vector<int64_t> &costs_sorted, const std::vector<int32_t> &idx_sorted,
+                   int workers, const Speeds &sp, float tau, const UnitGroups *groups,
+                   std::vector<int32_t> &worker, std::vector<int64_t> &load) {
   std::vector<Load> heap[8];
   for (int32_t r = 0; r < workers; ++r) heap[r % 8].push_back({0, r});   // ascending ids: valid heaps
+  double speed_sum = 0, cost_sum = 0;
+  for (int32_t r = 0; r < workers; ++r) speed_sum += (double)sp.s[r % 8];
+  int64_t total = 0;
+  for (int64_t c : costs_sorted) total += c;
+  cost_sum = (double)total;
+  const double budget = (1.0 + (double)tau) * cost_sum;
+  std::vector<uint8_t> held;                        // held[x * n_groups + g]: group g committed to XCD x
+  if (groups) held.assign((size_t)8 * groups->n_groups, 0);
   for (size_t k = 0; k < costs_sorted.size(); ++k) {
     const int64_t c = costs_sorted[k];
+    const int32_t u = idx_sorted[k];
     int best = -1;
+    bool best_fits = false;
+    int64_t best_term = 0;
     for (int x = 0; x < 8; ++x) {
       if (heap[x].empty()) continue;
-      if (best < 0) {
-        best = x;
-        continue;
+      const Load &t = heap[x][0];
+      const bool fits = (double)(t.load + c) * speed_sum <= budget * (double)sp.s[x];
+      int64_t term = 0;
+      if (groups) {
+        for (int64_t i = groups->off[u]; i < groups->off[u + 1]; ++i) {
+          const int32_t g = groups->ids[i];
+          if (!held[(size_t)x * groups->n_groups + g]) term += groups->vol[g];
+        }
       }
-      const Load &t = heap[x][0], &b = heap[best][0];
-      const int64_t lhs = (t.load + c) * sp.s[best], rhs = (b.load + c) * sp.s[x];
-      if (lhs < rhs || (lhs == rhs && t.worker < b.worker)) best = x;
+      bool better;
+      if (best < 0) {
+        better = true;
+      } else {
+        const Load &b = heap[best][0];
+        const int64_t lhs = (t.load + c) * sp.s[best], rhs = (b.load + c) * sp.s[x];   // finish x vs best
+        const int finish_cmp = lhs < rhs ? -1 : (lhs > rhs ? 1 : 0);
+        if (fits != best_fits) better = fits;
+        else if (fits && term != best_term) better = term < best_term;
+        else if (finish_cmp != 0) better = finish_cmp < 0;
+        else if (!fits && term != best_term) better = term < best_term;
+        else better = t.worker < b.worker;
+      }
+      if (better) {
+        best = x;
+        best_fits = fits;
+        best_term = term;
+      }
     }
     std::vector<Load> &h = heap[best];
     Load top = h[0];
-    worker[idx_sorted[k]] = top.worker;
+    worker[u] = top.worker;
     top.load += c;
     load[top.worker] = top.load;
-    size_t i = 0;                                             // sift the grown root down
-    for (;;) {
-      const size_t l = 2 * i + 1, r = l + 1;
-      size_t m = i;
-      const Load *bst = &top;
-      if (l < h.size() && lighter(h[l], *bst)) { m = l; bst = &h[l]; }
-      if (r < h.size() && lighter(h[r], *bst)) { m = r; bst = &h[r]; }
-      if (m == i) break;
-      h[i] = h[m];
-      i = m;
-    }
-    h[i] = top;
+    sift_root(h, top);
+    if (groups)
+      for (int64_t i = groups->off[u]; i < groups->off[u + 1]; ++i)
+        held[(size_t)best * groups->n_groups + groups->ids[i]] = 1;
   }
 }
 
-Queue place(const std::vector<libra_item> &units, int workers, int mode, const Speeds &sp) {
+// Place `units` (Algorithm 2, or round-robin) and emit per-worker queues as
+// CSR.  Units are taken heaviest first, ties to the lower index.
+Queue place(const std::vector<libra_item> &units, int workers, int mode, const Speeds &sp, float tau,
+            const UnitGroups *groups) {
   Queue q;
   const size_t n = units.size();
   std::vector<int32_t> worker(n);
   std::vector<int32_t> order(n);
   std::vector<int64_t> load(workers, 0);
-  if (mode == LIBRA_ASSIGN_PLACER && !sp.uniform) {
-    std::vector<int32_t> idx(n);
-    for (size_t i = 0; i < n; ++i) idx[i] = (int32_t)i;
-    std::sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
-      return units[a].cost != units[b].cost ? units[a].cost > units[b].cost : a < b;
-    });
-    std::vector<int64_t> cs(n);
-    for (size_t k = 0; k < n; ++k) {
-      cs[k] = units[idx[k]].cost;
-      order[k] = idx[k];
-    }
-    place_weighted(cs, idx, workers, sp, worker, load);
-  } else if (mode == LIBRA_ASSIGN_PLACER) {
-    struct Key {
-      int64_t cost;
-      int32_t idx;
-    };
-    std::vector<Key> keys(n);
-    int64_t cmax = 0;
-    for (size_t i = 0; i < n; ++i) {
-      keys[i] = {units[i].cost, (int32_t)i};
-      cmax = std::max(cmax, units[i].cost);
-    }
-    if (cmax < (int64_t(1) << 43) && n < (size_t(1) << 20)) {
-      // (cost descending, index ascending) as one ascending 64-bit key
-      std::vector<uint64_t> packed(n);
-      for (size_t i = 0; i < n; ++i)
-        packed[i] = (uint64_t)((int64_t(1) << 43) - 1 - keys[i].cost) << 20 | (uint64_t)i;
-      std::sort(packed.begin(), packed.end());
-      for (size_t k = 0; k < n; ++k) {
-        const int32_t i = (int32_t)(packed[k] & ((1u << 20) - 1));
-        keys[k] = {units[i].cost, i};
-      }
-    } else {
-      std::sort(keys.begin(), keys.end(), [](const Key &x, const Key &y) {
-        return x.cost != y.cost ? x.cost > y.cost : x.idx < y.idx;
-      });
-    }
-    std::vector<Load> heap(workers);
-    for (int32_t r = 0; r < workers; ++r) heap[r] = {0, r};   // ordered, hence a valid heap
-    for (size_t k = 0; k < n; ++k) {
-      const int32_t t = keys[k].idx;
-      order[k] = t;
-      Load top = heap[0];
-      worker[t] = top.worker;
-      top.load += keys[k].cost;
-      load[top.worker] = top.load;
-      size_t i = 0;                                            // sift the grown root down
-      for (;;) {
-        const size_t l = 2 * i + 1, r = l + 1;
-        size_t m = i;
-        const Load *best = &top;
-        if (l < heap.size() && lighter(heap[l], *best)) { m = l; best = &heap[l]; }
-        if (r < heap.size() && lighter(heap[r], *best)) { m = r; best = &heap[r]; }
-        if (m == i) break;
-        heap[i] = heap[m];
-        i = m;
-      }
-      heap[i] = top;
-    }
-  } else {
+  if (mode == LIBRA_ASSIGN_ROUND_ROBIN) {
     for (size_t t = 0; t < n; ++t) {
       order[t] = (int32_t)t;
       worker[t] = (int32_t)(t % workers);
       load[worker[t]] += units[t].cost;
+    }
+  } else {
+    int64_t cmax = 0;
+    for (size_t i = 0; i < n; ++i) cmax = std::max(cmax, units[i].cost);
+    if (cmax < (int64_t(1) << 43) && n < (size_t(1) << 20)) {
+      // (cost descending, index ascending) as one ascending 64-bit key
+      std::vector<uint64_t> packed(n);
+      for (size_t i = 0; i < n; ++i)
+        packed[i] = (uint64_t)((int64_t(1) << 43) - 1 - units[i].cost) << 20 | (uint64_t)i;
+      std::sort(packed.begin(), packed.end());
+      for (size_t k = 0; k < n; ++k) order[k] = (int32_t)(packed[k] & ((1u << 20) - 1));
+    } else {
+      for (size_t i = 0; i < n; ++i) order[i] = (int32_t)i;
+      std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+        return units[a].cost != units[b].cost ? units[a].cost > units[b].cost : a < b;
+      });
+    }
+    std::vector<int64_t> cs(n);
+    for (size_t k = 0; k < n; ++k) cs[k] = units[order[k]].cost;
+    const UnitGroups *g = mode == LIBRA_ASSIGN_PLACER_L2 ? groups : nullptr;
+    if (g || !sp.uniform) {
+      place_classes(cs, order, workers, sp, tau, g, worker, load);
+    } else {
+      // No communication term, equal speeds: the least loaded worker (ties: lowest id), one heap.
+      std::vector<Load> heap(workers);
+      for (int32_t r = 0; r < workers; ++r) heap[r] = {0, r};   // ordered, hence a valid heap
+      for (size_t k = 0; k < n; ++k) {
+        Load top = heap[0];
+        worker[order[k]] = top.worker;
+        top.load += cs[k];
+        load[top.worker] = top.load;
+        sift_root(heap, top);
+      }
     }
   }
   q.cu_off.assign(workers + 1, 0);
@@ -257,6 +321,23 @@ double finish_max_over_mean(const Queue &q, int workers, const Speeds &sp) {
   return sum > 0 ? mx * workers / sum : 1.0;
 }
 
+// Where the KV groups of the L2 term come from: the packing and the KV head count.
+struct GroupSource {
+  const int32_t *cu;
+  int n, h_kv;
+};
+
+// Append the KV groups (sample j, KV head) of item `it` -- every non-empty
+// sample its rows meet -- to `ids`, skipping those already listed from `from`.
+void append_groups(const GroupSource &gs, const libra_item &it, size_t from, std::vector<int32_t> &ids) {
+  const int64_t lo = it.row0, hi = (int64_t)it.row0 + it.nrows;
+  for (int j = sample_of(gs.cu, gs.n, lo); j < gs.n && gs.cu[j] < hi; ++j) {
+    if (gs.cu[j + 1] <= std::max<int64_t>(lo, gs.cu[j])) continue;
+    const int32_t g = j * gs.h_kv + it.kv_head;
+    if (std::find(ids.begin() + from, ids.end(), g) == ids.end()) ids.push_back(g);
+  }
+}
+
 // Zigzag units.  Items sharing a group key (for the dK/dV items: the sample
 // of the last key and the KV head; for forward and dQ items: the sample of
 // the first row, the KV head and the first head) are taken in row order
@@ -268,12 +349,13 @@ double finish_max_over_mean(const Queue &q, int workers, const Speeds &sp) {
 // that start together read the same K / V (or Q / dO) block at every step:
 // the CUs sharing an L2 share the streamed rows.  Equal-cost pairs are
 // coarser than single items: when one group holds most of the work they leave
-// too few small units to level the workers, so the pairs are kept only if
-// their largest finish time (load / speed) is within 0.5 % of the mean one;
-// otherwise the single items are placed, all in the default order.
+// too few small units to level the workers, so the pairs are kept only if,
+// placed by least finish time, their largest finish time is within 0.5 % of
+// the mean one; otherwise the single items are placed, all in the default
+// order.  The units are then placed in the plan's mode.
 // Items arrive in id order (id = index) and rows ascend within a group.
 Queue place_zigzag(const std::vector<libra_item> &items, const std::vector<int64_t> &group, int workers,
-                   int mode, const Speeds &sp) {
+                   int mode, const Speeds &sp, float tau, const GroupSource &gs) {
   const size_t n = items.size();
   std::vector<int32_t> second(n, -2);   // -2: not a unit's first item, -1: alone
   {
@@ -296,8 +378,29 @@ Queue place_zigzag(const std::vector<libra_item> &items, const std::vector<int64
       if (second[i] >= 0) u.cost += items[second[i]].cost;
       units.push_back(u);
     }
-  Queue uq = place(units, workers, mode, sp);
-  if (finish_max_over_mean(uq, workers, sp) > 1.005) return place(items, workers, mode, sp);
+  const int trial_mode = mode == LIBRA_ASSIGN_ROUND_ROBIN ? mode : LIBRA_ASSIGN_PLACER;
+  Queue uq = place(units, workers, trial_mode, sp, tau, nullptr);
+  if (finish_max_over_mean(uq, workers, sp) > 1.005) {   // pairs too coarse: single items
+    units = items;
+    std::fill(second.begin(), second.end(), -1);
+    if (mode == trial_mode) uq = place(units, workers, mode, sp, tau, nullptr);
+  }
+  if (mode != trial_mode) {
+    UnitGroups ug;
+    ug.n_groups = gs.n * gs.h_kv;
+    ug.vol.resize(ug.n_groups);
+    for (int j = 0; j < gs.n; ++j)
+      for (int kv = 0; kv < gs.h_kv; ++kv) ug.vol[(size_t)j * gs.h_kv + kv] = gs.cu[j + 1] - gs.cu[j];
+    ug.off.reserve(units.size() + 1);
+    ug.off.push_back(0);
+    for (const libra_item &u : units) {
+      const size_t from = ug.ids.size();
+      append_groups(gs, items[u.id], from, ug.ids);
+      if (second[u.id] >= 0) append_groups(gs, items[second[u.id]], from, ug.ids);
+      ug.off.push_back((int64_t)ug.ids.size());
+    }
+    uq = place(units, workers, mode, sp, tau, &ug);
+  }
   Queue q;
   q.load_max = uq.load_max;
   q.load_sum = uq.load_sum;
@@ -394,10 +497,39 @@ libra_status plan_header(const void *plan, libra_plan_info *out) {
   return LIBRA_OK;
 }
 
+libra_status plan_validate(const void *plan, libra_plan_info *out) {
+  libra_plan_info h;
+  if (plan_header(plan, &h) != LIBRA_OK) return LIBRA_EINVAL;
+  if (h.bytes < sizeof h || h.bytes % 8 || h.num_cus <= 0 || h.num_cus > kMaxCus) return LIBRA_EINVAL;
+  if (h.n_tiles < 0 || h.n_items < 0 || h.n_dq_items < 0 || h.n_kv_items < 0) return LIBRA_EINVAL;
+  const uint64_t sections[][2] = {
+      {h.off_tiles, (uint64_t)h.n_tiles * sizeof(libra_tile)},
+      {h.off_items, (uint64_t)h.n_items * sizeof(libra_item)},
+      {h.off_cu_off, (uint64_t)(h.num_cus + 1) * sizeof(int32_t)},
+      {h.off_dq_items, (uint64_t)h.n_dq_items * sizeof(libra_item)},
+      {h.off_dq_cu_off, (uint64_t)(h.num_cus + 1) * sizeof(int32_t)},
+      {h.off_kv_items, (uint64_t)h.n_kv_items * sizeof(libra_item)},
+      {h.off_kv_cu_off, (uint64_t)(h.num_cus + 1) * sizeof(int32_t)}};
+  for (const auto &sec : sections)
+    if (sec[0] % 64 || sec[0] < sizeof h || sec[0] > h.bytes || sec[1] > h.bytes - sec[0]) return LIBRA_EINVAL;
+  if (plan_checksum(plan, h.bytes) != h.checksum) return LIBRA_EINVAL;
+  *out = h;
+  return LIBRA_OK;
+}
+
 }  // namespace libra
 
-extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *pp, void *buf,
-                                   size_t *bytes) {
+namespace {
+
+// Joins its thread, if one was started, when it goes out of scope.
+struct Joiner {
+  std::thread t;
+  ~Joiner() {
+    if (t.joinable()) t.join();
+  }
+};
+
+libra_status plan_impl(const int32_t *cu, const libra_plan_params *pp, void *buf, size_t *bytes) {
   if (!bytes) return LIBRA_EINVAL;
   libra_status st = validate(cu, pp);
   if (st != LIBRA_OK) return st;
@@ -440,9 +572,12 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
   tiles.reserve(nblocks * S);
   items.reserve(n_items);
   dq_items.reserve(n_dq);
-  // Per-head pairs of a block's row chunks of one length, computed once per
-  // block and chunk length.
-  std::vector<std::pair<int, std::vector<int64_t>>> chunk_pairs;
+  // Per-head pairs and per-head executed 64-key wave blocks of a block's row
+  // chunks of one length, computed once per block and chunk length.
+  struct ChunkWork {
+    int64_t pairs, blocks;
+  };
+  std::vector<std::pair<int, std::vector<ChunkWork>>> chunk_pairs;
   int jb = 0;
   // Cut tile t (rows [lo, hi) of block b, whose first sample is jb) into
   // items of at most `columns` query columns, appended to `out`; returns how
@@ -454,15 +589,18 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
       const int a = std::max(h_lo, kv * g), e = std::min(h_hi, (kv + 1) * g);
       const int nh = head_group(e - a);
       const int rows = columns / nh;
-      std::vector<int64_t> *cp = nullptr;
+      std::vector<ChunkWork> *cp = nullptr;
       for (auto &c : chunk_pairs)
         if (c.first == rows) cp = &c.second;
       if (!cp) {
-        chunk_pairs.emplace_back(rows, std::vector<int64_t>());
+        chunk_pairs.emplace_back(rows, std::vector<ChunkWork>());
         cp = &chunk_pairs.back().second;
         int ji = jb;
-        for (int64_t r0 = lo; r0 < hi; r0 += rows)
-          cp->push_back(query_pairs(cu, n, r0, std::min<int64_t>(hi, r0 + rows), &ji));
+        for (int64_t r0 = lo; r0 < hi; r0 += rows) {
+          const int64_t r1 = std::min<int64_t>(hi, r0 + rows);
+          const int64_t pairs = query_pairs(cu, n, r0, r1, &ji);
+          cp->push_back({pairs, p.cost == LIBRA_COST_PAIRS ? 0 : executed_slots(cu, n, r0, r1 - r0, 1)});
+        }
       }
       for (int gi = 0; gi < (e - a) / nh; ++gi) {
         size_t ci = 0;
@@ -476,8 +614,8 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
           it.nheads = nh;
           it.tile_id = t.tile_id;
           it.id = (int32_t)out.size();
-          it.pairs = nh * (*cp)[ci];
-          it.cost = it.pairs + p.item_overhead;
+          it.pairs = nh * (*cp)[ci].pairs;
+          it.cost = (p.cost == LIBRA_COST_PAIRS ? it.pairs : nh * (*cp)[ci].blocks) + p.item_overhead;
           out.push_back(it);
           ++made;
         }
@@ -560,11 +698,32 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
     return key;
   };
   const Speeds sp(p.worker_speed);
-  std::thread t_dq([&] { dq = place_zigzag(dq_items, group_keys(dq_items, false), workers, p.assign, sp); });
-  std::thread t_kv([&] { kq = place_zigzag(kv_items, group_keys(kv_items, true), workers, p.assign, sp); });
-  fq = place_zigzag(items, group_keys(items, false), workers, p.assign, sp);
-  t_dq.join();
-  t_kv.join();
+  const GroupSource gs{cu, n, p.h_kv};
+  {
+    // An exception on a placement thread is carried to this one; the joiners
+    // join every started thread on any exit from this block.
+    std::exception_ptr err[2];
+    Joiner t_dq, t_kv;
+    t_dq.t = std::thread([&] {
+      try {
+        dq = place_zigzag(dq_items, group_keys(dq_items, false), workers, p.assign, sp, p.tau, gs);
+      } catch (...) {
+        err[0] = std::current_exception();
+      }
+    });
+    t_kv.t = std::thread([&] {
+      try {
+        kq = place_zigzag(kv_items, group_keys(kv_items, true), workers, p.assign, sp, p.tau, gs);
+      } catch (...) {
+        err[1] = std::current_exception();
+      }
+    });
+    fq = place_zigzag(items, group_keys(items, false), workers, p.assign, sp, p.tau, gs);
+    t_dq.t.join();
+    t_kv.t.join();
+    for (const std::exception_ptr &e : err)
+      if (e) std::rethrow_exception(e);
+  }
 
   libra_plan_info hdr{};
   hdr.magic = LIBRA_PLAN_MAGIC;
@@ -605,22 +764,23 @@ extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *p
   return LIBRA_OK;
 }
 
+}  // namespace
+
+extern "C" libra_status libra_plan(const int32_t *cu, const libra_plan_params *params, void *buf,
+                                   size_t *bytes) {
+  try {
+    return plan_impl(cu, params, buf, bytes);
+  } catch (...) {   // std::bad_alloc, std::system_error from std::thread
+    return LIBRA_EHOST;
+  }
+}
+
 extern "C" libra_status libra_plan_check(const void *plan, size_t bytes, libra_plan_info *info) {
   libra_plan_info hdr;
   if (!plan || bytes < sizeof hdr) return LIBRA_EINVAL;
-  if (libra::plan_header(plan, &hdr) != LIBRA_OK) return LIBRA_EINVAL;
+  std::memcpy(&hdr, plan, sizeof hdr);
   if (hdr.bytes != bytes) return LIBRA_EINVAL;
-  const uint64_t ends[] = {
-      hdr.off_tiles + (uint64_t)hdr.n_tiles * sizeof(libra_tile),
-      hdr.off_items + (uint64_t)hdr.n_items * sizeof(libra_item),
-      hdr.off_cu_off + (uint64_t)(hdr.num_cus + 1) * sizeof(int32_t),
-      hdr.off_dq_items + (uint64_t)hdr.n_dq_items * sizeof(libra_item),
-      hdr.off_dq_cu_off + (uint64_t)(hdr.num_cus + 1) * sizeof(int32_t),
-      hdr.off_kv_items + (uint64_t)hdr.n_kv_items * sizeof(libra_item),
-      hdr.off_kv_cu_off + (uint64_t)(hdr.num_cus + 1) * sizeof(int32_t)};
-  for (uint64_t e : ends)
-    if (e > bytes) return LIBRA_EINVAL;
-  if (libra::plan_checksum(plan, bytes) != hdr.checksum) return LIBRA_EINVAL;
+  if (libra::plan_validate(plan, &hdr) != LIBRA_OK) return LIBRA_EINVAL;
   if (info) *info = hdr;
   return LIBRA_OK;
 }

@@ -1,19 +1,20 @@
 // Variance-reduced sequence placement (host).
 //
-// Libra technical review, section 4.2, Algorithm 1, and Libra paper,
-// section 4.2: the packed sequences of one optimizer-step window are placed
-// heaviest first (workload F = sum of squared sample lengths, eq. 1), each on
-// the least-loaded pool that still holds fewer than P sequences; full pools
-// leave the candidate heap for good, which enforces the exact cardinality.
-// Ties: equal workloads by sequence index, equal loads by pool index.
+// Libra technical review, section 4.2 (Algorithm 1), and Libra paper,
+// section 4.2.  The rule: the packed sequences of one optimizer-step window
+// are dealt out heaviest first (workload F = sum of squared sample lengths,
+// eq. 1; equal workloads by sequence index), each to the pool with the least
+// summed workload among the pools that still hold fewer than P sequences
+// (equal loads by pool index), so that every pool ends with exactly P.
 //
-// Cost: one sort of the window and one heap operation per sequence,
-// O(D log D) time and O(K) pool state.
+// Here the pools are the leaves of a tournament tree: every inner node holds
+// the winner of its two children under (open, load, pool index), a full pool
+// losing to any open one.  The root is the pool the rule asks for; after a
+// sequence is added, only the path from that pool's leaf to the root is
+// replayed.  Cost: one sort of the window and O(log K) per sequence.
 #include <algorithm>
 #include <cstdint>
-#include <functional>
-#include <queue>
-#include <utility>
+#include <new>
 #include <vector>
 
 #include "libra.h"
@@ -31,8 +32,10 @@ extern "C" libra_status libra_pack_workload(const int32_t *cu_seqlens, int32_t n
   return LIBRA_OK;
 }
 
-extern "C" libra_status libra_vrsp(const int64_t *workload, int32_t num_seqs, int32_t pool_size, int32_t *pool_of,
-                                   int32_t *order, int64_t *pool_load) {
+namespace {
+
+libra_status vrsp_impl(const int64_t *workload, int32_t num_seqs, int32_t pool_size, int32_t *pool_of,
+                       int32_t *order, int64_t *pool_load) {
   if (workload == nullptr || pool_of == nullptr || order == nullptr || num_seqs <= 0 || pool_size <= 0 ||
       num_seqs % pool_size != 0)
     return LIBRA_EINVAL;
@@ -46,23 +49,41 @@ extern "C" libra_status libra_vrsp(const int64_t *workload, int32_t num_seqs, in
     return workload[x] != workload[y] ? workload[x] > workload[y] : x < y;
   });
 
-  // Min-heap of (load, pool) over the pools that still have room.
-  using Entry = std::pair<int64_t, int32_t>;
-  std::vector<Entry> init;
-  init.reserve(pools);
-  for (int32_t k = 0; k < pools; ++k) init.emplace_back(0, k);
-  std::priority_queue<Entry, std::vector<Entry>, std::greater<Entry>> heap(std::greater<Entry>(), std::move(init));
+  // Tournament tree over the pools: leaves at [width, width + pools), node i
+  // holds the better of nodes 2i and 2i + 1, or -1 when neither subtree has an
+  // open pool; padding leaves are -1.
+  int32_t width = 1;
+  while (width < pools) width *= 2;
   std::vector<int32_t> count(pools, 0);
   std::vector<int64_t> load(pools, 0);
+  std::vector<int32_t> node(2 * (size_t)width, -1);
+  auto better = [&](int32_t x, int32_t y) {   // the winner of pools x and y (-1: none)
+    if (x < 0) return y;
+    if (y < 0) return x;
+    return (load[x] < load[y] || (load[x] == load[y] && x < y)) ? x : y;
+  };
+  for (int32_t k = 0; k < pools; ++k) node[width + k] = k;
+  for (int32_t i = width - 1; i >= 1; --i) node[i] = better(node[2 * i], node[2 * i + 1]);
   for (int32_t i : seq) {
-    const int32_t k = heap.top().second;
-    heap.pop();
+    const int32_t k = node[1];                 // open pool of least (load, index)
     pool_of[i] = k;
     order[(int64_t)k * pool_size + count[k]] = i;
     load[k] += workload[i];
-    if (++count[k] < pool_size) heap.emplace(load[k], k);
+    if (++count[k] == pool_size) node[width + k] = -1;   // full: out of the contest
+    for (int32_t j = (width + k) / 2; j >= 1; j /= 2) node[j] = better(node[2 * j], node[2 * j + 1]);
   }
   if (pool_load != nullptr)
     for (int32_t k = 0; k < pools; ++k) pool_load[k] = load[k];
   return LIBRA_OK;
+}
+
+}  // namespace
+
+extern "C" libra_status libra_vrsp(const int64_t *workload, int32_t num_seqs, int32_t pool_size, int32_t *pool_of,
+                                   int32_t *order, int64_t *pool_load) {
+  try {
+    return vrsp_impl(workload, num_seqs, pool_size, pool_of, order, pool_load);
+  } catch (const std::bad_alloc &) {
+    return LIBRA_EHOST;
+  }
 }

@@ -4,7 +4,9 @@ This module produces the two things every run needs and nothing else:
 
 * sample lengths (and the ``cu_seqlens`` prefix array) for one packed
   sequence of ``L`` tokens, and
-* bf16 tensors (held as ``uint16`` bit patterns) drawn from N(0, 1).
+* bf16 tensors (held as ``uint16`` bit patterns) drawn from N(0, 1), and
+  seeded variants of them whose logits leave the N(0, 1) range (scaled,
+  rising or falling along each sample) for the numerics tests.
 
 It holds none of the attention arithmetic.  Both the fp64 oracle (``oracle/``)
 and the HIP path consume what it returns, so the two sides see identical bits.
@@ -166,3 +168,36 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).copy()
     b += ((b >> 16) & 1) + 0x7FFF
     return (b >> 16).astype(np.uint16)
+
+
+def extreme_logit_inputs(w: Workload, cu, kind: str, seed: int, names=("q", "k", "v")) -> dict:
+    """Seeded inputs whose scaled logits leave the N(0, 1) range (the bf16 bits are what both the
+    GPU and the oracle read, so any transformation before rounding is exact for both):
+      x4 / x8   q and k multiplied by 4 or 8 (powers of two: exact), logit std about 23 or 92 in
+                log2 units, so block maxima jump by far more than the forward's rescale slack;
+      rising    q ~ u and key j of a sample ~ a_j u with a_j growing 0.75 per 64 keys, so every key
+                block's logits exceed all earlier ones by about 12 (log2 units): a rescale per block;
+      falling   the same with a_j shrinking along the sample: later blocks sit far below the first
+                maximum and their weights underflow."""
+    t = make_tensors(w, seed, names=names)
+    q = bf16_bits_to_f32(t["q"])
+    k = bf16_bits_to_f32(t["k"])
+    if kind in ("x4", "x8"):
+        m = 4.0 if kind == "x4" else 8.0
+        q, k = q * m, k * m
+    elif kind in ("rising", "falling"):
+        rng = np.random.default_rng(seed + 1000)
+        u = rng.standard_normal(w.head_dim).astype(np.float32)
+        lens = np.diff(cu)
+        start = np.repeat(cu[:-1], lens)
+        pos = (np.arange(w.total_tokens) - start).astype(np.float32)
+        if kind == "falling":
+            pos = np.repeat(lens, lens).astype(np.float32) - 1 - pos
+        a = 0.75 * pos / 64.0
+        k = a[:, None, None] * u[None, None, :] + 0.3 * k
+        q = u[None, None, :] + 0.3 * q
+    else:
+        raise ValueError(kind)
+    t["q"] = f32_to_bf16_bits(q.astype(np.float32))
+    t["k"] = f32_to_bf16_bits(k.astype(np.float32))
+    return t

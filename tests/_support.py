@@ -168,6 +168,30 @@ def oracle_bwd_tails(qb, kb, vb, dob, cu, scale, units):
         return list(ex.map(_bwd_tail_job, jobs))
 
 
+def _bwd_head_job(args):
+    import oracle.attention as A
+    q, k, v, do, scale = args               # one query head and its KV head, one sample
+    return A.backward_tail(q, k, v, do, 0, q.shape[0], 0, 0, scale)
+
+
+def oracle_bwd_unit(qb, kb, vb, dob, s, e, kv, g, scale):
+    """Complete backward of one (sample [s, e), KV head kv) unit: dq [n, g, d] of its g query
+    heads and dk, dv [n, d] summed over them.  Each query head runs in its own thread, as a
+    one-head problem of the oracle; dk and dv add up the heads' contributions, as the oracle
+    does within a unit."""
+    import oracle.attention as A
+    k1 = A.widen_bf16(kb[s:e, kv:kv + 1])
+    v1 = A.widen_bf16(vb[s:e, kv:kv + 1])
+    jobs = [(A.widen_bf16(qb[s:e, h:h + 1]), k1, v1, A.widen_bf16(dob[s:e, h:h + 1]), scale)
+            for h in range(kv * g, (kv + 1) * g)]
+    with _pool(min(workers(), g)) as ex:
+        parts = list(ex.map(_bwd_head_job, jobs))
+    dq = np.stack([p_[0][:, 0] for p_ in parts], axis=1)
+    dk = sum(p_[1] for p_ in parts)
+    dv = sum(p_[2] for p_ in parts)
+    return dq, dk, dv
+
+
 def sample_rows(cu, tile_tokens, n_random, seed, long_len=4096, edge=32, boundary_stride=1):
     """Rows to check at full size: edges of long samples, tile boundaries, random rows."""
     rng = np.random.default_rng(seed)
@@ -188,34 +212,5 @@ def sample_rows(cu, tile_tokens, n_random, seed, long_len=4096, edge=32, boundar
     return np.array(sorted(r for r in rows if 0 <= r < L), dtype=np.int64)
 
 
-def extreme_logit_inputs(w: synth.Workload, cu, kind: str, seed: int, names=("q", "k", "v")) -> dict:
-    """Seeded inputs whose scaled logits leave the N(0, 1) range (the bf16 bits are what both the
-    GPU and the oracle read, so any transformation before rounding is exact for both):
-      x4 / x8   q and k multiplied by 4 or 8 (powers of two: exact), logit std about 23 or 92 in
-                log2 units, so block maxima jump by far more than the forward's rescale slack;
-      rising    q ~ u and key j of a sample ~ a_j u with a_j growing 0.75 per 64 keys, so every key
-                block's logits exceed all earlier ones by about 12 (log2 units): a rescale per block;
-      falling   the same with a_j shrinking along the sample: later blocks sit far below the first
-                maximum and their weights underflow."""
-    t = synth.make_tensors(w, seed, names=names)
-    q = synth.bf16_bits_to_f32(t["q"])
-    k = synth.bf16_bits_to_f32(t["k"])
-    if kind in ("x4", "x8"):
-        m = 4.0 if kind == "x4" else 8.0
-        q, k = q * m, k * m
-    elif kind in ("rising", "falling"):
-        rng = np.random.default_rng(seed + 1000)
-        u = rng.standard_normal(w.head_dim).astype(np.float32)
-        lens = np.diff(cu)
-        start = np.repeat(cu[:-1], lens)
-        pos = (np.arange(w.total_tokens) - start).astype(np.float32)
-        if kind == "falling":
-            pos = np.repeat(lens, lens).astype(np.float32) - 1 - pos
-        a = 0.75 * pos / 64.0
-        k = a[:, None, None] * u[None, None, :] + 0.3 * k
-        q = u[None, None, :] + 0.3 * q
-    else:
-        raise ValueError(kind)
-    t["q"] = synth.f32_to_bf16_bits(q.astype(np.float32))
-    t["k"] = synth.f32_to_bf16_bits(k.astype(np.float32))
-    return t
+# seeded inputs with logits far outside the N(0, 1) range live with the other generators
+extreme_logit_inputs = synth.extreme_logit_inputs

@@ -31,6 +31,19 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(handle, n), n
 
 
+def test_counting_build_exports_its_header_and_the_library():
+    """liblibra_debug.so: every libra.h entry point plus the libra_debug.h counter functions; the
+    regular library has no counter."""
+    dbg_header = os.path.join(os.path.dirname(HEADER), "libra_debug.h")
+    extra = sorted(set(re.findall(r"^\s*libra_status\s+(libra_\w+)\s*\(", open(dbg_header).read(), re.M)))
+    assert extra == ["libra_debug_reset_unmasked_pairs", "libra_debug_unmasked_pairs"]
+    handle = ctypes.CDLL(os.path.join(os.path.dirname(lib.LIB_PATH), "liblibra_debug.so"))
+    for n in declared_functions() + extra:
+        assert hasattr(handle, n), n
+    regular = ctypes.CDLL(lib.LIB_PATH)
+    assert not any(hasattr(regular, n) for n in extra)
+
+
 def make_plan(lens, h_q, h_kv, d, B, W, **kw):
     cu = synth.cu_seqlens(lens)
     return lib.Plan(cu, total_tokens=int(sum(lens)), h_q=h_q, h_kv=h_kv, head_dim=d, tile_tokens=B,
@@ -52,6 +65,17 @@ CASES = [
     (list(synth.make_lengths(synth.WORKLOADS["train_256k"].with_tokens(7000), 1)), 32, 4, 128, 1000, 4,
      {"num_cus": 24, "worker_speed": [1000, 940, 1010, 950, 1060, 1000, 990, 940]}),
     ([1024, 512, 256, 256], 4, 4, 64, 256, 2, {"num_cus": 13, "worker_speed": [500, 2000, 0, 1000, 1500, 800, 0, 700]}),
+    # eq. 8 pairs as the forward / dQ item cost
+    (list(synth.make_lengths(synth.WORKLOADS["gqa_32k"].with_tokens(9000), 1)), 32, 8, 128, 4096, 8,
+     {"num_cus": 40, "cost": 1}),
+    # Algorithm 2 with the L2 residency term (per-XCD committed KV groups)
+    (list(synth.make_lengths(synth.WORKLOADS["gqa_32k"].with_tokens(9000), 0)), 32, 8, 128, 4096, 8,
+     {"assign": 2}),
+    (list(synth.make_lengths(synth.WORKLOADS["train_256k"].with_tokens(7000), 1)), 32, 4, 128, 1000, 4,
+     {"assign": 2, "num_cus": 24, "worker_speed": [1000, 940, 1010, 950, 1060, 1000, 990, 940]}),
+    ([7, 300, 1, 0, 1, 250, 900], 12, 4, 64, 100, 6, {"assign": 2, "num_cus": 19, "tau": 0.0}),
+    (list(synth.make_lengths(synth.WORKLOADS["share_1m"].with_tokens(6000, (4000,)), 2)), 8, 1, 128, 512, 2,
+     {"num_cus": 32, "assign": 2}),
 ]
 
 
@@ -72,11 +96,13 @@ def test_planner_matches_oracle(lens, h_q, h_kv, d, B, W, kw):
             assert int(g_[f]) == r[f], f
     assert info.total_pairs == sum(t["pairs"] for t in ref_tiles)
     # forward items and their placement
-    mode = "rr" if kw.get("assign", 0) == 1 else "lpt"
+    mode = {0: "lpt", 1: "rr", 2: "l2"}[kw.get("assign", 0)]
+    cost = {0: "executed", 1: "pairs"}[kw.get("cost", 0)]
+    tau = kw.get("tau", 0.03)
     ov = kw.get("item_overhead", 0)
-    items = P.fwd_items(cu, L, h_q, h_kv, B, W, overhead=ov)
+    items = P.fwd_items(cu, L, h_q, h_kv, B, W, overhead=ov, cost=cost)
     sp = kw.get("worker_speed")
-    offsets, ids, flags, load = P.zigzag_queue(cu, items, ncu, 0.03, mode, speed=sp)
+    offsets, ids, flags, load = P.zigzag_queue(cu, items, ncu, tau, mode, speed=sp, h_kv=h_kv)
     assert list(plan.cu_off) == offsets
     got_items = plan.items
     assert [int(x) for x in got_items["id"]] == ids
@@ -89,8 +115,8 @@ def test_planner_matches_oracle(lens, h_q, h_kv, d, B, W, kw):
     assert [int(t["n_items"]) for t in got] == [sum(1 for it in items if it["tile_id"] == t["tile_id"])
                                                for t in ref_tiles]
     # dQ items (the same tiles, cut for the dQ kernel) and their placement
-    dq = P.fwd_items(cu, L, h_q, h_kv, B, W, overhead=ov, columns=P.DQ_ITEM_COLUMNS)
-    offsets, ids, flags, load = P.zigzag_queue(cu, dq, ncu, 0.03, mode, speed=sp)
+    dq = P.fwd_items(cu, L, h_q, h_kv, B, W, overhead=ov, columns=P.DQ_ITEM_COLUMNS, cost=cost)
+    offsets, ids, flags, load = P.zigzag_queue(cu, dq, ncu, tau, mode, speed=sp, h_kv=h_kv)
     assert list(plan.dq_cu_off) == offsets
     got_dq = plan.dq_items
     assert [int(x) for x in got_dq["id"]] == ids
@@ -102,7 +128,7 @@ def test_planner_matches_oracle(lens, h_q, h_kv, d, B, W, kw):
     assert info.dq_load_max == max(load) and info.dq_load_sum == sum(load)
     # key-major dK/dV items and their placement
     kv = P.kv_items(cu, L, h_q, h_kv, overhead=ov)
-    offsets, ids, flags, load = P.zigzag_queue(cu, kv, ncu, 0.03, mode, last_key=True, speed=sp)
+    offsets, ids, flags, load = P.zigzag_queue(cu, kv, ncu, tau, mode, last_key=True, speed=sp, h_kv=h_kv)
     assert list(plan.kv_cu_off) == offsets
     got_kv = plan.kv_items
     assert [int(x) for x in got_kv["id"]] == ids
@@ -121,14 +147,28 @@ def test_plan_is_bitwise_deterministic():
     assert np.array_equal(a.host, b.host)
 
 
-def test_full_size_plans_match_closed_form_and_balance():
-    for name in ("gqa_32k", "skew_128k_a", "skew_128k_b", "share_1m", "train_256k"):
-        w = synth.WORKLOADS[name]
-        lens = synth.make_lengths(w, 0)
-        plan, cu = make_plan(list(lens), w.h_q, w.h_kv, w.head_dim, w.tile_tokens, w.tile_heads)
-        assert plan.info.total_pairs == w.h_q * int((lens * (lens + 1) // 2).sum())
-        assert plan.info.load_sum == plan.info.total_pairs        # no overhead: cost == pairs
-        assert plan.info.load_max / (plan.info.load_sum / 256) < 1.01, name
+@pytest.mark.parametrize("name", ["gqa_32k", "skew_128k_a", "skew_128k_b", "share_1m", "train_256k"])
+def test_full_size_plans_match_closed_form_and_balance(name):
+    w = synth.WORKLOADS[name]
+    lens = synth.make_lengths(w, 0)
+    pairs = w.h_q * int((lens * (lens + 1) // 2).sum())
+    by_pairs, cu = make_plan(list(lens), w.h_q, w.h_kv, w.head_dim, w.tile_tokens, w.tile_heads,
+                             cost=lib.COST_PAIRS)
+    assert by_pairs.info.total_pairs == pairs
+    assert by_pairs.info.load_sum == pairs                   # no overhead: cost == pairs
+    plan, _ = make_plan(list(lens), w.h_q, w.h_kv, w.head_dim, w.tile_tokens, w.tile_heads)
+    assert plan.info.total_pairs == pairs
+    assert plan.info.load_sum >= pairs                        # executed slots cover every pair
+    # the dK/dV queue of the 32K pack has only 1368 items for 256 workers: 1.011
+    for mx, sm, bound in ((plan.info.load_max, plan.info.load_sum, 1.01),
+                          (plan.info.dq_load_max, plan.info.dq_load_sum, 1.01),
+                          (plan.info.kv_load_max, plan.info.kv_load_sum, 1.02)):
+        assert mx / (sm / 256) < bound, name
+    l2, _ = make_plan(list(lens), w.h_q, w.h_kv, w.head_dim, w.tile_tokens, w.tile_heads,
+                      assign=lib.ASSIGN_PLACER_L2)
+    assert l2.info.load_sum == plan.info.load_sum
+    assert l2.info.load_max / (l2.info.load_sum / 256) <= 1.03 + 1e-9 or \
+        l2.info.load_max <= plan.info.load_max, name         # within the soft target, or no worse
 
 
 def test_plan_check_rejects_corruption():
@@ -146,7 +186,7 @@ def test_plan_check_rejects_corruption():
 def _params(**over):
     p = dict(total_tokens=10, num_samples=2, h_q=4, h_kv=2, head_dim=128, tile_tokens=4, tile_heads=2,
              num_cus=0, tau=0.03, assign=0, item_overhead=0,
-             worker_speed=(ctypes.c_uint16 * 8)(*([0] * 8)))
+             worker_speed=(ctypes.c_uint16 * 8)(*([0] * 8)), cost=0, reserved=0)
     p.update(over)
     return lib.PlanParams(*[p[f] for f, _ in lib.PlanParams._fields_])
 
@@ -172,6 +212,9 @@ def _plan_status(cu, params, capacity=None):
     ([0, 4, 10], {"tile_tokens": 0}, lib.LIBRA_EINVAL),
     ([0, 4, 10], {"num_cus": -1}, lib.LIBRA_EINVAL),
     ([0, 4, 10], {"assign": 7}, lib.LIBRA_EINVAL),
+    ([0, 4, 10], {"cost": 2}, lib.LIBRA_EINVAL),
+    ([0, 4, 10], {"reserved": 1}, lib.LIBRA_EINVAL),
+    ([0, 4, 10], {"assign": 2}, lib.LIBRA_OK),
     ([0, 4, 10], {"tau": float("nan")}, lib.LIBRA_EINVAL),
     ([0, 4, 10], {"item_overhead": -1}, lib.LIBRA_EINVAL),
     ([0, 4, 10], {"head_dim": 96}, lib.LIBRA_EUNSUPPORTED),
@@ -235,6 +278,73 @@ def test_fwd_rejects_foreign_plan(small_plan):
     bad = small_plan.host.copy()
     bad[0] ^= 1
     assert call_fwd(fwd_args(small_plan, plan_host=bad)) == lib.LIBRA_EINVAL
+
+
+@pytest.mark.parametrize("where", ["items", "dq", "kv", "cu_off", "header"])
+def test_launches_reject_a_plan_whose_checksum_fails(small_plan, where):
+    """Every launch entry point verifies the host plan's checksum before enqueuing anything."""
+    info = small_plan.info
+    off = {"items": info.off_items + 3, "dq": info.off_dq_items + 17, "kv": info.off_kv_items + 40,
+           "cu_off": info.off_cu_off + 4, "header": 40}[where]        # 40: inside params (h_kv)
+    bad = small_plan.host.copy()
+    bad[off] ^= 0x10
+    assert call_fwd(fwd_args(small_plan, plan_host=bad)) == lib.LIBRA_EINVAL
+    h = bad.ctypes.data
+    bws = 1 << 20
+    assert lib._lib.libra_attn_bwd_dkdv(h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        ctypes.c_float(0.1), FAKE, bws, None, None) == lib.LIBRA_EINVAL
+    assert lib._lib.libra_attn_bwd_dq(h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1),
+                                      FAKE, bws, None, None) == lib.LIBRA_EINVAL
+    assert lib._lib.libra_attn_bwd_prepare(h, FAKE, FAKE, FAKE, FAKE, bws, None) == lib.LIBRA_EINVAL
+    assert lib._lib.libra_attn_bwd(h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   ctypes.c_float(0.1), FAKE, bws, None, None) == lib.LIBRA_EINVAL
+
+
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+
+    def define(name):
+        return int(re.search(rf"#define {name} (0x[0-9A-Fa-f]+|\d+)u?", text).group(1), 0)
+
+    def enum(name):
+        return int(re.search(rf"\b{name} = (-?\d+)", text).group(1))
+    assert lib.PLAN_VERSION == define("LIBRA_PLAN_VERSION")
+    assert lib.PLAN_MAGIC == define("LIBRA_PLAN_MAGIC")
+    assert lib.RECORD_PLAN_MISMATCH == define("LIBRA_RECORD_PLAN_MISMATCH")
+    for name in ("LIBRA_EINVAL", "LIBRA_ESIZE", "LIBRA_EUNSUPPORTED", "LIBRA_EHIP", "LIBRA_EHOST"):
+        assert getattr(lib, name) == enum(name), name
+    for py, c in (("ASSIGN_PLACER", "LIBRA_ASSIGN_PLACER"), ("ASSIGN_ROUND_ROBIN", "LIBRA_ASSIGN_ROUND_ROBIN"),
+                  ("ASSIGN_PLACER_L2", "LIBRA_ASSIGN_PLACER_L2"), ("COST_EXECUTED", "LIBRA_COST_EXECUTED"),
+                  ("COST_PAIRS", "LIBRA_COST_PAIRS"), ("QUEUE_KV", "LIBRA_QUEUE_KV")):
+        assert getattr(lib, py) == enum(c), c
+
+
+def test_wrappers_check_tensors_against_the_plan(small_plan):
+    """The torch wrappers refuse tensors that do not match the plan before any library call
+    (shapes first, then dtype, contiguity and device: CPU tensors of the right shape fail last)."""
+    import torch
+    L, h_q, h_kv, d = 128, 4, 2, 128
+    bf = torch.bfloat16
+    q = torch.zeros(L, h_q, d, dtype=bf)
+    k = torch.zeros(L, h_kv, d, dtype=bf)
+    v = torch.zeros(L, h_kv, d, dtype=bf)
+    with pytest.raises(ValueError, match="q: shape"):
+        lib.attn_fwd(small_plan, q[:-1], k, v)
+    with pytest.raises(ValueError, match="k: shape"):
+        lib.attn_fwd(small_plan, q, torch.zeros(L, h_q, d, dtype=bf), v)
+    with pytest.raises(ValueError, match="v: dtype"):
+        lib.attn_fwd(small_plan, q, k, v.float())
+    with pytest.raises(ValueError, match="contiguous"):
+        lib.attn_fwd(small_plan, q, k, torch.zeros(L, d, h_kv, dtype=bf).transpose(1, 2))
+    with pytest.raises(ValueError, match="lse: shape"):
+        lib.attn_fwd(small_plan, q, k, v, lse=torch.zeros(L, h_q))
+    with pytest.raises(ValueError, match="on a GPU"):
+        lib.attn_fwd(small_plan, q, k, v)
+    lse = torch.zeros(h_q, L)
+    with pytest.raises(ValueError, match="dout: shape"):
+        lib.attn_bwd(small_plan, q, k, v, q, lse, q[:, :2])
+    with pytest.raises(ValueError, match="on a GPU"):
+        lib.attn_bwd(small_plan, q, k, v, q, lse, q)
 
 
 def test_phase_entry_points_validate(small_plan):

@@ -286,39 +286,18 @@ def test_pins_catch_backward_sign_slip(monkeypatch):
         test_backward_matches_finite_differences()
 
 
-# ------------------------------------------------ the bf16 yardstick of the tolerance
-def test_round_bf16_is_nearest_ties_to_even():
-    """Against a distance-based statement of rounding: the nearer of the two neighbouring bf16
-    values, the one with an even last mantissa bit on a tie."""
-    rng = np.random.default_rng(7)
-    hi = rng.integers(0x0080, 0x7F00, 4000, dtype=np.uint32)          # normal, finite bf16 patterns
-    lo = rng.integers(0, 0x10000, 4000, dtype=np.uint32)
-    lo[:200] = 0x8000                                                  # exact ties
-    lo[200:300] = 0
-    f = ((hi << 16) | lo).view(np.float32).astype(np.float64)
-    down = (hi << 16).view(np.float32).astype(np.float64)
-    up = ((hi + 1) << 16).view(np.float32).astype(np.float64)
-    dd, du = f - down, up - f
-    expect = np.where(dd < du, down, np.where(du < dd, up, np.where(hi % 2 == 0, down, up)))
-    assert np.array_equal(A.round_bf16(f), expect)
-    assert np.array_equal(A.round_bf16(-f), -expect)
-
-
-def test_bf16_reference_is_the_same_attention_at_bf16_precision():
-    """The yardstick evaluates the oracle's function: its O and gradients sit within bf16-level
-    error of the exact results (and, rounding every tensor, are not identical to them)."""
-    rng = np.random.default_rng(11)
-    lens = [40, 1, 23, 0, 64]
-    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+def test_per_head_unit_assembly_equals_the_full_backward():
+    """The GPU tests' complete-unit check runs one oracle problem per query head in threads and
+    sums dK and dV over the group: that must equal the oracle's own backward of the unit."""
+    from tests import _support as S
+    rng = np.random.default_rng(21)
+    lens = [70, 130]
     L = sum(lens)
-    q, k, v = (A.round_bf16(x) for x in rand_qkv(rng, L, 4, 2, 32))
-    do = A.round_bf16(rng.standard_normal((L, 4, 32)))
-    scale = 1 / np.sqrt(32)
-    o_ref, _ = dense_reference(q, k, v, lens, scale)
-    g_ref = A.backward(q, k, v, do, cu, scale)
-    o_b, *g_b = A.backward_bf16_reference(q, k, v, do, cu, scale)
-    assert np.array_equal(A.round_bf16(o_b), o_b)
-    assert 0 < np.abs(o_b - o_ref).max() <= 2e-2
-    for r, b in zip(g_ref, g_b):
-        rel = np.abs(b - r).max() / np.abs(r).max()
-        assert 0 < rel <= 5e-2, rel
+    cu = np.array([0, 70, 200])
+    bits = {n: rng.integers(0x3000, 0x4000, size=(L, h, 32), dtype=np.uint16) | (rng.integers(0, 2, size=(L, h, 32), dtype=np.uint16) << 15)
+            for n, h in (("q", 6), ("k", 2), ("v", 2), ("dout", 6))}
+    full = A.backward(*(A.widen_bf16(bits[n]) for n in ("q", "k", "v", "dout")), cu, 0.2)
+    dq, dk, dv = S.oracle_bwd_unit(bits["q"], bits["k"], bits["v"], bits["dout"], 70, 200, 1, 3, 0.2)
+    assert np.allclose(dq, full[0][70:200, 3:6], rtol=0, atol=1e-12)
+    assert np.allclose(dk, full[1][70:200, 1], rtol=0, atol=1e-12)
+    assert np.allclose(dv, full[2][70:200, 1], rtol=0, atol=1e-12)

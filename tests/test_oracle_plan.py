@@ -81,7 +81,9 @@ def test_items_partition_tiles(h_q, h_kv, W):
             assert h // g == it["kv_head"]
             assert t["head_begin"] <= h < t["head_begin"] + t["head_count"]
         cover[it["row0"]:it["row0"] + it["nrows"], it["head0"]:it["head0"] + it["nheads"]] += 1
-        assert it["cost"] == it["pairs"] + 7
+        assert it["cost"] == P.executed_slots(P._ranges(cu), it["row0"], it["nrows"], it["nheads"],
+                                              P.ITEM_COLUMNS) + 7
+        assert it["cost"] - 7 >= it["pairs"]
         per_tile[it["tile_id"]] = per_tile.get(it["tile_id"], 0) + it["pairs"]
     assert (cover == 1).all()
     assert all(per_tile[i] == t["pairs"] for i, t in tiles.items())
@@ -189,3 +191,114 @@ def test_weighted_placement_hand_worked():
     sigma, order = P.place([6, 4, 3], 2, speed=[2000, 1000, 0, 0, 0, 0, 0, 0])
     assert order == [0, 1, 2] and sigma == [0, 1, 0]
     assert P.place([6, 4, 3], 2, speed=[700] * 8) == P.place([6, 4, 3], 2)
+
+
+# ------------------------------------------------ executed-work costs, worked by hand
+HAND_CU = [0, 100, 400, 450]          # samples of 100, 300 and 50 tokens
+
+
+def test_kv_item_cost_hand_worked():
+    """Chunks of 192 keys, g = 2.  Chunk 0 (keys 0-191): its last key lies in sample 1, which ends
+    at 400, so the query walk runs from 0 up to 400: ceil(400 / 64) = 7 blocks; executed
+    2 x 7 x 64 x 192 = 172032.  Pairs: keys 0-99 see 100 - k queries (5050 in all), keys 100-191
+    see 400 - k (209 + ... + 300 = 23414): 2 x 28464 = 56928.  Chunk 1 (192-383): walk 192 -> 400,
+    ceil(208 / 64) = 4 blocks, 2 x 4 x 64 x 192 = 98304; pairs 2 x (17 + ... + 208) = 43200.
+    Chunk 2 (384-449, 66 keys): its last key is in sample 2 (ends 450): walk 384 -> 450,
+    ceil(66 / 64) = 2 blocks, 2 x 2 x 64 x 66 = 16896; pairs 2 x (136 + 1275) = 2822."""
+    kv = P.kv_items(HAND_CU, 450, h_q=4, h_kv=2)
+    got = [(it["row0"], it["nrows"], it["kv_head"], it["pairs"], it["cost"]) for it in kv]
+    assert got == [(0, 192, 0, 56928, 172032), (0, 192, 1, 56928, 172032),
+                   (192, 192, 0, 43200, 98304), (192, 192, 1, 43200, 98304),
+                   (384, 66, 0, 2822, 16896), (384, 66, 1, 2822, 16896)]
+    assert [it["cost"] for it in P.kv_items(HAND_CU, 450, 4, 2, overhead=5)] == [172037] * 2 + [98309] * 2 + [16901] * 2
+
+
+def test_fwd_item_executed_cost_hand_worked():
+    """One tile of 450 tokens x 4 heads on one KV head: items of 96 rows x 4 heads, twelve waves of
+    32 rows (three row ranges, four heads each).  A row r of sample j needs the 64-key blocks
+    start_j / 64 .. r / 64.  Item rows 0-95: ranges 0-31 and 32-63 need block 0, 64-95 blocks
+    0-1: 4 blocks x 4 heads = 16.  Rows 96-191: 96-127 straddles samples 0 and 1 (blocks 0-1 and
+    1-1: 2), 128-159 and 160-191 need 1-2: 6 x 4 = 24.  Rows 192-287: 3 + 3 + 4 = 10, x 4 = 40.
+    Rows 288-383: 4 + 5 + 5 = 14, x 4 = 56.  Rows 384-449 (66 rows): 384-415 straddles (sample 1:
+    1-6, sample 2: 6-6: 6 blocks), 416-447 needs 6, 448-449 needs 6-7: 9 x 4 = 36.  Each
+    wave-block is 32 x 64 = 2048 slots.  Pairs: rows 0-95 are sample 0's first 96 queries,
+    4 x 96 x 97 / 2 = 18624."""
+    items = P.fwd_items(HAND_CU, 450, 4, 1, 450, 4)
+    assert [(it["row0"], it["nrows"], it["nheads"]) for it in items] == [(0, 96, 4), (96, 96, 4), (192, 96, 4),
+                                                                        (288, 96, 4), (384, 66, 4)]
+    assert [it["cost"] for it in items] == [2048 * b for b in (16, 24, 40, 56, 36)]
+    assert items[0]["pairs"] == 18624
+    by_pairs = P.fwd_items(HAND_CU, 450, 4, 1, 450, 4, overhead=3, cost="pairs")
+    assert [it["cost"] for it in by_pairs] == [it["pairs"] + 3 for it in items]
+
+
+def test_executed_cost_pins_catch_block_size_slips(monkeypatch):
+    """Planted in the oracle: a wrong key-block size, or query blocks of the dK/dV walk taken at
+    the wrong alignment; the hand pins above must fail."""
+    monkeypatch.setattr(P, "KEY_BLOCK", 32)
+    with pytest.raises(AssertionError):
+        test_fwd_item_executed_cost_hand_worked()
+    monkeypatch.undo()
+    monkeypatch.setattr(P, "KV_QUERY_BLOCK", 128)
+    with pytest.raises(AssertionError):
+        test_kv_item_cost_hand_worked()
+
+
+def test_executed_cost_covers_pairs_and_equals_them_on_full_blocks():
+    """Executed slots are at least the pairs (every pair lies in a computed block), and on a
+    sample whose rows are far from its start and end in whole blocks they count every block of
+    the walk: an item of 384 rows of one head at rows 4096-4479 of a 8192-token sample
+    computes, per wave w, blocks 0 .. (4096 + 32 w + 31) / 64."""
+    cu = [0, 8192]
+    items = P.fwd_items(cu, 8192, 1, 1, 8192, 1)
+    it = next(i for i in items if i["row0"] == 4224)
+    expect = sum((it["row0"] + 32 * w + 31) // 64 + 1 for w in range(12)) * 2048
+    assert it["cost"] == expect
+    for i in items:
+        assert i["cost"] >= i["pairs"]
+
+
+# ------------------------------------------------ Algorithm 2 with the L2 residency term
+def test_l2_residency_hand_worked():
+    """Ten workers (worker r on XCD r mod 8: workers 0 and 8 share XCD 0, 1 and 9 share XCD 1),
+    tau = 1: a worker fits while load + cost <= 2 x 14 / 10 = 2.8 (sum of costs 14).  Units
+    (cost, groups): 0 (6, A), 1 (3, B), 2 (3, A), 3 (1, B), 4 (1, B); volumes A = 5, B = 7.
+      unit 0: fits nowhere; all loads 0 and all terms 5 -> worker 0; XCD 0 holds A.
+      unit 1: fits nowhere; least load 0 on workers 1-9, terms all 7 -> worker 1; XCD 1 holds B.
+      unit 2: fits nowhere; least load 0 on workers 2-9, and worker 8 (XCD 0) already holds A
+              (term 0 against 5) -> worker 8.
+      unit 3: fits on workers 2-7 and 9 (load 0); worker 9 (XCD 1) holds B -> term 0 -> 9.
+      unit 4: fits on 2-7 (load 0, term 7) and 9 (load 1, term 0): the term ranks before the
+              load within the target -> 9.
+    Without the term the same units go to workers 0, 1, 2, 3, 4 (least load, then id)."""
+    A_, B_ = 0, 1
+    res = P.L2Residency([{A_}, {B_}, {A_}, {B_}, {B_}], {A_: 5, B_: 7})
+    sigma, order = P.place([6, 3, 3, 1, 1], 10, 1.0, dcomm=res.dcomm, commit=res.commit)
+    assert order == [0, 1, 2, 3, 4] and sigma == [0, 1, 8, 9, 9]
+    assert res.held[0] == {A_} and res.held[1] == {B_}
+    assert P.place([6, 3, 3, 1, 1], 10, 1.0)[0] == [0, 1, 2, 3, 4]
+
+
+def test_item_kv_groups_are_the_samples_its_rows_meet():
+    """eq. 7 for items: rows 96-191 of HAND_CU meet samples 0 and 1; with h_kv = 2 and KV head 1
+    the group ids are 0 * 2 + 1 and 1 * 2 + 1.  Empty samples hold no group."""
+    it = dict(row0=96, nrows=96, kv_head=1)
+    assert P.kv_groups(HAND_CU, it, 2) == {1, 3}
+    assert P.kv_groups([0, 100, 100, 400], dict(row0=99, nrows=2, kv_head=0), 1) == {0, 2}
+    assert P.group_volumes(HAND_CU, 2) == {0: 100, 1: 100, 2: 300, 3: 300, 4: 50, 5: 50}
+
+
+def test_l2_mode_places_every_item_once_and_keeps_loads():
+    """On a random pack the L2 mode places the same items (each once) with the same total load,
+    and no worker ends beyond the soft target by more than one unit's cost."""
+    rng = np.random.default_rng(5)
+    lens = [int(x) for x in rng.integers(1, 700, size=12)]
+    cu = cu_of(lens)
+    L = sum(lens)
+    items = P.fwd_items(cu, L, 8, 2, 512, 4)
+    o1, ids1, f1, load1 = P.zigzag_queue(cu, items, 16, 0.03, "lpt", h_kv=2)
+    o2, ids2, f2, load2 = P.zigzag_queue(cu, items, 16, 0.03, "l2", h_kv=2)
+    assert sorted(ids2) == sorted(ids1) == list(range(len(items)))
+    assert sum(load2) == sum(load1)
+    unit_max = max(it["cost"] for it in items) * 2
+    assert max(load2) <= 1.03 * sum(load2) / 16 + unit_max
