@@ -252,6 +252,28 @@ libra_status libra_attn_bwd(const void *plan, const void *plan_dev,
                             void *workspace, size_t workspace_bytes,
                             libra_cu_record *records, void *stream);
 
+/* The backward without any allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments, results and errors as libra_attn_bwd,
+ * but the workspace is a device array inside the library, one per GPU, of
+ * LIBRA_NOALLOC_SCRATCH_BYTES (64 MiB: h_q x L up to 8M, e.g. 32 query heads
+ * x 262144 tokens), held on every GPU the library's backward code is loaded
+ * on until the process ends.
+ * A plan needing more (libra_attn_bwd_workspace) gets LIBRA_ESIZE and nothing
+ * is enqueued.  The call allocates nothing (no hipMalloc, no host or library
+ * allocation) and synchronises nothing; nothing in the array needs to start
+ * at zero, since each call's first phase writes all of it before the later
+ * phases read it.  Every call on one GPU shares that GPU's array, so calls
+ * whose work overlaps on one GPU (other streams, other threads) race: order
+ * them on one stream or with events. */
+#define LIBRA_NOALLOC_SCRATCH_BYTES (64u << 20)
+libra_status libra_attn_bwd_noalloc(const void *plan, const void *plan_dev,
+                                    const void *q, const void *k, const void *v,
+                                    const void *o, const void *dout, const float *lse,
+                                    const int32_t *cu_seqlens_dev,
+                                    void *dq, void *dk, void *dv, float softmax_scale,
+                                    libra_cu_record *records, void *stream);
+
 /* The backward in three phases on the same stream (libra_attn_bwd enqueues
  * all three, in this order):
  *   _prepare: computes D = rowsum(dout * o) and LSE * log2(e) (fp32) into the

@@ -92,6 +92,7 @@ def _load():
     lib.libra_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp]
     lib.libra_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
                                    vp, sz, vp, vp]
+    lib.libra_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp]
     lib.libra_attn_bwd_prepare.argtypes = [vp, vp, vp, vp, vp, sz, vp]
     lib.libra_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
     lib.libra_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, sz, vp, vp]
@@ -105,7 +106,8 @@ def _load():
     lib.libra_worker_speed.argtypes = [vp, ctypes.c_int32, vp, vp]
     for name in ("libra_plan", "libra_plan_check", "libra_attn_bwd_workspace", "libra_attn_fwd",
                  "libra_attn_bwd", "libra_device_clock_khz", "libra_attn_bwd_prepare", "libra_attn_bwd_dkdv",
-                 "libra_attn_bwd_dq", "libra_pack_workload", "libra_vrsp"):
+                 "libra_attn_bwd_dq", "libra_pack_workload", "libra_vrsp", "libra_attn_bwd_noalloc",
+                 "libra_worker_speed"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -207,6 +209,17 @@ def libra_attn_bwd(plan_host, plan_dev, q, k, v, o, dout, lse, cu_seqlens_dev, d
                                float(softmax_scale), _ptr(workspace), int(workspace_bytes),
                                _ptr(records), stream),
            "libra_attn_bwd")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def libra_attn_bwd_noalloc(plan_host, plan_dev, q, k, v, o, dout, lse, cu_seqlens_dev, dq, dk, dv,
+                           softmax_scale, records, stream):
+    _check(_lib.libra_attn_bwd_noalloc(_ptr(plan_host), _ptr(plan_dev), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                       _ptr(dout), _ptr(lse), _ptr(cu_seqlens_dev), _ptr(dq), _ptr(dk),
+                                       _ptr(dv), float(softmax_scale), _ptr(records), stream),
+           "libra_attn_bwd_noalloc")
 
 
 def libra_attn_bwd_prepare(plan_host, o, dout, lse, workspace, workspace_bytes, stream):

@@ -32,6 +32,7 @@
 #include <cmath>
 #include <cstddef>
 #include <initializer_list>
+#include <mutex>
 #include <type_traits>
 
 #include "bwd_common.h"
@@ -484,6 +485,69 @@ extern "C" libra_status libra_attn_bwd(const void *plan, const void *plan_dev, c
   if (st != LIBRA_OK || h.params.total_tokens == 0) return st;
   if ((st = launch_prepare(h, o, dout, lse, workspace, stream)) != LIBRA_OK) return st;
   const BwdArgs a = make_args(h, q, k, v, dout, lse, cu_dev, workspace, softmax_scale);
+  if ((st = launch_dkdv(h, a, plan_dev, dk, dv, records, stream)) != LIBRA_OK) return st;
+  return launch_dq(h, a, plan_dev, dq, records ? records + h.num_cus : nullptr, stream);
+}
+
+// ----------------------------------------------------------------- backward without allocation
+// The backward's only scratch memory is its workspace (D and LSE * log2(e),
+// fp32 [h_q][L] each).  For callers that cannot allocate, it lives in this
+// file-scope device array, one copy per GPU the library runs on, held until
+// the process ends.  In host code `scratch` names a host-side stand-in, not
+// the device array: its device address comes from hipGetSymbolAddress, taken
+// once per device (with that device current) and kept in scratch_dev.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[LIBRA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_dev[kMaxDevices];   // device address of `scratch` on each device, once taken
+
+// The device address of the current device's copy of `scratch`.
+libra_status scratch_address(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LIBRA_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return LIBRA_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_dev[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return LIBRA_EHIP;
+    }
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return LIBRA_OK;
+}
+
+}  // namespace
+
+extern "C" libra_status libra_attn_bwd_noalloc(const void *plan, const void *plan_dev, const void *q,
+                                               const void *k, const void *v, const void *o, const void *dout,
+                                               const float *lse, const int32_t *cu_dev, void *dq, void *dk,
+                                               void *dv, float softmax_scale, libra_cu_record *records,
+                                               void *stream) {
+  libra_plan_info h;
+  libra_status st = check_header(plan, &h);
+  if (st != LIBRA_OK) return st;
+  const size_t need = bwd_layout(h.params).total;
+  if (need > (size_t)LIBRA_NOALLOC_SCRATCH_BYTES) return LIBRA_ESIZE;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return LIBRA_EINVAL;
+  if (h.params.total_tokens == 0) return LIBRA_OK;
+  // The checks of libra_attn_bwd, with a stand-in workspace address (the
+  // array's address is only taken once the arguments are known to be good).
+  const void *probe = reinterpret_cast<const void *>(uintptr_t(256));
+  st = check_prepare(h, o, dout, lse, probe, need);
+  if (st == LIBRA_OK)
+    st = check_pass(h, plan_dev, {q, k, v, dout, dq, dk, dv}, lse, cu_dev, softmax_scale, probe, need, records);
+  if (st != LIBRA_OK) return st;
+  void *ws = nullptr;
+  if ((st = scratch_address(&ws)) != LIBRA_OK) return st;
+  if ((st = launch_prepare(h, o, dout, lse, ws, stream)) != LIBRA_OK) return st;
+  const BwdArgs a = make_args(h, q, k, v, dout, lse, cu_dev, ws, softmax_scale);
   if ((st = launch_dkdv(h, a, plan_dev, dk, dv, records, stream)) != LIBRA_OK) return st;
   return launch_dq(h, a, plan_dev, dq, records ? records + h.num_cus : nullptr, stream);
 }

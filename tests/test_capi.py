@@ -386,6 +386,32 @@ def test_bwd_validation(small_plan):
     assert lib._lib.libra_attn_bwd(*args) == lib.LIBRA_ESIZE
 
 
+def test_noalloc_backward_validates_and_caps_its_size(small_plan):
+    """The backward without allocation takes libra_attn_bwd's checks, and a plan whose workspace
+    exceeds the library's 64 MiB array gets LIBRA_ESIZE; both return before the device is touched."""
+    h = small_plan.host.ctypes.data
+    full = [h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), None, None]
+    for i in range(1, 12):
+        args = list(full)
+        args[i] = None
+        assert lib._lib.libra_attn_bwd_noalloc(*args) == lib.LIBRA_EINVAL, i
+    args = list(full)
+    args[12] = ctypes.c_float(0.0)
+    assert lib._lib.libra_attn_bwd_noalloc(*args) == lib.LIBRA_EINVAL
+    text = open(HEADER).read()
+    assert lib.NOALLOC_SCRATCH_BYTES == int(re.search(r"#define LIBRA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)",
+                                                        text).group(1)) << 20
+    # 32 heads x 262144 tokens fit exactly (2 x 4 bytes each); one more sample of 64 tokens does not
+    for L, status in ((262144, None), (262144 + 64, lib.LIBRA_ESIZE)):
+        big = lib.Plan(np.array([0, L], dtype=np.int32), total_tokens=L, h_q=32, h_kv=4, head_dim=128,
+                       tile_tokens=8192, tile_heads=32)
+        assert lib.libra_attn_bwd_workspace(big.host) <= lib.NOALLOC_SCRATCH_BYTES or status is not None
+        if status is not None:
+            args = list(full)
+            args[0] = big.host.ctypes.data
+            assert lib._lib.libra_attn_bwd_noalloc(*args) == status
+
+
 def test_workspace_sizes(small_plan):
     # D and LSE * log2(e): fp32 [h_q][L] each, 256-byte aligned (L = 128, h_q = 4)
     assert lib.libra_attn_bwd_workspace(small_plan.host) == 2 * 2048
