@@ -142,10 +142,53 @@ def cpu_baseline(w, cu, tensors, scale, with_bwd=True, budget_s=15.0):
     if ctx is not None:
         ctx.restore_original_limits()
     flops = (3.5 if with_bwd else 1.0) * 4 * w.head_dim * pairs
+    full = (3.5 if with_bwd else 1.0) * 4 * w.head_dim * w.h_q * int((lens * (lens + 1) // 2).sum())
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "extrapolated_full_config_s": round(full / (flops / elapsed), 1),
             "sample": f"fp64 numpy oracle {'fwd+bwd' if with_bwd else 'fwd'} on {done} (sample, KV head) units of the same pack "
                       f"(the last 64, then 256, 1024, ... query rows of each sample, heaviest first, until "
                       f"{budget_s:.0f} s were spent; {pairs} causal pair-heads) in {elapsed:.1f} s"}
+
+
+def cpu_oracle_full(workloads=("tiny_2k", "gqa_32k", "skew_128k_b")):
+    """The complete fp64 forward oracle (every sample, every head) on whole packs, timed on the
+    host cores (one worker thread per core, one BLAS thread each, one (sample, head) per task);
+    prints a markdown table."""
+    import synth
+    import oracle.attention as A
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:          # pragma: no cover
+        threadpool_limits = None
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    print(f"| workload | L | h_q/h_kv | d | samples | fwd FLOPs | oracle s | oracle TFLOP/s | cores |")
+    print("|---|---|---|---|---|---|---|---|---|", flush=True)
+    for name in workloads:
+        w = synth.WORKLOADS[name]
+        lens = synth.make_lengths(w, 0)
+        cu = synth.cu_seqlens(lens)
+        t = synth.make_tensors(w, 0)
+        q, k, v = (A.widen_bf16(t[n]) for n in ("q", "k", "v"))
+        scale = 1.0 / math.sqrt(w.head_dim)
+        g = w.h_q // w.h_kv
+        units = [(int(cu[j]), int(cu[j + 1]), h) for j in range(len(lens)) if lens[j] > 0 for h in range(w.h_q)]
+        units.sort(key=lambda u: -(u[1] - u[0]))
+
+        def run(u):
+            s_, e_, h = u
+            return A.head_rows(q, k, v, s_, e_, h, h // g, 0, e_ - s_, scale)
+
+        ctx = threadpool_limits(limits=1) if threadpool_limits else None
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(cores) as ex:
+            for _ in ex.map(run, units):
+                pass
+        el = time.perf_counter() - t0
+        if ctx is not None:
+            ctx.restore_original_limits()
+        flops = 4.0 * w.head_dim * w.h_q * int((lens.astype(np.int64) * (lens + 1) // 2).sum())
+        print(f"| {name} | {w.total_tokens} | {w.h_q}/{w.h_kv} | {w.head_dim} | {len(lens)} | {flops:.3g} | "
+              f"{el:.1f} | {flops / el / 1e12:.3f} | {cores} |", flush=True)
 
 
 def traffic_for(kernel, workload, launches_bytes_fn):
@@ -514,7 +557,7 @@ def _make_inputs(workload, seed, names):
 
 def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, warmup=2, cpu=True,
             calibrate_copy=0, quiet=False, tiling=None, dump_records=None, speed_calibration=True,
-            cost=0, item_overhead=0):
+            cost=0, item_overhead=0, tau=0.03):
     """Time `steps` steps of the hot path on cuda:0; returns the JSON record.  `tiling`
     = (tile_tokens, tile_heads) replaces the workload's SH-Tile shape."""
     import torch
@@ -541,7 +584,7 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
 
     tile_tokens, tile_heads = tiling if tiling else (w.tile_tokens, w.tile_heads)
     plan_kw = dict(total_tokens=L, h_q=w.h_q, h_kv=w.h_kv, head_dim=d, tile_tokens=tile_tokens,
-                   tile_heads=tile_heads, assign=assign, cost=cost, item_overhead=item_overhead)
+                   tile_heads=tile_heads, assign=assign, cost=cost, item_overhead=item_overhead, tau=tau)
     plan0 = lib.Plan(cu, **plan_kw)
     ncu = plan0.info.num_cus
     ws_b = torch.empty(max(1, lib.libra_attn_bwd_workspace(plan0.host)), dtype=torch.uint8, device=dev)
@@ -740,6 +783,9 @@ def main():
     ap.add_argument("--cost", choices=("executed", "pairs"), default="executed",
                     help="forward / dQ item cost: executed query-key slots or eq. 8 pairs")
     ap.add_argument("--item-overhead", type=int, default=0, help="cost added to every work item")
+    ap.add_argument("--tau", type=float, default=0.03, help="soft-target slack of Algorithm 2")
+    ap.add_argument("--cpu-oracle-full", action="store_true",
+                    help="time the complete fp64 forward oracle on the 2K, 32K and uniform 128K packs (host only)")
     ap.add_argument("--ab", nargs="+", metavar="WORKLOAD",
                     help="plan variants side by side (executed vs pair cost, L2 term) on these workloads")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward only")
@@ -777,6 +823,9 @@ def main():
     if args.vrsp:
         vrsp_report()
         return
+    if args.cpu_oracle_full:
+        cpu_oracle_full()
+        return
     if args.simulate:
         simulate()
         return
@@ -797,7 +846,7 @@ def main():
     out = measure(args.workload, args.seed, args.assign, args.fwd_only, args.steps, args.warmup,
                   not args.no_cpu_baseline, args.calibrate_copy, dump_records=args.dump_records,
                   speed_calibration=not args.no_speed_calibration, cost=("executed", "pairs").index(args.cost),
-                  item_overhead=args.item_overhead)
+                  item_overhead=args.item_overhead, tau=args.tau)
     print(json.dumps(out), flush=True)
 
 

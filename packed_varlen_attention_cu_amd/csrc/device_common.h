@@ -177,6 +177,23 @@ __device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0
 // for the next block stay in flight across the barrier.
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Rows of a block sit in LDS permuted within each group of 16: logical row x
+// is stored at physical row lds_row(x), which swaps the two 2-bit fields of
+// x mod 16 (an involution).  With a row stride of an odd number of 16-byte
+// chunks, both operand read patterns are then free of bank conflicts:
+//   - a 16-byte direct read serves 16 lanes reading 16 rows of one 16-row
+//     group at one column: any permutation of the group keeps their chunks
+//     on 16 distinct groups of four banks;
+//   - a transposing read serves 32 lanes reading four consecutive logical
+//     rows 4i .. 4i + 3 of a group, 64 bytes each: they are stored at rows
+//     i, i + 4, i + 8, i + 12, whose starting banks lie 16 dwords apart for
+//     every odd chunk stride, so the four 64-byte pieces cover the 64 banks.
+// The copy into LDS fills physical row R with logical row lds_row(R); every
+// read offset stays a per-lane constant plus a compile-time immediate.
+__device__ __forceinline__ constexpr int lds_row(int x) {
+  return (x & ~15) | ((x & 3) << 2) | ((x >> 2) & 3);
+}
+
 // Row m of a 32-row C tile produced from A rows loaded in the order sigma:
 // sigma swaps bits 2 and 3, so C registers 8t..8t+7 of lane half h hold
 // A rows 16t + 8h + 0..7 (contiguous), ready to be a B operand.
@@ -193,21 +210,14 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
       (__attribute__((address_space(3))) s16x4 *)(const __attribute__((address_space(3))) void *)p);
 }
 
-// Row-major bf16 blocks of D columns live in LDS with a padded row stride.
-// The LDS has 64 four-byte banks.  A 16-byte read serves 16 lanes per cycle
-// (here 16 rows at one column), an 8-byte transposing read 32 lanes (here 4
-// rows x 64 bytes).  The first is conflict-free when the stride in 16-byte
-// units is odd, the second when the stride is an odd multiple of 64 bytes;
-// no stride is both, so each block takes the stride of the reads it serves:
-//   kStride       = 152 elements (D = 128) or 72 (D = 64): blocks read both ways
-//                   (direct reads conflict-free, transposing reads one extra
-//                   cycle in two);
-//   kDirectStride = 136 (D = 128) or 72 (D = 64): blocks read only directly,
-//                   the shortest conflict-free rows (17 copy instructions per
-//                   64-row block instead of 19).
-// Blocks read only through transposing reads would be conflict-free at 160
-// (D = 128); the kernels pick strides so that the copies of a block pair
-// divide evenly among their waves (PairCopy) instead.
+// Row-major bf16 blocks of D columns live in LDS with a padded row stride of
+// an odd number of 16-byte chunks; with the row permutation lds_row, direct
+// and transposing operand reads are then both free of bank conflicts.  The
+// kernels pick among such strides so that the copies of a block pair divide
+// evenly among their waves (PairCopy):
+//   kStride       = 152 elements (19 chunks; D = 128) or 72 (9; D = 64);
+//   kDirectStride = 136 (17 chunks; D = 128) or 72 (D = 64), the shortest
+//                   (17 copy instructions per 64-row block instead of 19).
 // Every operand address stays a per-lane base plus a compile-time offset.
 template <int D>
 struct PadRows {
@@ -246,9 +256,9 @@ struct PairCopy {
       const bool in_a = g < NA;
       const int rs = in_a ? RA : RB;
       const int e = 512 * (in_a ? g : g - NA) + 8 * lane;   // element offset of the lane's slot
-      const int row = e / rs, c = e - row * rs;
+      const int row = e / rs, c = e - row * rs;             // physical row of the slot
       const int col = c < D ? c : 0;
-      voff[j] = g < NI ? (uint32_t)(2 * ((int64_t)row * stride + col)) : 0u;
+      voff[j] = g < NI ? (uint32_t)(2 * ((int64_t)lds_row(row) * stride + col)) : 0u;
     }
   }
   // Rows r0 .. r0 + NR - 1 of both tensors; rows at or past `rows` (only in
@@ -287,30 +297,32 @@ struct PairCopy {
   }
 };
 
-// Direct A operand: lane (col, half) reads row sigma_row(col) + 32 t of the
-// block, reduction elements 16 s + 8 half .. + 7.  direct_lane_off is the
-// lane's part; slab (t, s) adds direct_off(t, s).
+// Direct A operand: lane (col, half) reads logical row sigma_row(col) + 32 t
+// of the block, reduction elements 16 s + 8 half .. + 7.  direct_lane_off is
+// the lane's part (its physical row); slab (t, s) adds direct_off(t, s).
 template <int RS>
 __device__ __forceinline__ int direct_lane_off(int lane) {
-  return sigma_row(lane & 31) * RS + 8 * (lane >> 5);
+  return lds_row(sigma_row(lane & 31)) * RS + 8 * (lane >> 5);
 }
 template <int RS>
 constexpr int direct_off(int t, int s) { return 32 * t * RS + 16 * s; }
 
 // MFMA A operand of Mat^T from a row-major padded block Mat [rows][D] in LDS:
 // lane (col, half) receives Mat[k0 + 8 half + i][r0 + col], i = 0..7.  Lane j
-// of 16-lane group g addresses row k0 + 8 (g >> 1) + 4 p + j / 4, columns
-// r0 + 16 (g & 1) + 4 (j % 4) + 0..3, for the two reads p = 0, 1; by the rule
-// of the transposing read the group's lane i then holds rows
-// k0 + 8 (g >> 1) + 4 p + 0..3 of column r0 + 16 (g & 1) + i.  tr_lane_off is
-// the lane's part; (k0, r0, p) add tr_off(k0, r0, p).
+// of 16-lane group g addresses logical row k0 + 8 (g >> 1) + 4 p + j / 4,
+// columns r0 + 16 (g & 1) + 4 (j % 4) + 0..3, for the two reads p = 0, 1; by
+// the rule of the transposing read the group's lane i then holds rows
+// k0 + 8 (g >> 1) + 4 p + 0..3 of column r0 + 16 (g & 1) + i.  With k0 a
+// multiple of 16 that logical row sits at physical row
+// k0 + 4 (j / 4) + 2 (g >> 1) + p (lds_row); tr_lane_off is the lane's part,
+// (k0, r0, p) add tr_off(k0, r0, p).
 template <int RS>
 __device__ __forceinline__ int tr_lane_off(int lane) {
   const int g = lane >> 4, j = lane & 15;
-  return (8 * (g >> 1) + (j >> 2)) * RS + 16 * (g & 1) + 4 * (j & 3);
+  return (4 * (j >> 2) + 2 * (g >> 1)) * RS + 16 * (g & 1) + 4 * (j & 3);
 }
 template <int RS>
-constexpr int tr_off(int k0, int r0, int p) { return (k0 + 4 * p) * RS + r0; }
+constexpr int tr_off(int k0, int r0, int p) { return (k0 + p) * RS + r0; }
 
 __device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t *lo_p, const uint16_t *hi_p) {
   const s16x4 lo = lds_read_tr16(lo_p), hi = lds_read_tr16(hi_p);
