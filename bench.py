@@ -9,6 +9,8 @@ timing starts.  Throughput counts only unmasked causal pairs:
 FLOPs_fwd = 4 d h_q sum_j l_j (l_j + 1) / 2, FLOPs_bwd = 2.5 FLOPs_fwd.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+After the train_256k step the same line reports the forward of the 1M-token head share
+(L = 1048576, 8 Q / 1 KV heads, one 600000-token sample plus filler) as "fwd_share_1m".
 """
 from __future__ import annotations
 
@@ -784,6 +786,8 @@ def main():
                     help="forward / dQ item cost: executed query-key slots or eq. 8 pairs")
     ap.add_argument("--item-overhead", type=int, default=0, help="cost added to every work item")
     ap.add_argument("--tau", type=float, default=0.03, help="soft-target slack of Algorithm 2")
+    ap.add_argument("--no-share-1m", action="store_true",
+                    help="skip the forward of the 1M-token head share that follows the train_256k step")
     ap.add_argument("--cpu-oracle-full", action="store_true",
                     help="time the complete fp64 forward oracle on the 2K, 32K and uniform 128K packs (host only)")
     ap.add_argument("--ab", nargs="+", metavar="WORKLOAD",
@@ -847,6 +851,16 @@ def main():
                   not args.no_cpu_baseline, args.calibrate_copy, dump_records=args.dump_records,
                   speed_calibration=not args.no_speed_calibration, cost=("executed", "pairs").index(args.cost),
                   item_overhead=args.item_overhead, tau=args.tau)
+    if args.workload == "train_256k" and not args.no_share_1m:
+        # The other configuration the forward target names: the 1M-token head share, forward only.
+        s1 = measure("share_1m", args.seed, args.assign, True, 5, 2, False, quiet=True,
+                     cost=("executed", "pairs").index(args.cost), item_overhead=args.item_overhead, tau=args.tau)
+        c = s1["config"]
+        out["fwd_share_1m"] = {"tflops": s1["fwd_tflops"], "frac_peak": s1["fwd_frac_peak"],
+                               "fwd_ms": round(s1["kernel_ms"]["fwd"], 3), "steps": 5,
+                               "cu_busy_max_over_mean": s1["cu_busy_max_over_mean"]["fwd"],
+                               "config": {k: c[k] for k in ("total_tokens", "h_q", "h_kv", "head_dim", "sh_tile",
+                                                             "samples", "max_sample")}}
     print(json.dumps(out), flush=True)
 
 
