@@ -851,7 +851,7 @@ def main():
                   not args.no_cpu_baseline, args.calibrate_copy, dump_records=args.dump_records,
                   speed_calibration=not args.no_speed_calibration, cost=("executed", "pairs").index(args.cost),
                   item_overhead=args.item_overhead, tau=args.tau)
-    if args.workload == "train_256k" and not args.no_share_1m:
+    if args.workload == "train_256k" and not args.fwd_only and not args.no_share_1m:
         # The other configuration the forward target names: the 1M-token head share, forward only.
         s1 = measure("share_1m", args.seed, args.assign, True, 5, 2, False, quiet=True,
                      cost=("executed", "pairs").index(args.cost), item_overhead=args.item_overhead, tau=args.tau)

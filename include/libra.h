@@ -26,13 +26,18 @@
  *     given (a hipStream_t passed as void*; NULL is the default stream).
  *   - Every argument is validated on the host before anything is enqueued;
  *     a failed check returns a negative libra_status and enqueues nothing.
- *     A launch error returns LIBRA_EHIP.  Faults inside kernels surface at
- *     the caller's next synchronisation.
+ *     Launches verify the whole host plan (magic, version, section bounds,
+ *     checksum over all its bytes; the plan's extent is the size its header
+ *     records).  A launch error returns LIBRA_EHIP.  Faults inside kernels
+ *     surface at the caller's next synchronisation.
  *   - A plan is a pure function of (cu_seqlens, libra_plan_params); one plan
  *     serves every layer with the same packing (Libra paper, section 4.1:
  *     the assignment is reused across layers with the same layout).  The
  *     device copy of a plan is a byte copy of the host buffer, uploaded by
- *     the caller.
+ *     the caller, at least as long as the plan.  The kernels compare its
+ *     checksum field with the host plan's before reading any queue; on a
+ *     mismatch they run no item and set LIBRA_RECORD_PLAN_MISMATCH in their
+ *     records (when records are given): the outputs are then left unwritten.
  */
 #ifndef LIBRA_H
 #define LIBRA_H

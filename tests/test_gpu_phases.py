@@ -8,7 +8,13 @@ import pytest
 import synth
 from tests import _support as S
 
-pytestmark = pytest.mark.gpu
+
+def _has_gpu():
+    import torch
+    return torch.cuda.is_available()
+
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not _has_gpu(), reason="no GPU")]
 
 
 def test_phases_match_one_call_entry_points():
@@ -50,3 +56,40 @@ def test_phases_match_one_call_entry_points():
     assert int(r[1]["n_items"].sum()) == plan.info.n_kv_items
     assert int(r[2]["n_items"].sum()) == plan.info.n_dq_items
     assert (r["t_end"] >= r["t_start"]).all()
+
+
+def test_device_plan_from_another_plan_runs_nothing():
+    """A device plan copied from a different plan (another packing) has another checksum: every
+    workgroup of the forward and backward kernels sees the mismatch, runs no item and flags its
+    record; the outputs keep what they held.  The kernels read only the checksum field of the
+    foreign copy, which any plan buffer holds."""
+    import torch
+    import packed_varlen_attention_cu_amd as lib
+    w = synth.WORKLOADS["train_256k"].with_tokens(3000)
+    cu_a = synth.cu_seqlens(synth.make_lengths(w, 0))
+    cu_b = synth.cu_seqlens(synth.make_lengths(w, 1))
+    plan_a, plan_b = S.make_plan(w, cu_a), S.make_plan(w, cu_b)
+    assert plan_a.info.checksum != plan_b.info.checksum
+    t = synth.make_tensors(w, 0, names=("q", "k", "v", "dout"))
+    q, k, v, do = (S.to_dev(t[n]) for n in ("q", "k", "v", "dout"))
+    dev = q.device
+    dev_b, cu_dev = plan_b.device(dev)[0], plan_a.device(dev)[1]
+    ncu = plan_a.info.num_cus
+    rec = torch.zeros(3 * ncu * lib.RECORD_DTYPE.itemsize, dtype=torch.uint8, device=dev)
+    o = torch.full_like(q, 7.0)
+    lse = torch.full((w.h_q, w.total_tokens), 7.0, dtype=torch.float32, device=dev)
+    stream = lib._stream_handle(dev)
+    S.say("[guard] forward with a foreign device plan")
+    lib.libra_attn_fwd(plan_a.host, dev_b, q, k, v, cu_dev, o, lse, S.scale_of(w), rec[:ncu * 32], stream)
+    dq, dk, dv = (torch.full_like(x, 7.0) for x in (q, k, v))
+    ws_bytes = lib.libra_attn_bwd_workspace(plan_a.host)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    S.say("[guard] backward with a foreign device plan")
+    lib.libra_attn_bwd(plan_a.host, dev_b, q, k, v, o, do, lse, cu_dev, dq, dk, dv, S.scale_of(w), ws, ws_bytes,
+                       rec[ncu * 32:], stream)
+    torch.cuda.synchronize()
+    r = rec.cpu().numpy().view(lib.RECORD_DTYPE)
+    assert (r["flags"] == lib.RECORD_PLAN_MISMATCH).all() and (r["n_items"] == 0).all()
+    for x in (o, dq, dk, dv):
+        assert (x.float() == 7.0).all().item()
+    assert (lse == 7.0).all().item()
