@@ -559,7 +559,7 @@ def _make_inputs(workload, seed, names):
 
 def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, warmup=2, cpu=True,
             calibrate_copy=0, quiet=False, tiling=None, dump_records=None, speed_calibration=True,
-            cost=0, item_overhead=0, tau=0.03):
+            cost=0, item_overhead=0, tau=0.03, num_cus=0):
     """Time `steps` steps of the hot path on cuda:0; returns the JSON record.  `tiling`
     = (tile_tokens, tile_heads) replaces the workload's SH-Tile shape."""
     import torch
@@ -586,7 +586,8 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
 
     tile_tokens, tile_heads = tiling if tiling else (w.tile_tokens, w.tile_heads)
     plan_kw = dict(total_tokens=L, h_q=w.h_q, h_kv=w.h_kv, head_dim=d, tile_tokens=tile_tokens,
-                   tile_heads=tile_heads, assign=assign, cost=cost, item_overhead=item_overhead, tau=tau)
+                   tile_heads=tile_heads, assign=assign, cost=cost, item_overhead=item_overhead, tau=tau,
+                   num_cus=num_cus)
     plan0 = lib.Plan(cu, **plan_kw)
     ncu = plan0.info.num_cus
     ws_b = torch.empty(max(1, lib.libra_attn_bwd_workspace(plan0.host)), dtype=torch.uint8, device=dev)
@@ -699,10 +700,10 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
             if n.startswith("bwd") and not do_bwd:
                 continue
             rec_ = rr.view(lib_.RECORD_DTYPE)[:ncu]
-            cost = its["cost"].astype(np.int64)
+            item_cost = its["cost"].astype(np.int64)
             out_[n] = [{"w": w_, "xcc": int(rec_["xcc_id"][w_]), "hw": int(rec_["hw_id"][w_]),
                         "busy": int(rec_["t_end"][w_] - rec_["t_start"][w_]), "n_items": int(rec_["n_items"][w_]),
-                        "planned": int(cost[off[w_]:off[w_ + 1]].sum()),
+                        "planned": int(item_cost[off[w_]:off[w_ + 1]].sum()),
                         "items": [int(x) for x in its["id"][off[w_]:off[w_ + 1]]]}
                        for w_ in range(ncu)]
         with open(dump_records, "w") as f:
@@ -786,6 +787,8 @@ def main():
                     help="forward / dQ item cost: executed query-key slots or eq. 8 pairs")
     ap.add_argument("--item-overhead", type=int, default=0, help="cost added to every work item")
     ap.add_argument("--tau", type=float, default=0.03, help="soft-target slack of Algorithm 2")
+    ap.add_argument("--num-cus", type=int, default=0,
+                    help="workers (persistent workgroups) the plan places on; 0: one per CU (256)")
     ap.add_argument("--no-share-1m", action="store_true",
                     help="skip the forward of the 1M-token head share that follows the train_256k step")
     ap.add_argument("--cpu-oracle-full", action="store_true",
@@ -850,7 +853,7 @@ def main():
     out = measure(args.workload, args.seed, args.assign, args.fwd_only, args.steps, args.warmup,
                   not args.no_cpu_baseline, args.calibrate_copy, dump_records=args.dump_records,
                   speed_calibration=not args.no_speed_calibration, cost=("executed", "pairs").index(args.cost),
-                  item_overhead=args.item_overhead, tau=args.tau)
+                  item_overhead=args.item_overhead, tau=args.tau, num_cus=args.num_cus)
     if args.workload == "train_256k" and not args.fwd_only and not args.no_share_1m:
         # The other configuration the forward target names: the 1M-token head share, forward only.
         s1 = measure("share_1m", args.seed, args.assign, True, 5, 2, False, quiet=True,
