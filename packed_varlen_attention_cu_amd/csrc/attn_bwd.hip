@@ -95,8 +95,9 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int w = blockIdx.x;
   const uint64_t t_start = wall_clock64();
   // A device plan that is not a copy of the host plan runs no item.
-  const bool plan_ok = *a.plan_sum_dev == a.plan_sum;
-  const int beg = plan_ok ? a.cu_off[w] : 0, end = plan_ok ? a.cu_off[w + 1] : 0;
+  const bool plan_ok = as_const(a.plan_sum_dev)[0] == a.plan_sum;
+  const int beg = plan_ok ? as_const(a.cu_off)[w] : 0, end = plan_ok ? as_const(a.cu_off)[w + 1] : 0;
+  const cptr<int32_t> cu = as_const(a.cu);
   const float c = a.scale_log2;
   const uint32_t q_base = lds_addr(q_lds);
   u32x4 *p_mine = reinterpret_cast<u32x4 *>(p_lds + kg * 32 * kQB) + lane;   // [4 slabs][64 lanes]
@@ -122,23 +123,23 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
     const int dlo = direct_lane_off<RA>(lane);
     const int tlo = tr_lane_off<RT>(lane);
     for (int it = beg; it < end; ++it) {
-      const libra_item item = a.items[it];
+      const libra_item item = load_item(a.items, it);
       const int row0 = item.row0, nrows = item.nrows, kvh = item.kv_head;
       const int kloc = kg * 32 + col;
       const bool kok = kloc < nrows;
       const int key = row0 + kloc;
-      const int kend = kok ? segment_end(a.cu, a.n_samples, key) : 0;   // queries [key, kend)
-
-      // B operand of this wave's first product: K (P wave) or V (dS wave).
-      bf16x8 bop[NS];
-      {
-        const uint16_t *src = (pwave ? a.k : a.v) + ((int64_t)key * a.h_kv + kvh) * D + 8 * half;
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-          bop[s] = as_bf16x8(kok ? *reinterpret_cast<const u32x4 *>(src + 16 * s) : zero_u32x4());
+      // End of each key's sample, queries [key, kend) (scalar loads only).
+      int kend = 0;
+      if (kg * 32 < nrows) {
+        int st, en;
+        lane_sample(cu, a.n_samples, row0 + kg * 32, row0 + min(nrows, kg * 32 + 32) - 1, key, st, en);
+        if (kok) kend = en;
       }
+      // B operand of this wave's first product: K (P wave) or V (dS wave),
+      // loaded once the previous item's buffers are free.
+      bf16x8 bop[NS];
       const int qstart = row0 & ~(kQB - 1);
-      const int qend = segment_end(a.cu, a.n_samples, row0 + nrows - 1);
+      const int qend = cu[sample_index(cu, a.n_samples, row0 + nrows - 1) + 1];
       const int nqb = (qend - qstart + kQB - 1) / kQB;
       const int nsteps = nqb * item.nheads;
 
@@ -301,14 +302,24 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
         }
       };
 
-      wait_vmem_lds();
+      // The previous item's dK / dV stores may still fly while this item's
+      // loads and first copies are issued; one wait then covers all of them
+      // (and tells the compiler that the operand registers are loaded).
+      wait_lds();
       block_barrier();              // the previous item's reads of every buffer and of P are done
+      {
+        const uint16_t *src = (pwave ? a.k : a.v) + ((int64_t)key * a.h_kv + kvh) * D + 8 * half;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+          bop[s] = as_bf16x8(kok ? *reinterpret_cast<const u32x4 *>(src + 16 * s) : zero_u32x4());
+      }
 #pragma unroll
       for (int i = 0; i < kStages - 1; ++i)
         if (i < nsteps) {
           issue(nh, nq0, i);
           advance(nh, nq0);
         }
+      wait_vmem<0>();
       for (int i = 0, buf = 0; i < nsteps; ++i, buf = buf == kStages - 1 ? 0 : buf + 1) step(i, buf);
 
       if (kok) {

@@ -69,8 +69,9 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const int w = blockIdx.x;
   const uint64_t t_start = wall_clock64();
   // A device plan that is not a copy of the host plan runs no item.
-  const bool plan_ok = *a.plan_sum_dev == a.plan_sum;
-  const int beg = plan_ok ? a.cu_off[w] : 0, end = plan_ok ? a.cu_off[w + 1] : 0;
+  const bool plan_ok = as_const(a.plan_sum_dev)[0] == a.plan_sum;
+  const int beg = plan_ok ? as_const(a.cu_off)[w] : 0, end = plan_ok ? as_const(a.cu_off)[w + 1] : 0;
+  const cptr<int32_t> cu = as_const(a.cu);
   const float c = a.scale_log2;
   const uint32_t kv_base = lds_addr(kv_lds);
   const int dlo = direct_lane_off<RS>(lane);       // K operand reads
@@ -82,27 +83,45 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   KVCopy kvcopy;
   kvcopy.init(wave, lane, kv_stride);
 
+  // Operands of the wave's query of item itq: Q and dO rows, LSE * log2(e)
+  // and D.  Each item's are loaded as soon as the previous item's last block
+  // is done, before that item's dQ is stored, so their latency overlaps the
+  // stores, the next item's set-up and the item-start barrier.
+  float lse2, dd;
+  bf16x8 qop[NS], dop[NS];
+  auto load_rows = [&](int itq) {
+    const libra_item nx = load_item(a.items, itq);
+    const int nhx = nx.nheads, hx = nx.head0 + (wave % nhx);
+    const int rx = (wave / nhx) * 32 + col;
+    const bool okx = rx < nx.nrows;
+    const int px = nx.row0 + rx;
+    lse2 = okx ? a.lse2[(int64_t)hx * a.L + px] : 0.0f;
+    dd = okx ? a.dvec[(int64_t)hx * a.L + px] : 0.0f;
+    const int64_t base = ((int64_t)px * a.h_q + hx) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qop[s] = as_bf16x8(okx ? *reinterpret_cast<const u32x4 *>(a.q + base + 16 * s) : zero_u32x4());
+      dop[s] = as_bf16x8(okx ? *reinterpret_cast<const u32x4 *>(a.dout + base + 16 * s) : zero_u32x4());
+    }
+  };
+
   for (int it = beg; it < end; ++it) {
-    const libra_item item = a.items[it];
+    const libra_item item = load_item(a.items, it);
+    if (it == beg) load_rows(it);
     const int row0 = item.row0, nrows = item.nrows, kvh = item.kv_head, nh = item.nheads;
     const int head = item.head0 + (wave % nh);
     const int sub = wave / nh;
     const int r = sub * 32 + col;
     const bool qok = r < nrows;
     const int qpos = row0 + r;
-    const int qss = qok ? segment_start(a.cu, a.n_samples, qpos) : 0;
-    const float lse2 = qok ? a.lse2[(int64_t)head * a.L + qpos] : 0.0f;
-    const float dd = qok ? a.dvec[(int64_t)head * a.L + qpos] : 0.0f;
-    bf16x8 qop[NS], dop[NS];
-    {
-      const int64_t base = ((int64_t)qpos * a.h_q + head) * D + 8 * half;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        qop[s] = as_bf16x8(qok ? *reinterpret_cast<const u32x4 *>(a.q + base + 16 * s) : zero_u32x4());
-        dop[s] = as_bf16x8(qok ? *reinterpret_cast<const u32x4 *>(a.dout + base + 16 * s) : zero_u32x4());
-      }
+    // Sample start of each query of the wave (scalar loads only).
+    int qss = 0;
+    if (sub * 32 < nrows) {
+      int st, en;
+      lane_sample(cu, a.n_samples, row0 + sub * 32, row0 + min(nrows, sub * 32 + 32) - 1, qpos, st, en);
+      if (qok) qss = st;
     }
-    const int kstart = segment_start(a.cu, a.n_samples, row0) & ~(kKB - 1);
+    const int kstart = cu[sample_index(cu, a.n_samples, row0)] & ~(kKB - 1);
     const int kend = row0 + nrows;
     const int nkb = (kend - kstart + kKB - 1) / kKB;
     // Step b's key block: up from the sample start, or (LIBRA_ITEM_REVERSE,
@@ -190,12 +209,19 @@ void attn_bwd_dq_kernel(BwdArgs a) {
       }
     };
 
-    wait_vmem_lds();
+    wait_lds();
     block_barrier();                // the previous item's reads of every buffer are done
+    // This item's operands and the previous item's dQ stores have been in
+    // flight since the previous item's last block: one full wait for them
+    // here, before the first copies, costs little and tells the compiler that
+    // the operand registers are loaded (it cannot see that the per-block copy
+    // waits cover them, and would otherwise wait for every copy at every block).
+    wait_vmem<0>();
 #pragma unroll
     for (int b = 0; b < kStages - 1; ++b)
       if (b < nkb) issue(kblock(b), b);
     for (int b = 0, buf = 0; b < nkb; ++b, buf = buf == kStages - 1 ? 0 : buf + 1) block(b, buf);
+    if (it + 1 < end) load_rows(it + 1);
 
     if (qok) {
       uint16_t *op = a.dq + ((int64_t)qpos * a.h_q + head) * D;

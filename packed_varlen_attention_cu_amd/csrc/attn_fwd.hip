@@ -100,8 +100,9 @@ void attn_fwd_kernel(FwdArgs a) {
   const int w = blockIdx.x;
   const uint64_t t_start = wall_clock64();
   // A device plan that is not a copy of the host plan runs no item.
-  const bool plan_ok = *a.plan_sum_dev == a.plan_sum;
-  const int beg = plan_ok ? a.cu_off[w] : 0, end = plan_ok ? a.cu_off[w + 1] : 0;
+  const bool plan_ok = as_const(a.plan_sum_dev)[0] == a.plan_sum;
+  const int beg = plan_ok ? as_const(a.cu_off)[w] : 0, end = plan_ok ? as_const(a.cu_off)[w + 1] : 0;
+  const cptr<int32_t> cu = as_const(a.cu);
   const float sl2 = a.scale_log2;
   const uint32_t kv_base = lds_addr(kv_lds);
   const float NEG_INF = -__builtin_inff();
@@ -118,29 +119,51 @@ void attn_fwd_kernel(FwdArgs a) {
   uint32_t counted = 0;   // unmasked (query, key) slots this lane computed
 #endif
 
+  // Q operands of the wave's queries of item itq.  Each item's Q is loaded
+  // as soon as the previous item's last block is done, before that item's
+  // output is normalised and stored, so its latency overlaps the output
+  // stores, the next item's set-up and the item-start barrier.
+  bf16x8 qop[QT][NS];
+  auto load_q = [&](int itq) {
+    const libra_item nx = load_item(a.items, itq);
+    const int nhx = nx.nheads, hx = nx.head0 + (wave % nhx), subx = wave / nhx;
+    const int r0x = nx.row0 + subx * QW, nrx = min(QW, nx.nrows - subx * QW);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int r = qt * 32 + col;
+      const bool ok = r < nrx;
+      const uint16_t *qp = a.q + ((int64_t)(r0x + r) * a.h_q + hx) * D + 8 * half;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        qop[qt][s] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(qp + 16 * s) : zero_u32x4());
+    }
+  };
+
   for (int it = beg; it < end; ++it) {
-    const libra_item item = a.items[it];
+    const libra_item item = load_item(a.items, it);
+    if (it == beg) load_q(it);
     const int row0 = item.row0, nrows = item.nrows, kvh = item.kv_head, nh = item.nheads;
     const int head = item.head0 + (wave % nh);
     const int sub = wave / nh;
     const int wrow0 = row0 + sub * QW;
     const int wrows = min(QW, nrows - sub * QW);
 
+    // Sample start of each query of the wave (scalar loads only).
     int qpos[QT], qss[QT];
     bool qok[QT];
-    bf16x8 qop[QT][NS];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const int r = qt * 32 + col;
       qok[qt] = r < wrows;
       qpos[qt] = wrow0 + r;
-      qss[qt] = qok[qt] ? segment_start(a.cu, a.n_samples, qpos[qt]) : 0;
-      const uint16_t *qp = a.q + ((int64_t)qpos[qt] * a.h_q + head) * D + 8 * half;
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        qop[qt][s] = as_bf16x8(qok[qt] ? *reinterpret_cast<const u32x4 *>(qp + 16 * s) : zero_u32x4());
+      qss[qt] = 0;
+      if (wrows > 0) {
+        int st, en;
+        lane_sample(cu, a.n_samples, wrow0, wrow0 + wrows - 1, qpos[qt], st, en);
+        if (qok[qt]) qss[qt] = st;
+      }
     }
-    const int kstart = segment_start(a.cu, a.n_samples, row0) & ~(kBN - 1);
+    const int kstart = cu[sample_index(cu, a.n_samples, row0)] & ~(kBN - 1);
     const int kend = row0 + nrows;
     const int nblk = (kend - kstart + kBN - 1) / kBN;
     // Step b's key block: up from the sample start, or (LIBRA_ITEM_REVERSE,
@@ -315,12 +338,19 @@ void attn_fwd_kernel(FwdArgs a) {
       }
     };
 
-    wait_vmem_lds();
+    wait_lds();
     block_barrier();                // the previous item's reads of every buffer are done
+    // This item's Q and the previous item's output stores have been in flight
+    // since the previous item's last block: one full wait for them here,
+    // before the first copies, costs little and tells the compiler that the
+    // Q registers are loaded (it cannot see that the per-block copy waits
+    // cover them, and would otherwise wait for every copy at every block).
+    wait_vmem<0>();
 #pragma unroll
     for (int b = 0; b < kStages - 1; ++b)
       if (b < nblk) issue(kblock(b), b);
     for (int b = 0, buf = 0; b < nblk; ++b, buf = buf == kStages - 1 ? 0 : buf + 1) block(b, buf);
+    if (it + 1 < end) load_q(it + 1);
 
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {

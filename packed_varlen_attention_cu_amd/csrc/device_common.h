@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "libra.h"
+
 namespace libra {
 
 typedef __bf16 bf16_t;
@@ -70,24 +72,69 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0; }
 
-// Start of the sample that contains token q: the largest cu[j] <= q, j < n.
-__device__ __forceinline__ int segment_start(const int32_t *__restrict__ cu, int n, int q) {
-  int lo = 0, hi = n;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= q) lo = mid; else hi = mid;
-  }
-  return cu[lo];
+// Plan arrays and cu_seqlens are never written while a kernel runs, so the
+// kernels read them through the constant address space: wave-uniform reads
+// then compile to scalar loads.  Those are counted apart from vector memory
+// operations, so an item's set-up (descriptor, sample bounds) does not wait
+// behind the vector memory queue that still holds the previous item's output
+// stores, as vector loads would.
+template <typename T>
+using cptr = const __attribute__((address_space(4))) T *;
+template <typename T>
+__device__ __forceinline__ cptr<T> as_const(const T *p) { return (cptr<T>)p; }
+
+// Work item it of a plan queue (wave-uniform it), read field by field through
+// the constant address space.  The kernels do not use the placement fields
+// (cost, pairs), which are left zero.
+__device__ __forceinline__ libra_item load_item(const libra_item *items, int it) {
+  static_assert(sizeof(libra_item) % 4 == 0, "32-bit fields");
+  const cptr<int32_t> f = as_const(reinterpret_cast<const int32_t *>(items + it));
+  libra_item r;
+  r.row0 = f[offsetof(libra_item, row0) / 4];
+  r.nrows = f[offsetof(libra_item, nrows) / 4];
+  r.kv_head = f[offsetof(libra_item, kv_head) / 4];
+  r.head0 = f[offsetof(libra_item, head0) / 4];
+  r.nheads = f[offsetof(libra_item, nheads) / 4];
+  r.tile_id = f[offsetof(libra_item, tile_id) / 4];
+  r.id = f[offsetof(libra_item, id) / 4];
+  r.flags = f[offsetof(libra_item, flags) / 4];
+  r.cost = 0;
+  r.pairs = 0;
+  return r;
 }
 
-// End of the sample that contains token k: the smallest cu[j] > k, j <= n.
-__device__ __forceinline__ int segment_end(const int32_t *__restrict__ cu, int n, int k) {
-  int lo = 0, hi = n;   // cu[lo] <= k < cu[hi]
+// Index of the sample that holds token t, for a wave-uniform t < cu[n]: the
+// largest j < n with cu[j] <= t (so empty samples are passed over).  A binary
+// search over cu_seqlens with scalar loads.
+__device__ __forceinline__ int sample_index(cptr<int32_t> cu, int n, int t) {
+  int lo = 0, hi = n;   // cu[lo] <= t < cu[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= k) lo = mid; else hi = mid;
+    if (cu[mid] <= t) lo = mid; else hi = mid;
   }
-  return cu[hi];
+  return lo;
+}
+
+// Bounds [start, end) of the sample that holds this lane's token q, where the
+// tokens of the wave lie in the wave-uniform range [t0, t1], t1 < cu[n].  The
+// samples that begin inside the range are walked in order with scalar loads
+// and each lane keeps the last one that starts at or before q; lanes whose q
+// lies outside the range get meaningless bounds.
+__device__ __forceinline__ void lane_sample(cptr<int32_t> cu, int n, int t0, int t1, int q,
+                                            int &start, int &end) {
+  int j = sample_index(cu, n, t0);
+  int s = cu[j], e = cu[j + 1];
+  start = s;
+  end = e;
+  while (e <= t1) {   // sample j + 1 begins inside the range; e <= t1 < cu[n] gives j + 1 < n
+    ++j;
+    s = e;
+    e = cu[j + 1];
+    if (q >= s) {
+      start = s;
+      end = e;
+    }
+  }
 }
 
 // Physical placement of the running wave, for per-CU busy records.
