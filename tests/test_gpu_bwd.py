@@ -95,7 +95,7 @@ def test_bwd_extreme_logits(lib, kind):
         S.check_grad(S.from_dev_bf16(g), r, f"{kind} {name_g}", g_bf16=y)
 
 
-@pytest.mark.parametrize("lens", [[1] * 200, [0, 3, 0, 140, 1, 0, 70], [64], [65, 63, 2, 129]])
+@pytest.mark.parametrize("lens", [[1] * 200, [0, 3, 0, 140, 1, 0, 70], [64], [65, 63, 2, 129], [0, 2, 33, 0, 0]])
 def test_bwd_edge_packs(lib, lens):
     import oracle.attention as A
     L = sum(lens)

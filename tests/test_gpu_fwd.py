@@ -71,6 +71,7 @@ def test_fwd_small_full(lib, name, L, first, kw):
     [1],                             # one token
     [64],                            # exactly one key block
     [63, 65, 1, 127, 2],             # ragged around block edges
+    [0, 0, 33, 1, 0, 0],             # empty samples first and last
 ])
 def test_fwd_edge_packs(lib, lens):
     L = sum(lens)
