@@ -719,7 +719,12 @@ def measure(workload="train_256k", seed=0, assign=0, fwd_only=False, steps=10, w
         for n, rr in (("fwd", r[:ncu * 32]), ("bwd_dkdv", r[ncu * 32:2 * ncu * 32]), ("bwd_dq", r[2 * ncu * 32:])):
             if n.startswith("bwd") and not do_bwd:
                 continue
-            ratio, _ = cu_busy_ratio(rr.cpu().numpy(), ncu)
+            raw = rr.cpu().numpy()
+            flags = raw.view(lib.RECORD_DTYPE)[:ncu]["flags"]
+            if (flags != 0).any():
+                raise RuntimeError(f"{n}: per-CU records flag {sorted(set(int(x) for x in flags if x))} "
+                                   "(plan mismatch or an expired wait): the step's results are not valid")
+            ratio, _ = cu_busy_ratio(raw, ncu)
             busy[n].append(ratio)
     ms_step = wall / steps * 1e3
     pairs = causal_pairs(cu) * w.h_q

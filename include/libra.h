@@ -194,8 +194,12 @@ typedef struct {
  * constant-rate device clock (libra_device_clock_khz).  flags holds
  * LIBRA_RECORD_PLAN_MISMATCH when the workgroup found that the device copy
  * of the plan is not a copy of the host plan it was launched with (its
- * checksum differs) and therefore ran no item. */
+ * checksum differs) and therefore ran no item.  In the dK/dV pass it holds
+ * LIBRA_RECORD_WAIT_EXPIRED when a wave's bounded wait for the P tile of its
+ * partner wave ran out (about 4M cycles); that is a defect, and the launch's
+ * dK and dV are not to be trusted.  Zero otherwise. */
 #define LIBRA_RECORD_PLAN_MISMATCH 1u
+#define LIBRA_RECORD_WAIT_EXPIRED 2u
 typedef struct {
   uint32_t hw_id, xcc_id, n_items, flags;
   uint64_t t_start, t_end;

@@ -26,6 +26,7 @@ COST_EXECUTED, COST_PAIRS = 0, 1
 QUEUE_FWD, QUEUE_DQ, QUEUE_KV = 0, 1, 2
 PLAN_MAGIC, PLAN_VERSION = 0x4152424C, 5
 RECORD_PLAN_MISMATCH = 1
+RECORD_WAIT_EXPIRED = 2
 
 
 class LibraError(RuntimeError):

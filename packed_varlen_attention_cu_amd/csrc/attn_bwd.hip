@@ -60,6 +60,9 @@ namespace {
 // computed while they fly.  Blocks use padded rows (PadRows).
 constexpr int kDkdvGroups = kKvItemKeys / 32;   // key groups of 32
 constexpr int kDkdvWaves = 2 * kDkdvGroups;      // a P wave and a dS wave per group
+// Bound of a dS wave's wait for its P wave's tile: polls 64 cycles apart,
+// about 4M cycles in all, against a few thousand when nothing is wrong.
+constexpr int kPWaitPolls = 1 << 16;
 static_assert(kDkdvWaves % 4 == 0, "whole waves per SIMD");
 
 // Q blocks take 152-element rows (D = 128; 72 at D = 64) and dO blocks 168
@@ -88,6 +91,10 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   // kStages buffers of a step's Q, dO, LSE and D; step i uses buffer i mod kStages.
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[kStages * DkdvLds<D>::kBuf];
   __shared__ __attribute__((aligned(16))) uint16_t p_lds[DkdvLds<D>::kP];
+  // Step at which each key group's P of query tile t was last published, and
+  // whether any wave's bounded wait for it ran out.
+  __shared__ int p_ready[kDkdvGroups][2];
+  __shared__ int wait_expired;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int half = lane >> 5, col = lane & 31;
@@ -114,6 +121,10 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   const bool rowvec = rv >= 0;
   const int copies = QOCopy::count(wave) + (rowvec ? 1 : 0);   // this wave's copies per step
 
+  if (tid < 2 * kDkdvGroups) (&p_ready[0][0])[tid] = -1;   // visible after the first item's barrier
+  if (tid == 0) wait_expired = 0;
+  int step_no = 0;   // steps run so far in this workgroup (the same count in every wave)
+  bool expired = false;   // one of this wave's waits for its P wave ran out
   // The two roles are separate instantiations, so each allocates registers
   // for its own path only; both pass the same barriers.
   auto run = [&](auto role) {
@@ -267,39 +278,49 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
           }
         };
 
-        // The two query tiles are staggered across two mid-step barriers so
-        // that the two waves of a SIMD alternate matrix and element-wise work:
-        //   P wave:  S0 P0 | dV0 S1 P1 | dV1
-        //   dS wave: dP0   | dS0 dK0 dP1 | dS1 dK1
+        // Within a step the dS wave of a key group waits only for its own P
+        // wave, not for the workgroup: P of query tile t is published with a
+        // flag in LDS (a release store after the P writes; an acquire load
+        // before the P reads), so the twelve waves drift freely between the
+        // step barriers:
+        //   P wave:  S0 P0 (publish) S1 P1 (publish) dV0 dV1
+        //   dS wave: dP0 dP1 (wait P0) dS0 dK0 (wait P1) dS1 dK1
+        // Both waves of a group skip a step together (act is the same for
+        // them).  The wait is bounded so that no defect can hang the
+        // workgroup; running out is reported in the record.
+        const int stamp = step_no;
         if constexpr (pwave) {
           u32x4 pw0[2], pw1[2];
-          if (act) p_tile(0, pw0);
-          wait_lds();
-          block_barrier();            // P of query tile 0 is in LDS
           if (act) {
-            second(0, pw0);
+            p_tile(0, pw0);
+            __hip_atomic_store(&p_ready[kg][0], stamp, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             p_tile(1, pw1);
+            __hip_atomic_store(&p_ready[kg][1], stamp, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            second(0, pw0);
+            second(1, pw1);
           }
-          wait_lds();
-          block_barrier();            // P of query tile 1 is in LDS
-          if (act) second(1, pw1);
         } else {
-          f32x16 pacc0, pacc1;
-          if (act) pacc0 = first(0);
-          block_barrier();
+          auto wait_p = [&](int t) {
+            int seen = -1;
+            for (int n = 0; n < kPWaitPolls; ++n) {
+              seen = __hip_atomic_load(&p_ready[kg][t], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+              if (seen >= stamp) break;
+              __builtin_amdgcn_s_sleep(1);
+            }
+            expired |= seen < stamp;
+          };
           if (act) {
+            const f32x16 pacc0 = first(0), pacc1 = first(1);
             u32x4 dsw[2];
+            wait_p(0);
             ds_tile(0, pacc0, dsw);
             second(0, dsw);
-            pacc1 = first(1);
-          }
-          block_barrier();
-          if (act) {
-            u32x4 dsw[2];
+            wait_p(1);
             ds_tile(1, pacc1, dsw);
             second(1, dsw);
           }
         }
+        ++step_no;
       };
 
       // The previous item's dK / dV stores may still fly while this item's
@@ -339,8 +360,10 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   };
   if (wave < kDkdvGroups) run(std::true_type{});
   else run(std::false_type{});
+  if (expired) wait_expired = 1;
   __syncthreads();
-  if (a.records != nullptr && tid == 0) write_record(a, w, end - beg, t_start, plan_ok);
+  if (a.records != nullptr && tid == 0)
+    write_record(a, w, end - beg, t_start, plan_ok, wait_expired ? LIBRA_RECORD_WAIT_EXPIRED : 0u);
 }
 
 libra_status check_header(const void *plan, libra_plan_info *h) {

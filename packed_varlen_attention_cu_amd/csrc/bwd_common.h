@@ -33,12 +33,13 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
-__device__ __forceinline__ void write_record(const BwdArgs &a, int w, int n, uint64_t t0, bool plan_ok) {
+__device__ __forceinline__ void write_record(const BwdArgs &a, int w, int n, uint64_t t0, bool plan_ok,
+                                             uint32_t flags = 0u) {
   libra_cu_record rec;
   rec.hw_id = hw_id_reg();
   rec.xcc_id = xcc_id_reg();
   rec.n_items = (uint32_t)n;
-  rec.flags = plan_ok ? 0u : LIBRA_RECORD_PLAN_MISMATCH;
+  rec.flags = (plan_ok ? 0u : LIBRA_RECORD_PLAN_MISMATCH) | flags;
   rec.t_start = t0;
   rec.t_end = wall_clock64();
   a.records[w] = rec;

@@ -311,6 +311,7 @@ def test_binding_constants_match_the_header():
     assert lib.PLAN_VERSION == define("LIBRA_PLAN_VERSION")
     assert lib.PLAN_MAGIC == define("LIBRA_PLAN_MAGIC")
     assert lib.RECORD_PLAN_MISMATCH == define("LIBRA_RECORD_PLAN_MISMATCH")
+    assert lib.RECORD_WAIT_EXPIRED == define("LIBRA_RECORD_WAIT_EXPIRED")
     for name in ("LIBRA_EINVAL", "LIBRA_ESIZE", "LIBRA_EUNSUPPORTED", "LIBRA_EHIP", "LIBRA_EHOST"):
         assert getattr(lib, name) == enum(name), name
     for py, c in (("ASSIGN_PLACER", "LIBRA_ASSIGN_PLACER"), ("ASSIGN_ROUND_ROBIN", "LIBRA_ASSIGN_ROUND_ROBIN"),

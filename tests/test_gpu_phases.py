@@ -56,6 +56,7 @@ def test_phases_match_one_call_entry_points():
     assert int(r[1]["n_items"].sum()) == plan.info.n_kv_items
     assert int(r[2]["n_items"].sum()) == plan.info.n_dq_items
     assert (r["t_end"] >= r["t_start"]).all()
+    assert (r["flags"] == 0).all()       # no plan mismatch, no expired wait in the dK/dV pass
 
 
 def test_device_plan_from_another_plan_runs_nothing():
