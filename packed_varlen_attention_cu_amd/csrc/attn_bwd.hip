@@ -45,9 +45,10 @@ namespace {
 // Twelve waves, three per SIMD.  The 192 keys of an item are split into six
 // groups of 32; each group has a P wave (waves 0-5: S = Q K^T, P, dV^T +=
 // dO^T P) and a dS wave (waves 6-11: dP = dO V^T, dS = P * (dP - D),
-// dK^T += Q^T dS).  The P wave publishes its bf16 P through LDS halfway
-// through each step, so the matrix products of some waves of a SIMD overlap
-// the element-wise work of others.  Only the P wave applies the
+// dK^T += Q^T dS).  The P wave publishes its bf16 P through LDS tile by
+// tile, with a flag its dS wave waits for (no workgroup barrier within a
+// step), so the matrix products of some waves of a SIMD overlap the
+// element-wise work of others.  Only the P wave applies the
 // block-diagonal mask: masked P is 0, hence masked dS is 0 too.  Three waves
 // per SIMD leave each 168 registers, which the kernel fits in; the larger
 // item shares each Q and dO block among 192 keys instead of 128.
