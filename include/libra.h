@@ -252,7 +252,9 @@ libra_status libra_attn_bwd_workspace(const void *plan, size_t *bytes);
  * the forward's o and lse, and dout.  Reuses the plan's forward assignment
  * for dQ and its key-major queue for dK/dV (Libra paper, section 4.3.3: the
  * backward reuses the forward placement).  records: NULL or device
- * libra_cu_record[2 * num_cus] (dK/dV kernel, then dQ kernel). */
+ * libra_cu_record[2 * num_cus] (dK/dV kernel, then dQ kernel); a dK/dV
+ * record with LIBRA_RECORD_WAIT_EXPIRED marks the launch's dk and dv as not
+ * to be trusted (a defect, see libra_cu_record). */
 libra_status libra_attn_bwd(const void *plan, const void *plan_dev,
                             const void *q, const void *k, const void *v,
                             const void *o, const void *dout, const float *lse,
