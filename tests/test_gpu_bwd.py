@@ -110,14 +110,17 @@ def test_bwd_edge_packs(lib, lens):
 
 
 @pytest.mark.timeout(900)
-def test_bwd_full_size_sampled(lib):
-    """The 256K fwd+bwd workload at full size, in the launch configuration the benchmark times:
+@pytest.mark.parametrize("name", ["train_256k", "gqa_32k"])
+def test_bwd_full_size_sampled(lib, name):
+    """A packed workload at full size, in the launch configuration the benchmark uses:
     complete (sample, KV head) units of short samples, the last 192 rows of every long sample,
-    and one complete unit -- all 8 query heads of one KV head, every row and key -- of the
-    longest sample (32475 tokens), whose first keys' dK/dV sum over about 4060 query-block steps
-    and whose zigzag partners walk in reverse."""
+    and one complete unit -- all query heads of one KV head, every row and key -- of the
+    longest sample.  On the 256K training pack that sample has 32475 tokens: its first keys'
+    dK/dV sum over about 4060 query-block steps, and its zigzag partners walk in reverse.  The
+    32K pack (8 KV heads of 4 query heads each, mostly short samples) is small enough to check
+    every sample complete, each for one KV head."""
     import torch
-    w = synth.WORKLOADS["train_256k"]
+    w = synth.WORKLOADS[name]
     cu = synth.cu_seqlens(synth.make_lengths(w, 0))
     S.say("[bwd-full] generating inputs")
     t = synth.make_tensors(w, 0, names=("q", "k", "v", "dout"))
@@ -130,8 +133,12 @@ def test_bwd_full_size_sampled(lib):
     lens = np.diff(cu)
     short = [j for j in range(len(lens)) if 0 < lens[j] <= 1024]
     longs = [j for j in range(len(lens)) if lens[j] > 1024]
-    units = [(j, int(rng.integers(0, w.h_kv)), 0) for j in short[:24]]
-    units += [(j, int(rng.integers(0, w.h_kv)), int(lens[j]) - 192) for j in longs]
+    if name == "gqa_32k":
+        # small enough to check every sample complete, each for one KV head
+        units = [(j, int(rng.integers(0, w.h_kv)), 0) for j in range(len(lens)) if lens[j] > 0]
+    else:
+        units = [(j, int(rng.integers(0, w.h_kv)), 0) for j in short[:24]]
+        units += [(j, int(rng.integers(0, w.h_kv)), int(lens[j]) - 192) for j in longs]
     S.say(f"[bwd-full] oracle on {len(units)} units")
     refs = S.oracle_bwd_tails(t["q"], t["k"], t["v"], t["dout"], cu, S.scale_of(w), units)
     got = {n: [] for n in ("dq", "dk", "dv")}
@@ -145,13 +152,13 @@ def test_bwd_full_size_sampled(lib):
         want["dk"].append(rk.ravel())
         want["dv"].append(rv.ravel())
     for n in ("dq", "dk", "dv"):
-        S.check_grad(np.concatenate(got[n]), np.concatenate(want[n]), f"train_256k {n}")
+        S.check_grad(np.concatenate(got[n]), np.concatenate(want[n]), f"{name} {n}")
     # the longest sample, one KV head, complete
     j = int(np.argmax(lens))
     kv = int(rng.integers(0, w.h_kv))
     s, e = int(cu[j]), int(cu[j + 1])
     S.say(f"[bwd-full] oracle on the whole unit (sample {j}: {e - s} tokens, KV head {kv}, {g} heads)")
     rq, rk, rv = S.oracle_bwd_unit(t["q"], t["k"], t["v"], t["dout"], s, e, kv, g, S.scale_of(w))
-    S.check_grad(S.from_dev_bf16(dq[s:e, kv * g:(kv + 1) * g]), rq, f"longest sample dq")
-    S.check_grad(S.from_dev_bf16(dk[s:e, kv]), rk, f"longest sample dk")
-    S.check_grad(S.from_dev_bf16(dv[s:e, kv]), rv, f"longest sample dv")
+    S.check_grad(S.from_dev_bf16(dq[s:e, kv * g:(kv + 1) * g]), rq, f"{name} longest sample dq")
+    S.check_grad(S.from_dev_bf16(dk[s:e, kv]), rk, f"{name} longest sample dk")
+    S.check_grad(S.from_dev_bf16(dv[s:e, kv]), rv, f"{name} longest sample dv")
