@@ -81,13 +81,16 @@ enum {
 };
 
 /* Cost of a forward or dQ work item (libra_plan_params::cost).  The pages
- * cost a tile by its unmasked causal pairs (eq. 8); a kernel that computes
- * whole 64-key blocks executes more than that on blocks that straddle a
- * sample start or the diagonal, most of all on short samples.
- *   LIBRA_COST_EXECUTED  the query-key slots the kernel computes: for each of
- *                        the item's waves (32 query positions of one head),
- *                        32 x 64 per 64-key block holding a key one of its
- *                        rows may see;
+ * cost a tile by its unmasked causal pairs (eq. 8); a kernel that steps
+ * through whole 64-key blocks spends more than that on blocks that straddle
+ * a sample start or the diagonal, most of all on short samples.
+ *   LIBRA_COST_EXECUTED  the query-key slots of the item's walk: for each of
+ *                        its waves (32 query positions of one head), 32 x 64
+ *                        per 64-key block from the one holding the start of
+ *                        its first row's sample to the one holding its last
+ *                        row (every step of the walk copies a block and
+ *                        synchronises all waves, whether or not their rows
+ *                        see a key in it);
  *   LIBRA_COST_PAIRS     the item's eq. 8 pairs.
  * Either way item_overhead is added.  dK/dV items are always costed by the
  * work their kernel executes (see libra_item). */

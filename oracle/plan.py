@@ -31,15 +31,16 @@ An item's pairs are eq. 8 restricted to its rows and heads.  Items are
 numbered in (tile_id, kappa, head group, row chunk) order.
 
 Item cost (a reading: the pages cost a tile by its causal pairs, eq. 8, which
-measures the useful work but not what a kernel that computes whole 64-key
-blocks executes).  An item's workgroup runs c / 32 waves; wave w holds the 32
-query positions row0 + 32 * (w div nh) .. + 31 (clipped to the item) of head
-head0 + w mod nh, and computes every 64-key block that holds a key one of its
-rows may see: for a row r of sample j, the blocks floor(start_j / 64) ..
-floor(r / 64).  The executed cost counts 32 x 64 query-key slots for every
-(wave, block) so computed, plus a fixed per-item overhead (a planner
-parameter).  The "pairs" cost model (eq. 8 pairs plus the overhead) is kept
-for comparison.
+measures the useful work but not what a kernel that steps through whole
+64-key blocks executes).  An item's workgroup holds its rows in waves of 32
+query positions of one head (nh * ceil(nrows / 32) waves) and steps through
+the 64-key blocks floor(start_j / 64) .. floor((row0 + nrows - 1) / 64), j
+being the sample of its first row.  Every step copies a block and
+synchronises the workgroup whether or not a wave's rows see a key in it, so a
+step costs about the same for every wave.  The executed cost counts 32 x 64
+query-key slots for every (wave, block) of that walk, plus a fixed per-item
+overhead (a planner parameter).  The "pairs" cost model (eq. 8 pairs plus the
+overhead) is kept for comparison.
 
 Key-major items for the dK/dV pass: keys are cut at global positions into
 chunks of 192 (the dK/dV kernel's six key groups of 32); item (chunk c, KV
@@ -163,20 +164,14 @@ def _head_group_size(n: int) -> int:
     return 1
 
 
-def executed_slots(ranges, row0: int, nrows: int, nheads: int, columns: int) -> int:
-    """Query-key slots a forward or dQ workgroup computes for one item: for every wave, the
-    64-key blocks holding a key that one of its rows may see, times 32 x 64."""
-    total = 0
-    for w in range(columns // QUERY_TILE):
-        a = row0 + QUERY_TILE * (w // nheads)
-        e = min(row0 + nrows, a + QUERY_TILE)
-        blocks = set()
-        for s, end in ranges:          # rows of one sample add nested ranges: take its last row
-            last = min(e, end) - 1
-            if s < end and max(a, s) <= last:
-                blocks.update(range(s // KEY_BLOCK, last // KEY_BLOCK + 1))
-        total += len(blocks)
-    return total * QUERY_TILE * KEY_BLOCK
+def executed_slots(ranges, row0: int, nrows: int, nheads: int) -> int:
+    """Query-key slots of one forward or dQ item's walk: every key block from the one holding
+    the start of its first row's sample to the one holding its last row, for every wave (32
+    rows of one head), times 32 x 64."""
+    start = next(s for s, end in ranges if s <= row0 < end)
+    blocks = range(start // KEY_BLOCK, (row0 + nrows - 1) // KEY_BLOCK + 1)
+    waves = nheads * -(-nrows // QUERY_TILE)
+    return waves * len(blocks) * QUERY_TILE * KEY_BLOCK
 
 
 def fwd_items(cu, total_tokens, h_q, h_kv, B, W, overhead=0, columns=ITEM_COLUMNS, cost="executed") -> list:
@@ -196,7 +191,7 @@ def fwd_items(cu, total_tokens, h_q, h_kv, B, W, overhead=0, columns=ITEM_COLUMN
                     r1 = min(t["tok_end"], r0 + rows)
                     per_head, _ = _block_pairs(ranges, r0, r1)
                     work = (nh * per_head if cost == "pairs"
-                            else executed_slots(ranges, r0, r1 - r0, nh, columns))
+                            else executed_slots(ranges, r0, r1 - r0, nh))
                     items.append(dict(id=len(items), tile_id=t["tile_id"], row0=r0, nrows=r1 - r0,
                                       kv_head=kappa, head0=heads[gi * nh], nheads=nh,
                                       pairs=nh * per_head, cost=work + overhead))

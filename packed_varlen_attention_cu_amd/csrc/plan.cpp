@@ -80,28 +80,17 @@ int sample_of(const int32_t *cu, int n, int64_t pos) {
   return (int)(std::upper_bound(cu, cu + n + 1, (int32_t)pos) - cu) - 1;
 }
 
-// 64-key blocks one wave of a forward or dQ workgroup computes for query rows
-// [a, e): for a row r of sample j, the blocks start_j / 64 .. r / 64; the
-// union over the rows, taken sample by sample (the ranges ascend).
-int64_t wave_blocks(const int32_t *cu, int n, int64_t a, int64_t e) {
-  int64_t count = 0, done = -1;   // blocks up to `done` are counted
-  for (int j = sample_of(cu, n, a); j < n && cu[j] < e; ++j) {
-    if (cu[j + 1] <= std::max<int64_t>(a, cu[j])) continue;   // empty, or before a
-    const int64_t lo = std::max<int64_t>(cu[j] / libra::kKeyBlock, done + 1);
-    const int64_t hi = (std::min<int64_t>(e, cu[j + 1]) - 1) / libra::kKeyBlock;
-    if (hi >= lo) count += hi - lo + 1;
-    done = std::max(done, hi);
-  }
-  return count;
-}
-
-// Query-key slots a forward or dQ workgroup computes for an item of rows
-// [row0, row0 + nrows) and nh heads: each row range of 32 is held by nh waves.
+// Query-key slots of the walk of a forward or dQ item of rows [row0, row0 +
+// nrows) and nh heads: its workgroup steps through every 64-key block from the
+// one holding the start of its first row's sample to the one holding its last
+// row, and each step copies the block and synchronises all of its waves (32
+// rows of one head each) whether or not their rows see a key there.
 int64_t executed_slots(const int32_t *cu, int n, int64_t row0, int64_t nrows, int nh) {
-  int64_t blocks = 0;
-  for (int64_t a = row0; a < row0 + nrows; a += libra::kQueryTile)
-    blocks += wave_blocks(cu, n, a, std::min(row0 + nrows, a + libra::kQueryTile));
-  return nh * blocks * libra::kQueryTile * libra::kKeyBlock;
+  if (nrows <= 0) return 0;
+  const int64_t first = cu[sample_of(cu, n, row0)] / libra::kKeyBlock;
+  const int64_t blocks = (row0 + nrows - 1) / libra::kKeyBlock - first + 1;
+  const int64_t waves = nh * ((nrows + libra::kQueryTile - 1) / libra::kQueryTile);
+  return waves * blocks * libra::kQueryTile * libra::kKeyBlock;
 }
 
 libra_status validate(const int32_t *cu, const libra_plan_params *p) {

@@ -81,8 +81,7 @@ def test_items_partition_tiles(h_q, h_kv, W):
             assert h // g == it["kv_head"]
             assert t["head_begin"] <= h < t["head_begin"] + t["head_count"]
         cover[it["row0"]:it["row0"] + it["nrows"], it["head0"]:it["head0"] + it["nheads"]] += 1
-        assert it["cost"] == P.executed_slots(P._ranges(cu), it["row0"], it["nrows"], it["nheads"],
-                                              P.ITEM_COLUMNS) + 7
+        assert it["cost"] == P.executed_slots(P._ranges(cu), it["row0"], it["nrows"], it["nheads"]) + 7
         assert it["cost"] - 7 >= it["pairs"]
         per_tile[it["tile_id"]] = per_tile.get(it["tile_id"], 0) + it["pairs"]
     assert (cover == 1).all()
@@ -215,21 +214,32 @@ def test_kv_item_cost_hand_worked():
 
 def test_fwd_item_executed_cost_hand_worked():
     """One tile of 450 tokens x 4 heads on one KV head: items of 96 rows x 4 heads, twelve waves of
-    32 rows (three row ranges, four heads each).  A row r of sample j needs the 64-key blocks
-    start_j / 64 .. r / 64.  Item rows 0-95: ranges 0-31 and 32-63 need block 0, 64-95 blocks
-    0-1: 4 blocks x 4 heads = 16.  Rows 96-191: 96-127 straddles samples 0 and 1 (blocks 0-1 and
-    1-1: 2), 128-159 and 160-191 need 1-2: 6 x 4 = 24.  Rows 192-287: 3 + 3 + 4 = 10, x 4 = 40.
-    Rows 288-383: 4 + 5 + 5 = 14, x 4 = 56.  Rows 384-449 (66 rows): 384-415 straddles (sample 1:
-    1-6, sample 2: 6-6: 6 blocks), 416-447 needs 6, 448-449 needs 6-7: 9 x 4 = 36.  Each
-    wave-block is 32 x 64 = 2048 slots.  Pairs: rows 0-95 are sample 0's first 96 queries,
+    32 rows (three row ranges, four heads each).  An item's walk runs from the block holding the
+    start of its first row's sample to the block holding its last row, and every wave counts
+    every block of it.  Rows 0-95 (sample 0, start 0): blocks 0-1, 2 x 12 = 24 wave-blocks.
+    Rows 96-191 (first row in sample 0): blocks 0-2, 3 x 12 = 36.  Rows 192-287 (sample 1,
+    start 100, block 1): blocks 1-4, 48.  Rows 288-383: blocks 1-5, 60.  Rows 384-449 (66 rows,
+    first row in sample 1, three row ranges): blocks 1-7, 7 x 12 = 84.  Each wave-block is
+    32 x 64 = 2048 slots.  Pairs: rows 0-95 are sample 0's first 96 queries,
     4 x 96 x 97 / 2 = 18624."""
     items = P.fwd_items(HAND_CU, 450, 4, 1, 450, 4)
     assert [(it["row0"], it["nrows"], it["nheads"]) for it in items] == [(0, 96, 4), (96, 96, 4), (192, 96, 4),
                                                                         (288, 96, 4), (384, 66, 4)]
-    assert [it["cost"] for it in items] == [2048 * b for b in (16, 24, 40, 56, 36)]
+    assert [it["cost"] for it in items] == [2048 * b for b in (24, 36, 48, 60, 84)]
     assert items[0]["pairs"] == 18624
     by_pairs = P.fwd_items(HAND_CU, 450, 4, 1, 450, 4, overhead=3, cost="pairs")
     assert [it["cost"] for it in by_pairs] == [it["pairs"] + 3 for it in items]
+
+
+def test_dq_item_executed_cost_hand_worked():
+    """The same tile cut into dQ items of 64 rows x 4 heads (eight waves: two row ranges of four
+    heads).  Rows 0-63: block 0, 1 x 8.  64-127: blocks 0-1, 16.  128-191 (sample 1, start 100,
+    block 1): blocks 1-2, 16.  192-255: blocks 1-3, 24.  256-319: 1-4, 32.  320-383: 1-5, 40.
+    384-447 (first row in sample 1): 1-6, 48.  448-449 (2 rows, one row range, four waves;
+    first row in sample 2, start 400, block 6): blocks 6-7, 2 x 4 = 8."""
+    items = P.fwd_items(HAND_CU, 450, 4, 1, 450, 4, columns=P.DQ_ITEM_COLUMNS)
+    assert [(it["row0"], it["nrows"]) for it in items] == [(r, 64) for r in range(0, 448, 64)] + [(448, 2)]
+    assert [it["cost"] for it in items] == [2048 * b for b in (8, 16, 16, 24, 32, 40, 48, 8)]
 
 
 def test_executed_cost_pins_catch_block_size_slips(monkeypatch):
@@ -238,24 +248,32 @@ def test_executed_cost_pins_catch_block_size_slips(monkeypatch):
     monkeypatch.setattr(P, "KEY_BLOCK", 32)
     with pytest.raises(AssertionError):
         test_fwd_item_executed_cost_hand_worked()
+    with pytest.raises(AssertionError):
+        test_dq_item_executed_cost_hand_worked()
+    monkeypatch.undo()
+    monkeypatch.setattr(P, "QUERY_TILE", 64)
+    with pytest.raises(AssertionError):
+        test_dq_item_executed_cost_hand_worked()
     monkeypatch.undo()
     monkeypatch.setattr(P, "KV_QUERY_BLOCK", 128)
     with pytest.raises(AssertionError):
         test_kv_item_cost_hand_worked()
 
 
-def test_executed_cost_covers_pairs_and_equals_them_on_full_blocks():
-    """Executed slots are at least the pairs (every pair lies in a computed block), and on a
-    sample whose rows are far from its start and end in whole blocks they count every block of
-    the walk: an item of 384 rows of one head at rows 4096-4479 of a 8192-token sample
-    computes, per wave w, blocks 0 .. (4096 + 32 w + 31) / 64."""
+def test_executed_cost_covers_pairs_and_counts_the_whole_walk():
+    """Executed slots are at least the pairs (every pair lies in a block of the walk).  An item of
+    384 rows of one head at rows 4224-4607 of an 8192-token sample walks blocks 0 .. 4607 / 64 =
+    71, and all twelve waves count all 72 of them, though the first wave's rows see keys only up
+    to block 4255 / 64 = 66.  An item whose first row lies in an earlier sample walks that
+    sample too: rows 96-191 of samples [0, 100) and [100, 400) start at block 0."""
     cu = [0, 8192]
     items = P.fwd_items(cu, 8192, 1, 1, 8192, 1)
     it = next(i for i in items if i["row0"] == 4224)
-    expect = sum((it["row0"] + 32 * w + 31) // 64 + 1 for w in range(12)) * 2048
-    assert it["cost"] == expect
+    assert it["cost"] == 12 * 72 * 2048
     for i in items:
         assert i["cost"] >= i["pairs"]
+    assert P.executed_slots(P._ranges(HAND_CU), 96, 96, 1) == 3 * 3 * 2048
+    assert P.executed_slots(P._ranges(HAND_CU), 100, 92, 1) == 3 * 2 * 2048
 
 
 # ------------------------------------------------ Algorithm 2 with the L2 residency term
