@@ -561,10 +561,10 @@ libra_status plan_impl(const int32_t *cu, const libra_plan_params *pp, void *buf
   tiles.reserve(nblocks * S);
   items.reserve(n_items);
   dq_items.reserve(n_dq);
-  // Per-head pairs and per-head executed 64-key wave blocks of a block's row
+  // Per-head pairs and per-head walk slots (executed_slots) of a block's row
   // chunks of one length, computed once per block and chunk length.
   struct ChunkWork {
-    int64_t pairs, blocks;
+    int64_t pairs, slots;
   };
   std::vector<std::pair<int, std::vector<ChunkWork>>> chunk_pairs;
   int jb = 0;
@@ -604,7 +604,7 @@ libra_status plan_impl(const int32_t *cu, const libra_plan_params *pp, void *buf
           it.tile_id = t.tile_id;
           it.id = (int32_t)out.size();
           it.pairs = nh * (*cp)[ci].pairs;
-          it.cost = (p.cost == LIBRA_COST_PAIRS ? it.pairs : nh * (*cp)[ci].blocks) + p.item_overhead;
+          it.cost = (p.cost == LIBRA_COST_PAIRS ? it.pairs : nh * (*cp)[ci].slots) + p.item_overhead;
           out.push_back(it);
           ++made;
         }
