@@ -162,3 +162,29 @@ def test_bwd_full_size_sampled(lib, name):
     S.check_grad(S.from_dev_bf16(dq[s:e, kv * g:(kv + 1) * g]), rq, f"{name} longest sample dq")
     S.check_grad(S.from_dev_bf16(dk[s:e, kv]), rk, f"{name} longest sample dk")
     S.check_grad(S.from_dev_bf16(dv[s:e, kv]), rv, f"{name} longest sample dv")
+
+
+@pytest.mark.timeout(600)
+def test_fwd_bwd_head_dim_64_mid_size(lib):
+    """The d = 64 kernels beyond the small packs: 12288 tokens in nine samples (4000 and 3000
+    tokens, block-edge lengths, an empty and a one-token sample), 16 query heads on 4 KV heads,
+    SH-Tiles of 4096 tokens x 4 heads; every output and gradient against the oracle."""
+    import torch
+    import oracle.attention as A
+    lens = (4000, 3000, 1, 0, 2047, 1025, 64, 65, 2086)
+    w = synth.Workload("d64_12k", sum(lens), 16, 4, 64, 4096, 4, fixed_lengths=lens, fill=False)
+    cu = synth.cu_seqlens(synth.make_lengths(w, 3))
+    t = synth.make_tensors(w, 3, names=("q", "k", "v", "dout"))
+    S.say(f"[d64] L={w.total_tokens} h={w.h_q}/{w.h_kv} samples={len(cu) - 1} max={int(np.diff(cu).max())}")
+    plan = S.make_plan(w, cu)
+    q, k, v, do = (S.to_dev(t[n]) for n in ("q", "k", "v", "dout"))
+    o, lse = lib.attn_fwd(plan, q, k, v, S.scale_of(w))
+    dq, dk, dv = lib.attn_bwd(plan, q, k, v, o, lse, do, S.scale_of(w))
+    torch.cuda.synchronize()
+    args = [A.widen_bf16(t[n]) for n in ("q", "k", "v")]
+    o_ref, lse_ref = A.forward(*args, cu, S.scale_of(w))
+    S.check_out(S.from_dev_bf16(o), o_ref, "d64 12K")
+    S.check_lse(lse.cpu().numpy().astype(np.float64), lse_ref, "d64 12K")
+    ref = A.backward(*args, A.widen_bf16(t["dout"]), cu, S.scale_of(w))
+    for name_g, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        S.check_grad(S.from_dev_bf16(g), r, f"d64 12K {name_g}")
