@@ -818,6 +818,7 @@ extern "C" const char *libra_status_str(libra_status s) {
     case LIBRA_ESIZE: return "buffer too small";
     case LIBRA_EUNSUPPORTED: return "unsupported configuration";
     case LIBRA_EHIP: return "HIP runtime error";
+    case LIBRA_EHOST: return "host out of memory or threads";
   }
   return "unknown status";
 }

@@ -422,6 +422,12 @@ def test_status_strings():
     assert lib.libra_status_str(0) == "ok"
     assert lib.libra_status_str(-2) == "buffer too small"
     assert lib.libra_status_str(123) == "unknown status"
+    # every status the header declares has its own text
+    text = open(HEADER).read()
+    codes = [int(v) for v in re.findall(r"LIBRA_E\w+\s*=\s*(-\d+)", text)]
+    assert len(codes) >= 5
+    for c in codes:
+        assert lib.libra_status_str(c) not in ("unknown status", "ok"), c
 
 
 def test_last_hip_error_is_empty_without_a_failed_launch():
